@@ -1,0 +1,33 @@
+"""CPU oracle for the DDTree tree-verify step -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously-correct NumPy/Python implementations of the four
+steps of the verify path.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the product path (the
+HIP library and its Python binding) never does, and shares no code with it.
+
+Sources (blog pages on DDTree speculative decoding):
+  * build   -- "The Architecture of Speculative Decoding: Dissecting DDTree's
+               Tree-Parallel Evaluation Strategy", Section 1 (five-step flow,
+               steps 2-3); "The Tree That Couldn't Branch", "Context: The Road
+               to DDTree" and "Hypothesis 4".
+  * attention -- same first page, Section 1 step 4 and Section 2 (context
+               loaded once, shared by every tree node); "The Pivot Point",
+               "The Design Constraint: Load Contexts Once".
+  * vocab   -- Section 1 step 4 (per-node argmax); Section 3 (softmax over the
+               verify logits at temperature T).
+  * verify  -- Section 1 step 5 (greedy walk, bonus token); Section 3 and
+               "Implementing Temperature-Aware Tree Sampling for DDTree",
+               "Path B: CPU-Side Tree Rejection Sampling" (tree rejection
+               sampling with residual renormalisation).
+
+Parity status: every function here is pinned by tests under tests/ that check
+it against brute force, closed forms, library routines or a statistical test
+(see the test modules' docstrings); none is "parity unpinned".
+"""
+from .build import build_tree, N_WORDS
+from .attention import tree_attention, to_f64
+from .vocab import vocab_reduce, weight_constants, weights
+from .verify import verify_greedy, verify_sample
+
+__all__ = ["build_tree", "N_WORDS", "tree_attention", "to_f64", "vocab_reduce",
+           "weight_constants", "weights", "verify_greedy", "verify_sample"]
