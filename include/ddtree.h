@@ -1,0 +1,223 @@
+/*
+ * libddtree -- DDTree tree-parallel verify step for AMD MI355X (gfx950).
+ *
+ * One verify step of tree speculative decoding, for a batch of B requests on
+ * one GPU, as described in the blog pages on DDTree ("The Architecture of
+ * Speculative Decoding: Dissecting DDTree's Tree-Parallel Evaluation
+ * Strategy", Sections 1-3; "The Pivot Point", "The Design Constraint: Load
+ * Contexts Once"; "Implementing Temperature-Aware Tree Sampling for DDTree",
+ * "Path B"; "The Tree That Couldn't Branch", "Hypothesis 3" and "Hypothesis 4"):
+ *
+ *   ddtree_build           per-depth draft top-k  ->  best-first token tree
+ *   ddtree_tree_attention  every tree node attends to its request's context
+ *                          (streamed from HBM once, shared by all nodes) and
+ *                          to its own ancestors
+ *   ddtree_vocab_reduce    per-node argmax / max / log-sum-exp and, for
+ *                          sampling, the exact integer softmax total R
+ *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
+ *   ddtree_verify_sample   temperature-T tree rejection sampling walk
+ *
+ * Conventions shared by every call
+ *   - Every data pointer is DEVICE memory owned by the caller (unless named
+ *     *_host).  The library allocates nothing and keeps no state between
+ *     calls; workspaces are passed in and sized by the *_workspace_size calls.
+ *   - Every call enqueues its kernels on `stream` and returns without waiting.
+ *   - The returned status covers argument validation (done on the host before
+ *     anything is launched: nothing is enqueued on a non-OK status) and launch
+ *     errors (DDTREE_EDEVICE).  ddtree_last_error() gives a thread-local message
+ *     for the last non-OK status of the calling thread.
+ *   - Preconditions not checked (undefined results otherwise): inputs are
+ *     finite; draft log-probs are non-increasing along the top-k axis; the
+ *     draft tokens of one (request, depth) are distinct; ctx_offsets_host holds
+ *     the same values as ctx_offsets.
+ *   - Tensors are dense, row-major, with 16-byte aligned base pointers.
+ *   - Calls are thread-safe (no shared state); calls on one stream are ordered.
+ */
+#ifndef DDTREE_H
+#define DDTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DDTREE_OK = 0,
+  DDTREE_EINVAL = 1,       /* bad argument (null pointer, size out of range, ...) */
+  DDTREE_EUNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim 96) */
+  DDTREE_EDEVICE = 3       /* a HIP launch or runtime call failed */
+} ddtree_status;
+
+typedef enum { DDTREE_F32 = 0, DDTREE_BF16 = 1 } ddtree_dtype;
+
+/* Size limits (validated). */
+#define DDTREE_MAX_NODES 128  /* N = budget + 1 */
+#define DDTREE_MAX_DEPTH 64   /* D */
+#define DDTREE_MAX_TOPK 64    /* K */
+
+/*
+ * The token tree of a batch: structure-of-arrays, one row of N = budget + 1
+ * entries per request, root at index 0, nodes numbered in the order the
+ * best-first build takes them (so parent[i] < i).  All arrays are device
+ * memory of the shapes given; entries n >= num_nodes[b] are padding
+ * (integer fields -1, score -inf, vis 0).
+ */
+typedef struct {
+  int32_t* token;        /* [B, N] draft token of the node (root: the anchor token) */
+  int32_t* parent;       /* [B, N] parent index, -1 for the root */
+  int32_t* depth;        /* [B, N] 0 for the root */
+  int32_t* rank;         /* [B, N] rank of the token in its depth's top-k, -1 for the root */
+  int32_t* position;     /* [B, N] prefix_len[b] + depth */
+  int32_t* first_child;  /* [B, N] lowest-rank child, -1 if none */
+  int32_t* next_sibling; /* [B, N] next-rank sibling, -1 if none */
+  float* score;          /* [B, N] cumulative draft log-prob (fp32 sum), root 0 */
+  uint64_t* vis;         /* [B, N, W] bit j of row i: node i sees node j (ancestors and itself) */
+  int32_t* num_nodes;    /* [B] 1 + number of nodes taken (<= N) */
+  int32_t B, N, D, K, W; /* W = (N + 63) / 64 */
+} ddtree_tree;
+
+/*
+ * ddtree_build -- best-first tree from per-depth top-k draft log-probs.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1,
+ * steps 2-3 (heap on cumulative log-prob: take the best entry, add it, offer
+ * its best child and next sibling, until `budget` nodes; visibility = the
+ * ancestors); "The Tree That Couldn't Branch", "Hypothesis 3" (position =
+ * prefix length + depth) and "Hypothesis 4" (every depth-d node draws its
+ * children from the same depth-d top-k).
+ *   draft_lp   [B, D, K] fp32  log-prob of the rank-r token at depth d+1
+ *   draft_tok  [B, D, K] int32 the token itself
+ *   root_tok   [B] int32, prefix_len [B] int32
+ *   budget     nodes to take besides the root, 1 <= budget <= 127;
+ *              tree->N must equal budget + 1 and tree->B/D/K/W match.
+ * Order: larger cumulative score first (score(child) = fp32(score(parent) +
+ * draft_lp), one rounded add), ties by smaller parent index then smaller rank.
+ * Errors: DDTREE_EINVAL for null pointers or out-of-range sizes.
+ */
+ddtree_status ddtree_build(const float* draft_lp, const int32_t* draft_tok,
+                           const int32_t* root_tok, const int32_t* prefix_len, int32_t B,
+                           int32_t D, int32_t K, int32_t budget, const ddtree_tree* tree,
+                           hipStream_t stream);
+
+/*
+ * ddtree_tree_attention -- tree attention with the context loaded once.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1
+ * step 4 and Section 2; "The Pivot Point", "The Design Constraint: Load
+ * Contexts Once": every tree node of request b attends to all L_b context
+ * keys and to the tree keys its vis row marks; each context K/V element is
+ * read from HBM once and used by every tree query.
+ *   q            [B, N, Hq, Dh]        dtype
+ *   k_ctx, v_ctx [ctx_offsets[B], Hkv, Dh] dtype; request b owns rows
+ *                [ctx_offsets[b], ctx_offsets[b+1])
+ *   ctx_offsets  [B+1] int32 device;  ctx_offsets_host: the same values in host memory
+ *   k_tree, v_tree [B, N, Hkv, Dh]    dtype (the tree tokens' own K/V)
+ *   tree         from ddtree_build (uses vis, num_nodes)
+ *   Hq % Hkv == 0, query head h reads KV head h / (Hq / Hkv); Dh in {64, 128};
+ *   M = N * Hq / Hkv <= 1024 query rows per KV head.  Up to 128 rows share
+ *   one pass over the context; larger M is processed in 128-row slices, each
+ *   of which reads the context once more.
+ *   scale        score scale (1/sqrt(Dh) is the usual choice)
+ *   out          [B, N, Hq, Dh] dtype; padding nodes get 0
+ *   lse          [B, N, Hq] fp32 natural-log softmax denominator, or NULL
+ *   workspace    device scratch of at least
+ *                ddtree_tree_attention_workspace_size(...) bytes (contents
+ *                need no initialisation and are garbage afterwards)
+ * Errors: DDTREE_EINVAL (null pointers, sizes, small workspace),
+ *         DDTREE_EUNSUPPORTED (other Dh, too many query rows per KV head).
+ */
+size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                            int32_t Dh, const int32_t* ctx_offsets_host);
+
+ddtree_status ddtree_tree_attention(const void* q, const void* k_ctx, const void* v_ctx,
+                                    const int32_t* ctx_offsets, const int32_t* ctx_offsets_host,
+                                    const void* k_tree, const void* v_tree,
+                                    const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh,
+                                    ddtree_dtype dtype, float scale, void* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ddtree_vocab_reduce -- one pass over the target logits of every tree node.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1
+ * step 4 (argmax at every node in parallel) and Section 3 (softmax at
+ * temperature T over the verify logits).
+ *   logits    [B, N, V] dtype (row b, n: the target's prediction after node n)
+ *   num_nodes [B] rows n >= num_nodes[b] are skipped (argmax -1, maxv -inf, R 0,
+ *             lse -inf)
+ *   argmax    [B, N] int32, lowest token id among equal maxima
+ *   maxv      [B, N] fp32, the logit at argmax (+0.0 for a zero)
+ *   temperature  0 => greedy only; > 0 => also R
+ *   R         [B, N] uint64 (required iff temperature > 0): exact sum over the
+ *             row of the integer weights w(l) = floor(p * 2^(32+k)) where
+ *             y = (l - maxv) * c, c = fp32(log2(e) / T), k = rint(y),
+ *             f = y - k, p = degree-6 Taylor polynomial of 2^f in fp32 with
+ *             separately rounded multiplies and adds, coefficients
+ *             fp32((ln 2)^n / n!), and w = 0 when y < -32.  w/R is the
+ *             temperature-T softmax to ~1e-6 relative; ddtree_verify_sample
+ *             recomputes the same w.
+ *   lse       [B, N] fp32 natural-log log-sum-exp of the raw logits, or NULL
+ *   workspace ddtree_vocab_reduce_workspace_size(B, N, V) bytes (may be 0)
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature < 0 or NaN).
+ */
+size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32_t V);
+
+ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_t B, int32_t N,
+                                  int32_t V, const int32_t* num_nodes, float temperature,
+                                  int32_t* argmax, float* maxv, uint64_t* R, float* lse,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ddtree_verify_greedy -- greedy verified-tree walk.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1
+ * step 5: from the root take the child whose token equals the argmax at the
+ * current node; stop when none does; the bonus is the argmax at the last node.
+ *   argmax      [B, N] from ddtree_vocab_reduce
+ *   accept_len  [B]          number of accepted draft tokens (0..D)
+ *   path_nodes  [B, D+1]     root, then the accepted nodes, then -1
+ *   out_tokens  [B, D+1]     the accepted draft tokens, then the bonus, then -1
+ *   bonus       [B]
+ * Errors: DDTREE_EINVAL (null pointers, tree sizes).
+ */
+ddtree_status ddtree_verify_greedy(const ddtree_tree* tree, const int32_t* argmax,
+                                   int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                                   int32_t* bonus, hipStream_t stream);
+
+/*
+ * ddtree_verify_sample -- temperature-T tree rejection sampling walk.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 3
+ * (tree-structured rejection sampling: test the children, renormalise the
+ * residual on rejection, draw the bonus from the residual and stop);
+ * "Implementing Temperature-Aware Tree Sampling for DDTree", "Path B".
+ * The children are the deterministic top-k, so child c is accepted with the
+ * residual target probability of its token: with t = floor(u * R_res / 2^64),
+ * c is accepted iff t < w(c); on rejection R_res -= w(c) and the token is
+ * excluded.  Children are tried in rank order.  When no child is accepted (or
+ * the node is a leaf), the bonus is the smallest token x whose running sum of
+ * non-excluded weights exceeds floor(u' * R_res / 2^64).
+ *   logits [B, N, V] dtype, maxv [B, N], R [B, N] from ddtree_vocab_reduce with
+ *   the same temperature; uniforms [B, N, 2] uint64: slot 0 = the node's
+ *   accept test, slot 1 = its bonus draw.  Outputs as ddtree_verify_greedy.
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature <= 0 or NaN).
+ */
+ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const void* logits,
+                                   ddtree_dtype dtype, int32_t V, const float* maxv,
+                                   const uint64_t* R, float temperature, const uint64_t* uniforms,
+                                   int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
+                                   int32_t* bonus, hipStream_t stream);
+
+/* Host-only helper: the constants the sampling weights use for temperature T
+ * (c = fp32(log2(e)/T) and a[0..6] = fp32((ln 2)^n / n!)).  No GPU needed. */
+ddtree_status ddtree_sampling_constants(float temperature, float* c, float* a7);
+
+/* Thread-local message for the last non-OK status returned on this thread. */
+const char* ddtree_last_error(void);
+
+/* Library version string. */
+const char* ddtree_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DDTREE_H */

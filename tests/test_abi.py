@@ -1,0 +1,117 @@
+"""The C-ABI library: loads, exports every declared symbol, validates arguments on the host.
+
+No kernel is launched here (these run without a GPU): every call below is
+rejected by host-side validation before anything is enqueued, or is a
+host-only helper.
+"""
+import ctypes
+import decimal
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddtree.h")
+LIB = os.path.join(ROOT, "tree_verification_build_amd", "libddtree.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libddtree.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddtree_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert {"ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce",
+            "ddtree_verify_greedy", "ddtree_verify_sample"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_error_string():
+    import tree_verification_build_amd as t
+    assert "gfx950" in t.ddtree_version()
+    assert isinstance(t.ddtree_last_error(), str)
+
+
+def test_sampling_constants_match_oracle_and_exact_values():
+    import tree_verification_build_amd as t
+    from oracle import weight_constants
+    decimal.getcontext().prec = 50
+    ln2 = decimal.Decimal(2).ln()
+    for T in (0.3, 0.7, 1.0, 1.7, 2.0):
+        c, a = t.ddtree_sampling_constants(T)
+        oc, oa = weight_constants(T)
+        assert c == oc
+        assert np.array_equal(a, oa)
+        for n in range(7):
+            exact = ln2 ** n / math.factorial(n)
+            err = abs(decimal.Decimal(float(a[n])) - exact)
+            ulp = decimal.Decimal(float(np.spacing(a[n])))
+            assert err <= ulp / 2
+    with pytest.raises(t.DdtreeError):
+        t.ddtree_sampling_constants(0.0)
+
+
+def _fake_tree(B=1, N=9, D=8, K=2, W=1):
+    from tree_verification_build_amd._lib import _CTree
+    return _CTree(*([16] * 10), B, N, D, K, W)
+
+
+def test_host_validation_rejects_bad_arguments():
+    from tree_verification_build_amd._lib import lib
+    fake = ctypes.c_void_p(16)
+    t = _fake_tree()
+    # ddtree_build
+    assert lib.ddtree_build(None, fake, fake, fake, 1, 8, 2, 8, ctypes.byref(t), None) == 1
+    assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 200, ctypes.byref(t), None) == 1
+    assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 7, ctypes.byref(t), None) == 1
+    bad = _fake_tree(W=2)
+    assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 8, ctypes.byref(bad), None) == 1
+    assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 8, None, None) == 1
+    # vocab
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 0, fake, 0.0, fake, fake, None, None, None, 0,
+                                   None) == 1
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 100, fake, -1.0, fake, fake, None, None, None,
+                                   0, None) == 1
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 100, fake, 0.5, fake, fake, None, None, None,
+                                   0, None) == 1                     # R missing with T > 0
+    assert lib.ddtree_vocab_reduce(fake, 7, 1, 9, 100, fake, 0.0, fake, fake, None, None, None,
+                                   0, None) == 1                     # unknown dtype
+    # greedy split pass needs its workspace at this size
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 163840, fake, 0.0, fake, fake, None, None,
+                                   None, 0, None) == 1
+    # walks
+    assert lib.ddtree_verify_greedy(ctypes.byref(t), None, fake, fake, fake, fake, None) == 1
+    assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, 0.0, fake, fake,
+                                    fake, fake, fake, None) == 1
+    # attention
+    offs = (ctypes.c_int32 * 2)(0, 64)
+    args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]
+    assert lib.ddtree_tree_attention(*args, 4, 3, 64, 1, 0.125, fake, None, None, 0, None) == 1
+    assert lib.ddtree_tree_attention(*args, 4, 4, 96, 1, 0.125, fake, None, None, 0, None) == 2
+    assert lib.ddtree_tree_attention(*args, 128, 1, 64, 1, 0.125, fake, None, None, 0, None) == 2
+    assert lib.ddtree_tree_attention(*args, 4, 4, 64, 1, -1.0, fake, None, None, 0, None) == 1
+    assert lib.ddtree_tree_attention(*args, 4, 4, 64, 5, 0.125, fake, None, None, 0, None) == 1
+    mis = ctypes.c_void_p(24)
+    assert lib.ddtree_tree_attention(mis, *args[1:], 4, 4, 64, 1, 0.125, fake, None, None, 0,
+                                     None) == 1
+    lib.ddtree_last_error.restype = ctypes.c_char_p
+    assert b"aligned" in lib.ddtree_last_error()
+
+
+def test_workspace_sizes_are_host_only_and_sane():
+    import tree_verification_build_amd as t
+    offs = np.array([0, 8192], np.int32)
+    ws = t.ddtree_tree_attention_workspace_size(1, 33, 8, 8, 128, offs)
+    assert ws > 0 and ws % 4 == 0
+    assert t.ddtree_tree_attention_workspace_size(1, 9, 4, 4, 96, offs) == 0
+    assert t.ddtree_vocab_reduce_workspace_size(1, 33, 163840) > 0
+    assert t.ddtree_vocab_reduce_workspace_size(64, 33, 163840) == 0

@@ -1,0 +1,175 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded inputs.
+
+Bit-exact: tree structure and scores, argmax, maxv, R, accept length, path,
+tokens and bonus.  Tolerance (tree attention): max-abs 2e-2 for bf16 and
+1e-4 for fp32, also relative to max|o|.  Small cases cover every output; the
+full-size workloads (single request 8192 ctx, batch of 16 x 4096, 65536 ctx,
+ragged batch of 64) cover all of the tree, vocabulary and walk outputs and
+spot-check attention on a sample of (request, head) pairs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_cases import Case, assert_attention_close, assert_tree_equal, attn_to_f64, say
+
+pytestmark = pytest.mark.gpu
+
+# small variants: span several tiles, a ragged tail, empty contexts, GQA, both head dims
+SMALL = {
+    "tiny": workloads.config("tiny"),
+    "bf16_gqa": workloads.config("ragged", B=3, ctx=(0, 300), Hq=8, Hkv=2, Dh=128, V=4096,
+                                 plant=True, seed_index=21),
+    "bf16_dh64": workloads.config("batched", B=2, ctx=200, Hq=4, Hkv=4, Dh=64, V=2048,
+                                  seed_index=22),
+    "f32_dh128": workloads.config("tiny", ctx=130, Hq=2, Hkv=2, Dh=128, seed_index=23),
+    "short_tree": workloads.config("tiny", D=2, K=2, budget=10, ctx=70, seed_index=24),
+    "chain_topk1": workloads.config("single", ctx=500, budget=7, K=1, D=8, V=4096,
+                                    seed_index=25),
+    "max_nodes": workloads.config("long", B=2, ctx=(64, 400), D=16, K=8, budget=127, Hq=2,
+                                  Hkv=2, V=2048, seed_index=26),
+    "odd_vocab": workloads.config("batched", B=2, ctx=100, V=1001, Hq=2, Hkv=2,
+                                  seed_index=27),
+}
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        cfg = SMALL.get(name) or workloads.config(name)
+        _cache[name] = Case(cfg)
+    return _cache[name]
+
+
+ALL = list(SMALL) + ["single", "batched", "long", "ragged"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_build(name):
+    c = case(name)
+    say("build", name, c.cfg)
+    t = c.gpu_tree()
+    torch.cuda.synchronize()
+    assert_tree_equal(t.to_numpy(), c.tree)
+
+
+def _temps(c):
+    return sorted({0.0, c.cfg.temperature, 0.8 if c.cfg.V <= 4096 else c.cfg.temperature})
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_vocab_reduce(name):
+    import tree_verification_build_amd as lib
+    c = case(name)
+    nn = c.tree["num_nodes"]
+    for T in _temps(c):
+        say("vocab", name, "T", T)
+        r = lib.ddtree_vocab_reduce(c.d("logits"), torch.from_numpy(nn).to("cuda:0"), T,
+                                    want_lse=True)
+        torch.cuda.synchronize()
+        ref = oracle.vocab_reduce(c.logits, nn, T, dtype=c.cfg.dtype)
+        assert np.array_equal(r["argmax"].cpu().numpy(), ref["argmax"])
+        assert np.array_equal(r["maxv"].cpu().numpy().view(np.uint32), ref["maxv"].view(np.uint32))
+        lse = r["lse"].cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref["lse"])
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.abs(lse[fin] - ref["lse"][fin]).max() <= 1e-4
+        if T > 0:
+            assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_verify_greedy(name):
+    import tree_verification_build_amd as lib
+    c = case(name)
+    say("verify_greedy", name)
+    t = c.gpu_tree()
+    ref_v = oracle.vocab_reduce(c.logits, c.tree["num_nodes"], 0.0, dtype=c.cfg.dtype)
+    # the walk consumes the GPU's own argmax, whose parity is pinned above
+    v = lib.ddtree_vocab_reduce(c.d("logits"), t.num_nodes, 0.0)
+    o = lib.ddtree_verify_greedy(t, v["argmax"])
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(c.tree, ref_v["argmax"], c.cfg.D)
+    for k in ref:
+        assert np.array_equal(o[k].cpu().numpy(), ref[k]), k
+    if c.cfg.plant:
+        assert ref["accept_len"].max() > 0
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_verify_sample(name):
+    import tree_verification_build_amd as lib
+    c = case(name)
+    T = c.cfg.temperature if c.cfg.temperature > 0 else 0.8
+    say("verify_sample", name, "T", T)
+    t = c.gpu_tree()
+    v = lib.ddtree_vocab_reduce(c.d("logits"), t.num_nodes, T)
+    o = lib.ddtree_verify_sample(t, c.d("logits"), v["maxv"], v["R"], T, c.d("uniforms"))
+    torch.cuda.synchronize()
+    ref_v = oracle.vocab_reduce(c.logits, c.tree["num_nodes"], T, dtype=c.cfg.dtype)
+    ref = oracle.verify_sample(c.tree, c.logits, ref_v["maxv"], ref_v["R"], T,
+                               c.inp["uniforms"], c.cfg.D, dtype=c.cfg.dtype)
+    for k in ref:
+        assert np.array_equal(o[k].cpu().numpy(), ref[k]), k
+
+
+def _attn_sample(c):
+    """(requests, heads) for the oracle: everything when small, a sample at full size."""
+    cfg = c.cfg
+    if name_is_full(cfg):
+        rng = np.random.default_rng(7)
+        reqs = sorted(set([0, cfg.B - 1] + list(rng.integers(0, cfg.B, size=min(cfg.B, 2)))))
+        heads = sorted(set([0, cfg.Hq - 1]))
+        return reqs, heads
+    return None, None
+
+
+def name_is_full(cfg):
+    return cfg.name in ("single", "batched", "long", "ragged") and cfg == workloads.config(cfg.name)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_tree_attention(name):
+    c = case(name)
+    say("attention", name, c.cfg)
+    t = c.gpu_tree()
+    out, lse = c.gpu_attention(t)
+    torch.cuda.synchronize()
+    reqs, heads = _attn_sample(c)
+    o_ref, lse_ref = c.oracle_attention(reqs, heads)
+    o = attn_to_f64(out)
+    err, scale = assert_attention_close(o, o_ref, c.cfg.dtype)
+    say("attention", name, "max abs err", err, "max |o|", scale)
+    l = lse.cpu().numpy().astype(np.float64)
+    sel = ~np.isnan(lse_ref) & np.isfinite(lse_ref)
+    assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
+    assert np.all(np.isneginf(l[np.isneginf(lse_ref)]))
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa", "single", "ragged"])
+def test_attention_deterministic(name):
+    c = case(name)
+    say("attention determinism", name)
+    t = c.gpu_tree()
+    a, _ = c.gpu_attention(t, want_lse=False)
+    b, _ = c.gpu_attention(t, want_lse=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+
+
+def test_attention_split_size_invariance(monkeypatch):
+    """Other context split sizes change only rounding, within tolerance."""
+    c = case("single")
+    t = c.gpu_tree()
+    base, _ = c.gpu_attention(t, want_lse=False)
+    for sk in ("64", "1024", "8192"):
+        monkeypatch.setenv("DDTREE_ATTN_SPLIT_KEYS", sk)
+        say("attention split keys", sk)
+        o, _ = c.gpu_attention(t, want_lse=False)
+        torch.cuda.synchronize()
+        d = (o.float() - base.float()).abs().max().item()
+        assert d <= 2e-2 * base.float().abs().max().item(), (sk, d)
+    monkeypatch.delenv("DDTREE_ATTN_SPLIT_KEYS")

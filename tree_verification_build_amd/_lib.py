@@ -1,0 +1,247 @@
+"""ctypes binding of libddtree.so (argument marshalling only)."""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libddtree.so")
+
+if not os.path.exists(library_path):
+    raise ImportError(f"{library_path} is missing: build it first (__graft_entry__.build() or "
+                      "python tree_verification_build_amd/_build.py)")
+lib = ctypes.CDLL(library_path)
+
+DDTREE_OK, DDTREE_EINVAL, DDTREE_EUNSUPPORTED, DDTREE_EDEVICE = 0, 1, 2, 3
+DDTREE_F32, DDTREE_BF16 = 0, 1
+_STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EDEVICE"}
+
+
+class DdtreeError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class _CTree(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("token", "parent", "depth", "rank", "position",
+                                               "first_child", "next_sibling", "score", "vis",
+                                               "num_nodes")] + \
+               [(n, ctypes.c_int32) for n in ("B", "N", "D", "K", "W")]
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_tp = ctypes.POINTER(_CTree)
+lib.ddtree_build.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _tp, _vp]
+lib.ddtree_tree_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp]
+lib.ddtree_tree_attention_workspace_size.restype = _sz
+lib.ddtree_tree_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32, _i32,
+                                      ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp]
+lib.ddtree_vocab_reduce_workspace_size.argtypes = [_i32, _i32, _i32]
+lib.ddtree_vocab_reduce_workspace_size.restype = _sz
+lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp,
+                                    _vp, _vp, _vp, _sz, _vp]
+lib.ddtree_verify_greedy.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
+                                     _vp, _vp, _vp]
+lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
+for _f in ("ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce", "ddtree_verify_greedy",
+           "ddtree_verify_sample", "ddtree_sampling_constants"):
+    getattr(lib, _f).restype = ctypes.c_int
+lib.ddtree_last_error.restype = ctypes.c_char_p
+lib.ddtree_version.restype = ctypes.c_char_p
+
+
+def ddtree_last_error() -> str:
+    return lib.ddtree_last_error().decode()
+
+
+def ddtree_version() -> str:
+    return lib.ddtree_version().decode()
+
+
+def _check(st):
+    if st != DDTREE_OK:
+        raise DdtreeError(st, ddtree_last_error())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DDTREE_BF16
+    if t.dtype == torch.float32:
+        return DDTREE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+class Tree:
+    """Device arrays of a token tree ([B, N] each; vis [B, N, W]; num_nodes [B])."""
+
+    FIELDS = ("token", "parent", "depth", "rank", "position", "first_child", "next_sibling")
+
+    def __init__(self, B, N, D, K, device):
+        self.B, self.N, self.D, self.K, self.W = B, N, D, K, (N + 63) // 64
+        for f in self.FIELDS:
+            setattr(self, f, torch.empty((B, N), dtype=torch.int32, device=device))
+        self.score = torch.empty((B, N), dtype=torch.float32, device=device)
+        self.vis = torch.empty((B, N, self.W), dtype=torch.int64, device=device)
+        self.num_nodes = torch.empty((B,), dtype=torch.int32, device=device)
+        self._c = _CTree(*[t.data_ptr() for t in (*[getattr(self, f) for f in self.FIELDS],
+                                                   self.score, self.vis, self.num_nodes)],
+                         B, N, D, K, self.W)
+
+    @property
+    def cstruct(self):
+        return ctypes.byref(self._c)
+
+    def to_numpy(self) -> dict:
+        out = {f: getattr(self, f).cpu().numpy() for f in self.FIELDS}
+        out["score"] = self.score.cpu().numpy()
+        out["vis"] = self.vis.cpu().numpy().view(np.uint64)
+        out["num_nodes"] = self.num_nodes.cpu().numpy()
+        return out
+
+
+def alloc_tree(B, budget, D, K, device="cuda") -> Tree:
+    return Tree(B, budget + 1, D, K, device)
+
+
+def ddtree_build(draft_lp, draft_tok, root_tok, prefix_len, budget, tree=None, stream=None):
+    """Best-first tree from draft_lp/draft_tok [B, D, K]; returns a Tree."""
+    B, D, K = draft_lp.shape
+    _dev(draft_lp, "draft_lp", torch.float32)
+    _dev(draft_tok, "draft_tok", torch.int32, (B, D, K))
+    _dev(root_tok, "root_tok", torch.int32, (B,))
+    _dev(prefix_len, "prefix_len", torch.int32, (B,))
+    if tree is None:
+        tree = alloc_tree(B, budget, D, K, draft_lp.device)
+    _check(lib.ddtree_build(_ptr(draft_lp), _ptr(draft_tok), _ptr(root_tok), _ptr(prefix_len),
+                            B, D, K, budget, tree.cstruct, _stream(stream)))
+    return tree
+
+
+def _host_offsets(ctx_offsets_host):
+    a = np.ascontiguousarray(np.asarray(ctx_offsets_host, dtype=np.int32))
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, ctx_offsets_host) -> int:
+    a, p = _host_offsets(ctx_offsets_host)
+    return int(lib.ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, p))
+
+
+def ddtree_tree_attention(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree, v_tree, tree,
+                          scale=None, out=None, want_lse=False, workspace=None, stream=None):
+    """Returns (out [B, N, Hq, Dh], lse [B, N, Hq] or None)."""
+    B, N, Hq, Dh = q.shape
+    Hkv = k_tree.shape[2]
+    _dev(q, "q", (torch.bfloat16, torch.float32))
+    _dev(k_tree, "k_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(v_tree, "v_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(k_ctx, "k_ctx", q.dtype)
+    _dev(v_ctx, "v_ctx", q.dtype, tuple(k_ctx.shape))
+    _dev(ctx_offsets, "ctx_offsets", torch.int32, (B + 1,))
+    hoff, hptr = _host_offsets(ctx_offsets_host)
+    if k_ctx.shape[0] < int(hoff[-1]) or tuple(k_ctx.shape[1:]) != (Hkv, Dh):
+        raise ValueError("k_ctx must be [ctx_offsets[B], Hkv, Dh]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, tuple(q.shape))
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    need = int(lib.ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, hptr))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(Dh) ** 0.5
+    _check(lib.ddtree_tree_attention(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), hptr, _ptr(k_tree), _ptr(v_tree),
+        tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), float(scale), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def ddtree_vocab_reduce_workspace_size(B, N, V) -> int:
+    return int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
+
+
+def ddtree_vocab_reduce(logits, num_nodes, temperature=0.0, want_lse=False, workspace=None,
+                        stream=None):
+    """Returns dict(argmax [B,N] i32, maxv [B,N] f32, R [B,N] int64 bits of uint64 or None,
+    lse [B,N] f32 or None)."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(num_nodes, "num_nodes", torch.int32, (B,))
+    dev = logits.device
+    argmax = torch.empty((B, N), dtype=torch.int32, device=dev)
+    maxv = torch.empty((B, N), dtype=torch.float32, device=dev)
+    R = torch.empty((B, N), dtype=torch.int64, device=dev) if temperature > 0 else None
+    lse = torch.empty((B, N), dtype=torch.float32, device=dev) if want_lse else None
+    need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check(lib.ddtree_vocab_reduce(_ptr(logits), _dtype_code(logits), B, N, V, _ptr(num_nodes),
+                                   float(temperature), _ptr(argmax), _ptr(maxv), _ptr(R),
+                                   _ptr(lse), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)))
+    return {"argmax": argmax, "maxv": maxv, "R": R, "lse": lse}
+
+
+def _walk_outputs(tree):
+    dev = tree.token.device
+    return {"accept_len": torch.empty((tree.B,), dtype=torch.int32, device=dev),
+            "path_nodes": torch.empty((tree.B, tree.D + 1), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((tree.B, tree.D + 1), dtype=torch.int32, device=dev),
+            "bonus": torch.empty((tree.B,), dtype=torch.int32, device=dev)}
+
+
+def ddtree_verify_greedy(tree, argmax, outputs=None, stream=None):
+    _dev(argmax, "argmax", torch.int32, (tree.B, tree.N))
+    o = outputs or _walk_outputs(tree)
+    _check(lib.ddtree_verify_greedy(tree.cstruct, _ptr(argmax), _ptr(o["accept_len"]),
+                                    _ptr(o["path_nodes"]), _ptr(o["out_tokens"]),
+                                    _ptr(o["bonus"]), _stream(stream)))
+    return o
+
+
+def ddtree_verify_sample(tree, logits, maxv, R, temperature, uniforms, outputs=None,
+                         stream=None):
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(maxv, "maxv", torch.float32, (B, N))
+    _dev(R, "R", torch.int64, (B, N))
+    _dev(uniforms, "uniforms", torch.int64, (B, N, 2))
+    o = outputs or _walk_outputs(tree)
+    _check(lib.ddtree_verify_sample(tree.cstruct, _ptr(logits), _dtype_code(logits), V,
+                                    _ptr(maxv), _ptr(R), float(temperature), _ptr(uniforms),
+                                    _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
+                                    _ptr(o["out_tokens"]), _ptr(o["bonus"]), _stream(stream)))
+    return o
+
+
+def ddtree_sampling_constants(temperature):
+    """(c, a[7]) the library uses for the integer softmax weights at this temperature."""
+    c = ctypes.c_float()
+    a = (ctypes.c_float * 7)()
+    _check(lib.ddtree_sampling_constants(float(temperature), ctypes.byref(c), a))
+    return np.float32(c.value), np.array(list(a), dtype=np.float32)

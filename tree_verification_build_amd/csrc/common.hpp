@@ -1,0 +1,136 @@
+// Shared device helpers for the libddtree kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ddtree.h"
+
+namespace ddt {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- host side errors
+ddtree_status fail(ddtree_status st, const char* fmt, ...);
+ddtree_status check_launch(const char* what);
+__host__ __device__ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------- scalar conversions
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Monotone map float -> uint32 (a < b  <=>  ord(a) < ord(b)); -0.0 is first
+// turned into +0.0 so that the two zeros compare equal, as they do as floats.
+__device__ __forceinline__ uint32_t ord_f32(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------- wave reductions
+// Max over the 16 lanes of each DPP row, via quad_perm and row_ror moves.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  return v;
+}
+
+// Wave-uniform max of a uint32 over all 64 lanes (all lanes must be active).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row_max_u32(v);
+  uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Wave-uniform max of a uint64 (lexicographic on the two halves).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
+  uint32_t lo = wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
+  return __shfl_up(v, d, kWave);
+}
+
+// Inclusive prefix sum of a uint64 across the wave (exact integer arithmetic).
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint64_t o = shfl_up_u64(v, d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- sampling weights
+// Constants of the integer softmax weights for one temperature.
+struct WeightConsts {
+  float c;      // fp32(log2(e) / T)
+  float a[7];   // fp32((ln 2)^n / n!)
+};
+
+WeightConsts weight_consts(float temperature);  // host
+
+// w(l) = floor(p * 2^(32+k)) with y = (l - m) * c, k = rint(y), f = y - k and
+// p the degree-6 Taylor polynomial of 2^f, every multiply and add rounded to
+// fp32 on its own (no fused multiply-add); w = 0 when y < -32.  p * 2^24 is an
+// exact integer P, so w = P * 2^(8+k), done with integer shifts.  Branch-free:
+// a cut-off y is clamped to -32 for the arithmetic and its result discarded.
+__device__ __forceinline__ uint64_t weight(float l, float m, const WeightConsts& wc) {
+#pragma clang fp contract(off)
+  const float y0 = (l - m) * wc.c;
+  const bool keep = y0 >= -32.0f;
+  const float y = keep ? y0 : -32.0f;
+  float k = __builtin_rintf(y);
+  float f = y - k;
+  float p = wc.a[6];
+  p = p * f; p = p + wc.a[5];
+  p = p * f; p = p + wc.a[4];
+  p = p * f; p = p + wc.a[3];
+  p = p * f; p = p + wc.a[2];
+  p = p * f; p = p + wc.a[1];
+  p = p * f; p = p + wc.a[0];
+  uint32_t P = static_cast<uint32_t>(p * 16777216.0f);
+  const int e = 8 + static_cast<int>(k);
+  const uint64_t w = e >= 0 ? (static_cast<uint64_t>(P) << e) : static_cast<uint64_t>(P >> (-e));
+  return keep ? w : 0ull;
+}
+
+// ---------------------------------------------------------------- element access
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPer16 = 4;
+  __device__ __forceinline__ static float get(const float* p, long i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kPer16 = 8;
+  __device__ __forceinline__ static float get(const uint16_t* p, long i) {
+    return bf16_to_f32(p[i]);
+  }
+};
+
+}  // namespace ddt

@@ -1,0 +1,499 @@
+// ddtree_vocab_reduce: one pass over the target logits of every tree node.
+//
+// "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1 step 4
+// (argmax at every node) and Section 3 (softmax at temperature T).
+//
+// Greedy mode streams each row in S slices: a workgroup of 256 threads reads
+// its slice with 16-byte coalesced loads and reduces a packed 64-bit key
+// (order-preserving value bits << 32 | ~token id), whose maximum is the
+// largest logit at the lowest id; it also keeps a running (max, sum exp) for
+// the optional log-sum-exp.  When a row is split (S > 1) a small finalize
+// kernel merges the S partial results.  Integer keys make the merge order
+// irrelevant, so the argmax is the same for any S.
+//
+// Sampling mode needs the row maximum before any weight can be formed, so one
+// 1024-thread workgroup owns a row and keeps it in registers: one HBM read,
+// then the max/argmax reduction, then the exact 64-bit sum of the integer
+// weights (common.hpp: weight()).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace ddt {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSplitThreads = 256;
+constexpr int kRowThreads = 1024;
+
+// 16 bytes of logits (E = 8 bf16 or 4 fp32 values): raw bits and their floats.
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int E = 8;
+  __device__ __forceinline__ static void unpack(const u32x4_t& r, float* v) {
+    const u32x4_t w = r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(w[k] << 16);
+      v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
+  // element-wise gather with -inf (0xFF80) past `lim`
+  __device__ __forceinline__ static u32x4_t gather(const uint16_t* row, long i, long lim) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t a = (i + 2 * k < lim) ? row[i + 2 * k] : 0xFF80u;
+      const uint32_t b = (i + 2 * k + 1 < lim) ? row[i + 2 * k + 1] : 0xFF80u;
+      w[k] = a | (b << 16);
+    }
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
+};
+template <> struct Vec<float> {
+  static constexpr int E = 4;
+  __device__ __forceinline__ static void unpack(const u32x4_t& r, float* v) {
+    v[0] = __uint_as_float(r[0]);
+    v[1] = __uint_as_float(r[1]);
+    v[2] = __uint_as_float(r[2]);
+    v[3] = __uint_as_float(r[3]);
+  }
+  __device__ __forceinline__ static u32x4_t gather(const float* row, long i, long lim) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = (i + k < lim) ? __float_as_uint(row[i + k]) : 0xFF800000u;
+    return u32x4_t{w[0], w[1], w[2], w[3]};
+  }
+  static constexpr uint32_t kNegInfWord = 0xFF800000u;
+};
+
+// Raw 16 bytes of logits starting at index i; elements at or past `lim`
+// read as -inf.  `vec` says the row base is 16-byte aligned.
+template <typename T>
+__device__ __forceinline__ u32x4_t load_raw(const T* row, long i, long lim, bool vec) {
+  constexpr int E = Vec<T>::E;
+  if (vec && i + E <= lim) return *reinterpret_cast<const u32x4_t*>(row + i);
+  if (i >= lim) {
+    const uint32_t z = Vec<T>::kNegInfWord;
+    return u32x4_t{z, z, z, z};
+  }
+  return Vec<T>::gather(row, i, lim);
+}
+
+template <typename T>
+__device__ __forceinline__ void load_e(const T* row, long i, long lim, bool vec, float* v) {
+  Vec<T>::unpack(load_raw<T>(row, i, lim, vec), v);
+}
+
+__device__ __forceinline__ uint64_t pack_key(float v, int idx) {
+  return (static_cast<uint64_t>(ord_f32(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+
+// Running (max, sum exp(x - max)) merge.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+  } else if (m2 > -__builtin_huge_valf()) {
+    s += s2 * __expf(m2 - m);
+  }
+}
+
+template <typename T, bool kLse>
+__global__ __launch_bounds__(kSplitThreads) void split_kernel(
+    const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes, int S,
+    int chunk, uint64_t* __restrict__ ws_key, float2* __restrict__ ws_ms,
+    int32_t* __restrict__ argmax, float* __restrict__ maxv, float* __restrict__ lse) {
+  constexpr int E = Vec<T>::E;
+  __shared__ uint64_t s_key[kSplitThreads / kWave];
+  __shared__ float2 s_ms[kSplitThreads / kWave];
+  const int row = blockIdx.y;
+  const int s = blockIdx.x;
+  const int b = row / N, n = row % N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool valid = n < num_nodes[b];
+  uint64_t key = 0;
+  float m = -__builtin_huge_valf(), sum = 0.0f;
+  if (valid) {
+    const T* rp = logits + static_cast<long>(row) * V;
+    const bool vec = aligned16(rp);
+    const int lo = s * chunk, hi = min(V, lo + chunk);
+    for (int i = lo + tid * E; i < hi; i += kSplitThreads * E) {
+      float v[E];
+      load_e<T>(rp, i, hi, vec, v);
+      float vm = v[0];
+      int vi = 0;
+#pragma unroll
+      for (int k = 1; k < E; ++k)
+        if (v[k] > vm) { vm = v[k]; vi = k; }
+      const uint64_t kk = pack_key(vm, i + vi);
+      key = kk > key ? kk : key;
+      if (kLse) {
+        float es = 0.0f;
+        const float mm = max(m, vm);
+#pragma unroll
+        for (int k = 0; k < E; ++k) es += __expf(v[k] - mm);
+        sum = (m > -__builtin_huge_valf() ? sum * __expf(m - mm) : 0.0f) + es;
+        m = mm;
+      }
+    }
+  }
+  key = wave_max_u64(key);
+  if (kLse) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float m2 = shfl_xor_f32(m, o), s2 = shfl_xor_f32(sum, o);
+      lse_merge(m, sum, m2, s2);
+    }
+  }
+  if (lane == 0) {
+    s_key[wave] = key;
+    s_ms[wave] = make_float2(m, sum);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kSplitThreads / kWave; ++w) {
+      key = s_key[w] > key ? s_key[w] : key;
+      if (kLse) lse_merge(m, sum, s_ms[w].x, s_ms[w].y);
+    }
+    if (S == 1) {
+      argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
+      maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
+      if (kLse) lse[row] = valid ? m + __logf(sum) : -__builtin_huge_valf();
+    } else {
+      ws_key[static_cast<long>(row) * S + s] = valid ? key : 0ull;
+      if (kLse) ws_ms[static_cast<long>(row) * S + s] = make_float2(m, sum);
+    }
+  }
+}
+
+template <bool kLse>
+__global__ __launch_bounds__(256) void finalize_kernel(int rows, int N, const int32_t* __restrict__ num_nodes,
+                                                       int S, const uint64_t* __restrict__ ws_key,
+                                                       const float2* __restrict__ ws_ms,
+                                                       int32_t* __restrict__ argmax,
+                                                       float* __restrict__ maxv,
+                                                       float* __restrict__ lse) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= rows) return;
+  const int b = row / N, n = row % N;
+  if (n >= num_nodes[b]) {
+    argmax[row] = -1;
+    maxv[row] = -__builtin_huge_valf();
+    if (kLse) lse[row] = -__builtin_huge_valf();
+    return;
+  }
+  uint64_t key = 0;
+  float m = -__builtin_huge_valf(), sum = 0.0f;
+  for (int s = 0; s < S; ++s) {
+    const uint64_t k = ws_key[static_cast<long>(row) * S + s];
+    key = k > key ? k : key;
+    if (kLse) {
+      const float2 ms = ws_ms[static_cast<long>(row) * S + s];
+      lse_merge(m, sum, ms.x, ms.y);
+    }
+  }
+  argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+  maxv[row] = unord_f32(static_cast<uint32_t>(key >> 32));
+  if (kLse) lse[row] = m + __logf(sum);
+}
+
+// Sampling mode: one workgroup per row, row held in registers (MAXP 16-byte
+// vectors per thread, covering up to MAXP * 1024 * E logits).
+template <typename T, int MAXP, bool kLse>
+__global__ __launch_bounds__(kRowThreads) void row_kernel(
+    const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
+    WeightConsts wc, int32_t* __restrict__ argmax, float* __restrict__ maxv,
+    uint64_t* __restrict__ R, float* __restrict__ lse) {
+  constexpr int E = Vec<T>::E;
+  constexpr int kWaves = kRowThreads / kWave;
+  __shared__ uint64_t s_u[kWaves];
+  __shared__ float s_f[kWaves];
+  const int row = blockIdx.x;
+  const int b = row / N, n = row % N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n >= num_nodes[b]) {
+    if (tid == 0) {
+      argmax[row] = -1;
+      maxv[row] = -__builtin_huge_valf();
+      R[row] = 0;
+      if (kLse) lse[row] = -__builtin_huge_valf();
+    }
+    return;
+  }
+  // rows are 16-byte aligned and V is a multiple of E here (checked on the host)
+  const T* rp = logits + static_cast<long>(row) * V;
+  u32x4_t raw[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const long i = static_cast<long>(p) * kRowThreads * E + tid * E;
+    const uint32_t z = Vec<T>::kNegInfWord;
+    raw[p] = i < V ? *reinterpret_cast<const u32x4_t*>(rp + i) : u32x4_t{z, z, z, z};
+  }
+  uint64_t key = 0;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    float v[E];
+    Vec<T>::unpack(raw[p], v);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const uint64_t kk = pack_key(v[k], p * kRowThreads * E + tid * E + k);
+      key = kk > key ? kk : key;
+    }
+    __builtin_amdgcn_sched_barrier(0);   // one pass at a time: bounds live registers
+  }
+  key = wave_max_u64(key);
+  if (lane == 0) s_u[wave] = key;
+  __syncthreads();
+  key = s_u[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) key = s_u[w] > key ? s_u[w] : key;
+  const float m = unord_f32(static_cast<uint32_t>(key >> 32));
+  __syncthreads();
+
+  uint64_t wsum = 0;
+  float esum = 0.0f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    // opaque to the optimiser: stops it from keeping the first pass's
+    // unpacked floats alive (160 of them) instead of the packed raw bits
+    __asm__ volatile("" : "+v"(raw[p]));
+    float v[E];
+    Vec<T>::unpack(raw[p], v);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      wsum += weight(v[k], m, wc);
+      if (kLse) esum += __expf(v[k] - m);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  wsum = wave_sum_u64(wsum);
+  if (kLse) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) esum += shfl_xor_f32(esum, o);
+  }
+  if (lane == 0) {
+    s_u[wave] = wsum;
+    s_f[wave] = esum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tot = 0;
+    float et = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      tot += s_u[w];
+      et += s_f[w];
+    }
+    argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+    maxv[row] = m;
+    R[row] = tot;
+    if (kLse) lse[row] = m + __logf(et);
+  }
+}
+
+// Sampling mode for rows too long for registers: two passes over the row.
+template <typename T, bool kLse>
+__global__ __launch_bounds__(kRowThreads) void row2_kernel(
+    const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
+    WeightConsts wc, int32_t* __restrict__ argmax, float* __restrict__ maxv,
+    uint64_t* __restrict__ R, float* __restrict__ lse) {
+  constexpr int E = Vec<T>::E;
+  constexpr int kWaves = kRowThreads / kWave;
+  __shared__ uint64_t s_u[kWaves];
+  __shared__ float s_f[kWaves];
+  const int row = blockIdx.x;
+  const int b = row / N, n = row % N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (n >= num_nodes[b]) {
+    if (tid == 0) {
+      argmax[row] = -1;
+      maxv[row] = -__builtin_huge_valf();
+      R[row] = 0;
+      if (kLse) lse[row] = -__builtin_huge_valf();
+    }
+    return;
+  }
+  const T* rp = logits + static_cast<long>(row) * V;
+  const bool vec = aligned16(rp);
+  uint64_t key = 0;
+  for (long i = static_cast<long>(tid) * E; i < V; i += kRowThreads * E) {
+    float v[E];
+    load_e<T>(rp, i, V, vec, v);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      const uint64_t kk = pack_key(v[k], static_cast<int>(i) + k);
+      key = kk > key ? kk : key;
+    }
+  }
+  key = wave_max_u64(key);
+  if (lane == 0) s_u[wave] = key;
+  __syncthreads();
+  key = s_u[0];
+  for (int w = 1; w < kWaves; ++w) key = s_u[w] > key ? s_u[w] : key;
+  const float m = unord_f32(static_cast<uint32_t>(key >> 32));
+  __syncthreads();
+  uint64_t wsum = 0;
+  float esum = 0.0f;
+  for (long i = static_cast<long>(tid) * E; i < V; i += kRowThreads * E) {
+    float v[E];
+    load_e<T>(rp, i, V, vec, v);
+#pragma unroll
+    for (int k = 0; k < E; ++k) {
+      wsum += weight(v[k], m, wc);
+      if (kLse) esum += __expf(v[k] - m);
+    }
+  }
+  wsum = wave_sum_u64(wsum);
+  if (kLse) {
+    for (int o = 32; o >= 1; o >>= 1) esum += shfl_xor_f32(esum, o);
+  }
+  if (lane == 0) {
+    s_u[wave] = wsum;
+    s_f[wave] = esum;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tot = 0;
+    float et = 0.0f;
+    for (int w = 0; w < kWaves; ++w) {
+      tot += s_u[w];
+      et += s_f[w];
+    }
+    argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+    maxv[row] = m;
+    R[row] = tot;
+    if (kLse) lse[row] = m + __logf(et);
+  }
+}
+
+// Split count for the greedy pass: enough workgroups to cover the chip
+// (about 1024 resident), each slice a whole number of 16-byte vectors per thread.
+void split_plan(int rows, int V, int elem_bytes, int* S_out, int* chunk_out) {
+  const int per_pass = kSplitThreads * (16 / elem_bytes);
+  int S = std::max(1, std::min((1024 + rows - 1) / rows, (V + per_pass - 1) / per_pass));
+  int chunk = (V + S - 1) / S;
+  chunk = (chunk + per_pass - 1) / per_pass * per_pass;
+  S = (V + chunk - 1) / chunk;
+  *S_out = S;
+  *chunk_out = chunk;
+}
+
+template <typename T, int MAXP>
+void launch_row(dim3 grid, hipStream_t st, const void* logits, int N, int V, const int32_t* nn,
+                const WeightConsts& wc, int32_t* am, float* mx, uint64_t* R, float* lse) {
+  if (lse)
+    hipLaunchKernelGGL((row_kernel<T, MAXP, true>), grid, dim3(kRowThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+  else
+    hipLaunchKernelGGL((row_kernel<T, MAXP, false>), grid, dim3(kRowThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+}
+
+template <typename T>
+void launch_sampling(int rows, hipStream_t st, const void* logits, int N, int V,
+                     const int32_t* nn, const WeightConsts& wc, int32_t* am, float* mx,
+                     uint64_t* R, float* lse) {
+  const int per_pass = kRowThreads * Vec<T>::E;
+  const int passes = (V + per_pass - 1) / per_pass;
+  const bool fits = V % Vec<T>::E == 0 && aligned16(logits);
+  const dim3 g(rows);
+  if (!fits) {
+    if (lse)
+      hipLaunchKernelGGL((row2_kernel<T, true>), g, dim3(kRowThreads), 0, st,
+                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+    else
+      hipLaunchKernelGGL((row2_kernel<T, false>), g, dim3(kRowThreads), 0, st,
+                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+  } else if (passes <= 1) launch_row<T, 1>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 2) launch_row<T, 2>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 4) launch_row<T, 4>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 8) launch_row<T, 8>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 12) launch_row<T, 12>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 16) launch_row<T, 16>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (passes <= 20) launch_row<T, 20>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+  else if (lse)
+    hipLaunchKernelGGL((row2_kernel<T, true>), g, dim3(kRowThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+  else
+    hipLaunchKernelGGL((row2_kernel<T, false>), g, dim3(kRowThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+}
+
+template <typename T>
+void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
+                   int S, int chunk, void* ws, int32_t* am, float* mx, float* lse) {
+  uint64_t* ws_key = static_cast<uint64_t*>(ws);
+  float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<long>(rows) * S);
+  const dim3 grid(S, rows);
+  if (lse)
+    hipLaunchKernelGGL((split_kernel<T, true>), grid, dim3(kSplitThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx, lse);
+  else
+    hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx, lse);
+  if (S > 1) {
+    const dim3 g2((rows + 255) / 256);
+    if (lse)
+      hipLaunchKernelGGL(finalize_kernel<true>, g2, dim3(256), 0, st, rows, N, nn, S, ws_key,
+                         ws_ms, am, mx, lse);
+    else
+      hipLaunchKernelGGL(finalize_kernel<false>, g2, dim3(256), 0, st, rows, N, nn, S, ws_key,
+                         ws_ms, am, mx, lse);
+  }
+}
+
+}  // namespace
+}  // namespace ddt
+
+extern "C" size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32_t V) {
+  if (B < 1 || N < 1 || V < 1) return 0;
+  int S2, S4, chunk;
+  ddt::split_plan(B * N, V, 2, &S2, &chunk);
+  ddt::split_plan(B * N, V, 4, &S4, &chunk);
+  const int S = S2 > S4 ? S2 : S4;               // covers both element sizes
+  if (S <= 1) return 0;
+  return static_cast<size_t>(B) * N * S * (sizeof(uint64_t) + 2 * sizeof(float));
+}
+
+extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_t B,
+                                             int32_t N, int32_t V, const int32_t* num_nodes,
+                                             float temperature, int32_t* argmax, float* maxv,
+                                             uint64_t* R, float* lse, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+  using namespace ddt;
+  if (!logits || !num_nodes || !argmax || !maxv)
+    return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: null pointer");
+  if (B < 1 || N < 1 || N > DDTREE_MAX_NODES || V < 1)
+    return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: sizes out of range (B=%d N=%d V=%d)", B, N, V);
+  if (!(temperature >= 0.0f) || !(temperature < __builtin_huge_valf()))
+    return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: temperature must be >= 0 and finite");
+  if (dtype != DDTREE_BF16 && dtype != DDTREE_F32)
+    return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: unknown dtype %d", static_cast<int>(dtype));
+  const int rows = B * N;
+  if (temperature > 0.0f) {
+    if (!R) return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: R is required when temperature > 0");
+    const WeightConsts wc = weight_consts(temperature);
+    if (dtype == DDTREE_BF16)
+      launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, lse);
+    else
+      launch_sampling<float>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, lse);
+    return check_launch("ddtree_vocab_reduce");
+  }
+  int S, chunk;
+  split_plan(rows, V, dtype == DDTREE_BF16 ? 2 : 4, &S, &chunk);
+  if (S > 1) {
+    const size_t need = static_cast<size_t>(rows) * S * (sizeof(uint64_t) + 2 * sizeof(float));
+    if (!workspace || workspace_bytes < need)
+      return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: workspace of %zu bytes needed, got %zu",
+                  need, workspace_bytes);
+  }
+  if (dtype == DDTREE_BF16)
+    launch_greedy<uint16_t>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
+                            maxv, lse);
+  else
+    launch_greedy<float>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
+                         maxv, lse);
+  return check_launch("ddtree_vocab_reduce");
+}
