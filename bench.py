@@ -1,0 +1,278 @@
+"""Benchmark: DDTree tree-verify steps/s on one MI355X.
+
+One step = ddtree_build -> ddtree_tree_attention -> ddtree_vocab_reduce ->
+ddtree_verify_greedy (or ddtree_verify_sample when the workload samples), then
+a device-to-host copy of accept_len and bonus and a stream synchronisation
+(the serving loop's per-step sync).  By default each step is a captured HIP
+graph replayed once per step (--eager launches every call from Python).  Inputs are seeded synthetic tensors of
+the workload's shapes, resident in HBM before timing starts; several copies
+of the input set are rotated so that consecutive steps do not find their
+inputs in the 256 MB last-level cache.
+
+Prints one JSON line: steps/s, a roofline entry for the tree-attention call
+(algorithmic bytes / measured duration vs 8 TB/s), and the CPU oracle timed on
+the host cores for the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tree-verify steps/s at 1 GPU (budget=32); KV+vocab HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15         # dense bf16
+MFMA_F32_PEAK = 157.3e12
+
+
+def describe(cfg):
+    ctx = cfg.ctx if not isinstance(cfg.ctx, tuple) else f"U[{cfg.ctx[0]},{cfg.ctx[1]}]"
+    mode = "greedy" if cfg.temperature == 0 else f"T={cfg.temperature} rejection sampling"
+    return (f"{cfg.name}: batch {cfg.B}, context {ctx}, {cfg.Hq}/{cfg.Hkv} heads, head_dim "
+            f"{cfg.Dh}, {cfg.dtype}; depth {cfg.D}, budget {cfg.budget}, top-k cap {cfg.K}; "
+            f"vocab {cfg.V}; {mode}")
+
+
+def algorithmic_bytes(cfg, total_ctx):
+    """Bytes the step must move at least once (context KV once, tree Q/K/V/O, logits once)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    kv = 2 * total_ctx * cfg.Hkv * cfg.Dh * e
+    tree_qkvo = cfg.B * cfg.N * cfg.Dh * e * (2 * cfg.Hq + 2 * cfg.Hkv)
+    logits = cfg.B * cfg.N * cfg.V * e
+    residual = cfg.B * cfg.V * e if cfg.temperature > 0 else 0
+    return {"attention": kv + tree_qkvo, "vocab": logits, "residual": residual,
+            "total": kv + tree_qkvo + logits + residual}
+
+
+def attention_flops(cfg, total_ctx):
+    return 4.0 * cfg.N * total_ctx * cfg.Hq * cfg.Dh
+
+
+def run_gpu(cfg, steps, warmup, rotate, graph=True):
+    import torch
+    import tree_verification_build_amd as lib
+    import workloads
+
+    dev = "cuda:0"
+    inp = workloads.make_inputs(cfg)
+    tot_ctx = int(inp["ctx_offsets"][-1])
+
+    def d(x, dt=None):
+        x = np.ascontiguousarray(x)
+        if dt == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x.view(np.int64) if x.dtype == np.uint64 else x).to(dev)
+
+    base = {k: d(inp[k], cfg.dtype) for k in ("q", "k_ctx", "v_ctx", "k_tree", "v_tree")}
+    small = {k: d(inp[k]) for k in ("draft_lp", "draft_tok", "root_tok", "prefix_len",
+                                     "ctx_offsets", "uniforms")}
+    # the target logits depend on the tree shape: build it once on the GPU
+    t0 = lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                          small["prefix_len"], cfg.budget)
+    torch.cuda.synchronize()
+    tn = t0.to_numpy()
+    logits_np, _ = workloads.make_target_logits(cfg, inp, tn["depth"], tn["num_nodes"])
+    base["logits"] = d(logits_np, cfg.dtype)
+    del logits_np
+
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(rotate - 1)]
+    tree = lib.alloc_tree(cfg.B, cfg.budget, cfg.D, cfg.K, dev)
+    outputs = {"accept_len": torch.empty(cfg.B, dtype=torch.int32, device=dev),
+               "path_nodes": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
+               "out_tokens": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
+               "bonus": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
+    attn_out = torch.empty_like(base["q"])
+    ws_a = torch.empty(max(16, lib.ddtree_tree_attention_workspace_size(
+        cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, inp["ctx_offsets"])), dtype=torch.uint8,
+        device=dev)
+    ws_v = torch.zeros(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
+                       dtype=torch.uint8, device=dev)
+    host_acc = torch.empty(cfg.B, dtype=torch.int32, pin_memory=True)
+    host_bonus = torch.empty(cfg.B, dtype=torch.int32, pin_memory=True)
+    stream = torch.cuda.current_stream()
+    T = cfg.temperature
+
+    def attention(s):
+        lib.ddtree_tree_attention(s["q"], s["k_ctx"], s["v_ctx"], small["ctx_offsets"],
+                                  inp["ctx_offsets"], s["k_tree"], s["v_tree"], tree,
+                                  out=attn_out, workspace=ws_a)
+
+    def vocab(s):
+        return lib.ddtree_vocab_reduce(s["logits"], tree.num_nodes, T, workspace=ws_v)
+
+    def step(i):
+        s = sets[i % rotate]
+        lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                         small["prefix_len"], cfg.budget, tree=tree)
+        attention(s)
+        v = vocab(s)
+        if T > 0:
+            lib.ddtree_verify_sample(tree, s["logits"], v["maxv"], v["R"], T,
+                                     small["uniforms"], outputs=outputs)
+        else:
+            lib.ddtree_verify_greedy(tree, v["argmax"], outputs=outputs)
+        host_acc.copy_(outputs["accept_len"], non_blocking=True)
+        host_bonus.copy_(outputs["bonus"], non_blocking=True)
+
+    for i in range(warmup):
+        step(i)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    if graph:
+        # one captured step per input set; replaying it is the serving loop
+        graphs = []
+        for i in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(warmup):
+            graphs[i % rotate].replay()
+            stream.synchronize()
+        run = lambda i: graphs[i % rotate].replay()  # noqa: E731
+    else:
+        run = step
+    # timed: per-step synchronised serving loop (step + D2H of accept_len/bonus + sync)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        run(i)
+        stream.synchronize()
+    t_sync = time.perf_counter() - t_start
+    # pipelined: the same steps without the per-step synchronisation
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(steps):
+        run(i)
+    torch.cuda.synchronize()
+    t_pipe = time.perf_counter() - t_start
+
+    # kernel durations: a HIP graph of back-to-back calls over the rotated input sets,
+    # replayed between two HIP events on this stream (no host gaps fall inside)
+    def timed_calls(fn, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(rotate):
+                fn(sets[i])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * rotate)
+    reps = max(1, steps // rotate)
+    attn_ms = timed_calls(attention, reps)
+    vocab_ms = timed_calls(vocab, reps)
+    return {"t_sync": t_sync, "t_pipe": t_pipe, "attn_ms": attn_ms, "vocab_ms": vocab_ms,
+            "total_ctx": tot_ctx, "accept_len_mean": float(host_acc.float().mean())}
+
+
+def run_cpu_baseline(cfg, seconds):
+    """The oracle as it stands, same workload, on the host cores (one step = build,
+    float64 attention, vocabulary pass, walk)."""
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    inp = workloads.make_inputs(cfg)
+    t = oracle.build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"], inp["prefix_len"],
+                          cfg.budget)
+    logits, _ = workloads.make_target_logits(cfg, inp, t["depth"], t["num_nodes"])
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        tr = oracle.build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"],
+                               inp["prefix_len"], cfg.budget)
+        oracle.tree_attention(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
+                              inp["k_tree"], inp["v_tree"], tr["vis"], tr["num_nodes"],
+                              dtype=cfg.dtype)
+        vr = oracle.vocab_reduce(logits, tr["num_nodes"], cfg.temperature, dtype=cfg.dtype)
+        if cfg.temperature > 0:
+            oracle.verify_sample(tr, logits, vr["maxv"], vr["R"], cfg.temperature,
+                                 inp["uniforms"], cfg.D, dtype=cfg.dtype)
+        else:
+            oracle.verify_greedy(tr, vr["argmax"], cfg.D)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} full oracle steps of the {cfg.name} workload in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="single")
+    ap.add_argument("--rotate", type=int, default=0, help="input sets (0: >= 1 GiB in total)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every call from Python instead of replaying a HIP graph")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the verify path here is built and timed on a "
+              "single MI355X (no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import workloads
+    cfg = workloads.config(args.config)
+    offs = np.concatenate([[0], np.cumsum(workloads.ctx_lengths(cfg))])
+    ab = algorithmic_bytes(cfg, int(offs[-1]))
+    rotate = args.rotate or int(max(1, min(32, np.ceil(2 ** 30 / ab["total"]))))
+    r = run_gpu(cfg, args.steps, args.warmup, rotate, graph=not args.eager)
+    steps_s = args.steps / r["t_sync"]
+    attn_gbs = ab["attention"] / (r["attn_ms"] * 1e-3) / 1e9
+    vocab_gbs = ab["vocab"] / (r["vocab_ms"] * 1e-3) / 1e9
+    flops = attention_flops(cfg, r["total_ctx"])
+    mfma_peak = MFMA_BF16_PEAK if cfg.dtype == "bf16" else MFMA_F32_PEAK
+    line = {
+        "metric": METRIC,
+        "value": round(steps_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * r["t_sync"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "B": cfg.B, "ctx_tokens": r["total_ctx"],
+                   "heads_q": cfg.Hq, "heads_kv": cfg.Hkv, "head_dim": cfg.Dh, "depth": cfg.D,
+                   "budget": cfg.budget, "topk_cap": cfg.K, "vocab": cfg.V,
+                   "temperature": cfg.temperature, "input_sets_rotated": rotate,
+                   "launch": "eager" if args.eager else "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "ddtree_tree_attention",
+                     "bytes_per_launch": ab["attention"], "avg_ms": round(r["attn_ms"], 5)},
+        "pipelined_steps_per_s": round(args.steps / r["t_pipe"], 2),
+        "vocab_reduce": {"achieved_GBs": round(vocab_gbs, 1), "avg_ms": round(r["vocab_ms"], 5),
+                         "bytes_per_launch": ab["vocab"]},
+        "attention_plus_vocab_GBs": round((ab["attention"] + ab["vocab"]) /
+                                          ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9, 1),
+        "mfma_util": round(flops / (r["attn_ms"] * 1e-3) / mfma_peak, 4),
+        "accept_len_mean": r["accept_len_mean"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = run_cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -88,13 +88,14 @@ struct PolicyBF16 {
   }
   // store one 4-key block (keys key0..key0+3, 16-byte column e) to LDS
   template <int KT>
-  __device__ __forceinline__ static void store_block(elem* k_lds, elem* vt_lds, int key0, int e, const u32x4_t (&kr)[4],
-                                     const u32x4_t (&vr)[4]) {
+  __device__ __forceinline__ static void store_block(elem* k_lds, elem* vt_lds, int key0, int e,
+                                                     int vkey0, int ve, const u32x4_t (&kr)[4],
+                                                     const u32x4_t (&vr)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       *reinterpret_cast<u32x4_t*>(k_lds + (key0 + c) * k_stride<KT>() + e * 8) = kr[c];
     // V^T: within a 32-key group, key 16a + 4g + c lives at position 8g + 4a + c
-    const int grp = key0 >> 5, kk = key0 & 31;
+    const int grp = vkey0 >> 5, kk = vkey0 & 31;
     const int pos = grp * 32 + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4);
     const u32x4_t w0 = vr[0], w1 = vr[1], w2 = vr[2], w3 = vr[3];
 #pragma unroll
@@ -108,7 +109,7 @@ struct PolicyBF16 {
         lo = (w0[h] & 0xFFFFu) | (w1[h] << 16);
         hi = (w2[h] & 0xFFFFu) | (w3[h] << 16);
       }
-      *reinterpret_cast<u32x2_t*>(vt_lds + (e * 8 + t) * v_stride<KT>() + pos) = u32x2_t{lo, hi};
+      *reinterpret_cast<u32x2_t*>(vt_lds + (ve * 8 + t) * v_stride<KT>() + pos) = u32x2_t{lo, hi};
     }
   }
   // S^T block (16 keys from kbase) against this wave's 16 queries
@@ -163,12 +164,13 @@ struct PolicyF32 {
     for (int s = 0; s < QF; ++s) qf.f[s] = qrow[4 * s + g];
   }
   template <int KT>
-  __device__ __forceinline__ static void store_block(elem* k_lds, elem* v_lds, int key0, int e, const u32x4_t (&kr)[4],
-                                     const u32x4_t (&vr)[4]) {
+  __device__ __forceinline__ static void store_block(elem* k_lds, elem* v_lds, int key0, int e,
+                                                     int vkey0, int ve, const u32x4_t (&kr)[4],
+                                                     const u32x4_t (&vr)[4]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       *reinterpret_cast<u32x4_t*>(k_lds + (key0 + c) * k_stride<KT>() + e * 4) = kr[c];
-      *reinterpret_cast<u32x4_t*>(v_lds + (key0 + c) * v_stride<KT>() + e * 4) = vr[c];
+      *reinterpret_cast<u32x4_t*>(v_lds + (vkey0 + c) * v_stride<KT>() + ve * 4) = vr[c];
     }
   }
   template <int KT>
@@ -269,18 +271,23 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const elem* kt = static_cast<const elem*>(a.k_tree);
   const elem* vt = static_cast<const elem*>(a.v_tree);
 
-  // this thread's 4-key block of every tile: keys 4*vq .. 4*vq+3, column e
+  // this thread's 4-key blocks of every tile: keys 4*q .. 4*q+3 of 16-byte column e.
+  // K: column fastest (a row is read whole, LDS rows written whole).  V: key quad
+  // fastest, so that the transposed LDS writes of one instruction land in one row.
   const bool loader = tid < 256;
   const int vq = (tid & 255) / P::CH, e = (tid & 255) % P::CH;
+  const int vq_v = (tid & 255) % (KT / 4), e_v = (tid & 255) / (KT / 4);
   u32x4_t kr[4], vr[4];
+#define DDT_ROW(q_, c_)                                                                     \
+  (is_ctx_ ? (static_cast<long>(ctx0 + min(base_ + 4 * (q_) + (c_), lim_ - 1)) * a.Hkv + kvh) \
+           : ((static_cast<long>(b) * a.N + min(base_ + 4 * (q_) + (c_), lim_ - 1)) * a.Hkv + kvh))
 #define DDT_LOAD_KEY(c_)                                                                    \
   do {                                                                                      \
-    const int key_ = min(base_ + 4 * vq + (c_), lim_ - 1);                                  \
-    const long row_ = is_ctx_ ? (static_cast<long>(ctx0 + key_) * a.Hkv + kvh)              \
-                              : ((static_cast<long>(b) * a.N + key_) * a.Hkv + kvh);        \
-    const long off_ = row_ * DH + e * (16 / sizeof(elem));                                  \
-    kr[c_] = *reinterpret_cast<const u32x4_t*>((is_ctx_ ? kc : kt) + off_);                 \
-    vr[c_] = *reinterpret_cast<const u32x4_t*>((is_ctx_ ? vc : vt) + off_);                 \
+    kr[c_] = *reinterpret_cast<const u32x4_t*>((is_ctx_ ? kc : kt) + DDT_ROW(vq, c_) * DH + \
+                                               e * (16 / sizeof(elem)));                    \
+    vr[c_] = *reinterpret_cast<const u32x4_t*>((is_ctx_ ? vc : vt) +                        \
+                                               DDT_ROW(vq_v, c_) * DH +                     \
+                                               e_v * (16 / sizeof(elem)));                  \
   } while (0)
 #define DDT_LOAD_TILE(t_)                                                                   \
   do {                                                                                      \
@@ -319,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
     if (loader) {
-      P::template store_block<KT>(k_lds, v_lds, 4 * vq, e, kr, vr);
+      P::template store_block<KT>(k_lds, v_lds, 4 * vq, e, 4 * vq_v, e_v, kr, vr);
       if (t + 1 < ntiles) DDT_LOAD_TILE(t + 1);
     }
     __syncthreads();
@@ -368,6 +375,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   }
 #undef DDT_LOAD_TILE
 #undef DDT_LOAD_KEY
+#undef DDT_ROW
   if (!computes) return;
 
   float l_tot = l_run + shfl_xor_f32(l_run, 16);
@@ -393,10 +401,294 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ DMA pipeline (bf16, Dh 128)
+// The same computation as attn_kernel, with the context streamed by the
+// global->LDS DMA path of gfx950 (global_load_lds_dwordx4: each lane's 16 bytes
+// land at M0 + 16 * lane) into a ring of NS tile buffers, so that NS - 1 tiles
+// are in flight while one is computed and no registers are spent on staging.
+// Rows are stored whole (256 bytes) with their sixteen 16-byte chunks XOR-
+// swizzled by (row & 7), which keeps both the DMA writes and the MFMA operand
+// reads free of bank conflicts.  V stays row-major: the V^T operand of the
+// PV product comes from ds_read_b64_tr_b16, whose 16-lane transpose yields, for
+// lane (g, i), V[4g + k][d0 + i] (k = 0..3) when lane j of the 16 points at
+// row 4g + j/4, column d0 + 4 (j % 4) -- exactly the key order of the S^T
+// accumulator.  The DMA is issued from inline asm with explicit vmcnt waits,
+// because the compiler's own tracking would wait for every DMA before each
+// LDS read.
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_byte) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_byte);   // wave-uniform by construction
+  // M0 written by a scalar move needs one wait state before an LDS-DMA load
+  // reads it.  M0 is a reserved register the compiler does not allocate; no
+  // other code of these kernels relies on its contents.
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v), "v"(g)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int QB, int NW, int NS>
+__global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
+  using elem = uint16_t;
+  constexpr int DH = 128, KT = 64, KB = KT / 16, QF = DH / 32;
+  constexpr int TILE = 2 * KT * DH * 2;           // bytes: K then V
+  constexpr int DPW = 32 / NW;                    // 1 KB DMA instructions per wave per tile
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int s_b, s_split, s_nsplit, s_ctx0, s_len;
+  const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<size_t>(
+      (__attribute__((address_space(3))) unsigned char*)(smem)));
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int sid = blockIdx.x, kvh = blockIdx.y;
+  const int row0 = blockIdx.z * 128;
+  const int SK = a.split_keys;
+
+  if (wave == 0) {
+    int acc = 0, fb = -1, fs = 0, fn = 0, fo = 0, fl = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      int nb = 0, off = 0, L = 0;
+      if (bb < a.B) {
+        off = a.ctx_offsets[bb];
+        L = a.ctx_offsets[bb + 1] - off;
+        nb = L > 0 ? (L + SK - 1) / SK : 1;
+      }
+      int incl = nb;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+      }
+      const int excl = acc + incl - nb;
+      if (bb < a.B && sid >= excl && sid < excl + nb) {
+        fb = bb;
+        fs = sid - excl;
+        fn = nb;
+        fo = off;
+        fl = L;
+      }
+      acc += __shfl(incl, 63, 64);
+    }
+    const uint64_t hit = __ballot(fb >= 0);
+    if (lane == 0) s_b = -1;
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      const int bb = __shfl(fb, src, 64), ss = __shfl(fs, src, 64), nn2 = __shfl(fn, src, 64);
+      const int oo = __shfl(fo, src, 64), ll = __shfl(fl, src, 64);
+      if (lane == 0) {
+        s_b = bb;
+        s_split = ss;
+        s_nsplit = nn2;
+        s_ctx0 = oo;
+        s_len = ll;
+      }
+    }
+  }
+  __syncthreads();
+  const int b = s_b;
+  if (b < 0) return;
+  const int split = s_split, nsplit = s_nsplit;
+  const int ctx0 = s_ctx0, L = s_len;
+  const int k0 = split * SK, k1 = min(L, k0 + SK);
+  const bool last = split == nsplit - 1;
+  const int nctx_tiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
+  const int ntiles = nctx_tiles + (last ? (a.N + KT - 1) / KT : 0);
+  const elem* kc = static_cast<const elem*>(a.k_ctx);
+  const elem* vc = static_cast<const elem*>(a.v_ctx);
+  const elem* kt = static_cast<const elem*>(a.k_tree);
+  const elem* vt = static_cast<const elem*>(a.v_tree);
+
+  // DMA of tile t into ring slot t % NS: this wave's DPW groups of four rows
+  const int rstride = a.Hkv * DH;   // elements between consecutive keys
+  const elem* kc0 = kc + (static_cast<long>(ctx0) * a.Hkv + kvh) * DH;
+  const elem* vc0 = vc + (static_cast<long>(ctx0) * a.Hkv + kvh) * DH;
+  const elem* kt0 = kt + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
+  const elem* vt0 = vt + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
+#define DDT_DMA_TILE(T_)                                                                        \
+  do {                                                                                          \
+    const int t_ = (T_);                                                                        \
+    const bool ctx_ = t_ < nctx_tiles;                                                          \
+    const int base_ = ctx_ ? k0 + t_ * KT : (t_ - nctx_tiles) * KT;                             \
+    const int lim_ = (ctx_ ? k1 : a.N) - 1;                                                     \
+    const uint32_t slot_ = smem_base + static_cast<uint32_t>((t_ % NS) * TILE);                 \
+    _Pragma("unroll") for (int j_ = 0; j_ < DPW; ++j_) {                                        \
+      const int rg_ = wave * DPW + j_; /* 0..15: K rows, 16..31: V rows */                      \
+      const int vp_ = rg_ >> 4, rq_ = rg_ & 15;                                                 \
+      const int r_ = 4 * rq_ + (lane >> 4);                                                     \
+      const int key_ = min(base_ + r_, lim_);                                                   \
+      const elem* src_ = (vp_ ? (ctx_ ? vc0 : vt0) : (ctx_ ? kc0 : kt0)) +                      \
+                         static_cast<long>(key_) * rstride + (((lane & 15) ^ (r_ & 7)) * 8);    \
+      dma16(src_, slot_ + static_cast<uint32_t>(vp_ * (KT * DH * 2) + rq_ * 1024));             \
+    }                                                                                           \
+  } while (0)
+
+  // The first NS - 1 tiles go out before anything else is read, so that their
+  // latency overlaps that of the query and visibility loads below.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) DDT_DMA_TILE(t);
+
+  const int nn = a.num_nodes[b];
+  const bool computes = wave < QB && row0 + 16 * wave < a.M;
+  const int r = row0 + 16 * wave + l16;
+  const int rq = min(r, a.M - 1);
+  const int node = rq / a.G, head = kvh * a.G + rq % a.G;
+  bf16x8_t qf[QF];
+  uint64_t vis0 = 0, vis1 = 0;
+  if (computes) {
+    const elem* qrow = static_cast<const elem*>(a.q) +
+                       ((static_cast<long>(b) * a.N + node) * a.Hq + head) * DH;
+#pragma unroll
+    for (int s = 0; s < QF; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qrow + s * 32 + 8 * g);
+    if (node < nn) {
+      const uint64_t* vr_ = a.vis + (static_cast<long>(b) * a.N + node) * a.W;
+      vis0 = vr_[0];
+      vis1 = a.W > 1 ? vr_[1] : 0ull;
+    }
+  }
+  // Wait for all of it (the prologue tiles included): afterwards the only
+  // loads in flight are the DMAs counted below.  The builtin form lets the
+  // compiler's own wait tracking see this wait.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  f32x4_t o[DH / 16];
+#pragma unroll
+  for (int db = 0; db < DH / 16; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, l_run = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    // tiles issued after t and possibly still in flight: min(ntiles - 1, t + NS - 2) - t
+    const int after = min(ntiles - 1, t + NS - 2) - t;
+    if (after >= 2) wait_vmcnt<2 * DPW>();
+    else if (after == 1) wait_vmcnt<DPW>();
+    else wait_vmcnt<0>();
+    // a barrier that LDS reads of this tile cannot be moved above
+    asm volatile("s_barrier" ::: "memory");
+    if (t + NS - 1 < ntiles) DDT_DMA_TILE(t + NS - 1);
+    if (!computes) continue;
+    const unsigned char* kbuf = smem + (t % NS) * TILE;
+    const unsigned char* vbuf = kbuf + KT * DH * 2;
+    // key mask of this tile for this lane's query row: context keys below k1,
+    // tree keys by the visibility word (tree tiles are the 64-key words)
+    uint64_t mask;
+    if (t < nctx_tiles) {
+      const int n = k1 - (k0 + t * KT);
+      mask = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    } else {
+      mask = t == nctx_tiles ? vis0 : vis1;
+    }
+    const uint64_t mg = mask >> (4 * g);
+    f32x4_t sv[KB];
+    float tmax = kNegBig;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int row = kb * 16 + l16;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < QF; ++s) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+            kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & 7)) * 16));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (mg >> (kb * 16 + i)) & 1ull;
+        const float sc = ok ? acc[i] * a.scale_log2 : -__builtin_huge_valf();
+        acc[i] = sc;
+        tmax = max(tmax, sc);
+      }
+      sv[kb] = acc;
+    }
+    tmax = max(tmax, shfl_xor_f32(tmax, 16));
+    tmax = max(tmax, shfl_xor_f32(tmax, 32));
+    const float m_new = max(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - m_new);
+        sv[kb][i] = pv;
+        psum += pv;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) o[db] *= alpha;
+#pragma unroll
+    for (int j = 0; j < KT / 32; ++j) {
+      bf16x8_t pf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pf[i] = static_cast<__bf16>(sv[2 * j][i]);
+        pf[4 + i] = static_cast<__bf16>(sv[2 * j + 1][i]);
+      }
+#pragma unroll
+      for (int db = 0; db < DH / 16; ++db) {
+        i16x4_t h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * j + 16 * hh + 4 * g + (l16 >> 2);
+          const int chunk = 2 * db + ((l16 & 3) >> 1);
+          const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & 7)) * 16) + (l16 & 1) * 8;
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+        }
+        // whole-vector casts: element-wise bf16 inserts from the 16-bit lanes
+        // are lowered wrongly (the upper half of each read is dropped)
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, h[0]);
+        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, h[1]);
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+      }
+    }
+  }
+  if (!computes) return;
+
+  float l_tot = l_run + shfl_xor_f32(l_run, 16);
+  l_tot += shfl_xor_f32(l_tot, 32);
+  if (r >= a.M) return;
+  if (nsplit == 1) {
+    elem* orow = static_cast<elem*>(a.out) + ((static_cast<long>(b) * a.N + node) * a.Hq + head) * DH;
+    const bool valid = node < nn;
+    const float inv = valid && l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db) PolicyBF16<DH>::store_out(orow + db * 16 + 4 * g, o[db] * inv);
+    if (a.lse && g == 0)
+      a.lse[(static_cast<long>(b) * a.N + node) * a.Hq + head] =
+          valid ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
+  } else {
+    const long pr = (static_cast<long>(sid) * a.Hkv + kvh) * a.M + r;
+    float* dst = a.ws_o + pr * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 16; ++db)
+      *reinterpret_cast<float4*>(dst + db * 16 + 4 * g) =
+          make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+    if (g == 0) a.ws_ml[pr] = make_float2(m_run, l_tot);
+  }
+}
+
 // ------------------------------------------------------------------ combine
+// One workgroup per (request, KV head, query row): the four waves each take a
+// quarter of the splits (lanes over splits for the running maxima, then every
+// lane over Dh/64 output dims with unrolled loads); the four partial sums meet
+// in LDS.
 template <typename elem, int DH>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-  const int b = blockIdx.x, kvh = blockIdx.y;
+  constexpr int PER = DH / 64;                // output dims per lane
+  __shared__ float s_m[4], s_l[4];
+  __shared__ float s_acc[4][DH];
+  const int b = blockIdx.x / a.Hkv, kvh = blockIdx.x % a.Hkv;
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int SK = a.split_keys;
   auto nsplits = [&](int bb) {
     const int L = a.ctx_offsets[bb + 1] - a.ctx_offsets[bb];
@@ -405,47 +697,71 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int ns = nsplits(b);
   if (ns == 1) return;
   int start = 0;
-  for (int bb = 0; bb < b; ++bb) start += nsplits(bb);
-  const int nn = a.num_nodes[b];
-  constexpr int TPR = DH / 4;                 // threads per row, 4 dims each
-  constexpr int RPI = 256 / TPR;              // rows per iteration
-  const int sub = threadIdx.x / TPR, d4 = (threadIdx.x % TPR) * 4;
-  for (int r = sub; r < a.M; r += RPI) {
-    const int node = r / a.G, head = kvh * a.G + r % a.G;
-    const long orow = ((static_cast<long>(b) * a.N + node) * a.Hq + head);
-    elem* dst = static_cast<elem*>(a.out) + orow * DH + d4;
-    if (node >= nn) {
-      if constexpr (sizeof(elem) == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
-      else *reinterpret_cast<float4*>(dst) = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (a.lse && d4 == 0) a.lse[orow] = -__builtin_huge_valf();
-      continue;
+  for (int bb = lane; bb < b; bb += 64) start += nsplits(bb);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) start += __shfl_xor(start, o, 64);
+  const int node = r / a.G, head = kvh * a.G + r % a.G;
+  const long orow = (static_cast<long>(b) * a.N + node) * a.Hq + head;
+  elem* dst = static_cast<elem*>(a.out) + orow * DH;
+  if (node >= a.num_nodes[b]) {
+    if (wave == 0) {
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        if constexpr (sizeof(elem) == 2) dst[lane * PER + k] = 0; else dst[lane * PER + k] = 0.f;
+      }
+      if (a.lse && lane == 0) a.lse[orow] = -__builtin_huge_valf();
     }
-    float mstar = kNegBig;
-    for (int s = 0; s < ns; ++s)
-      mstar = max(mstar, a.ws_ml[(static_cast<long>(start + s) * a.Hkv + kvh) * a.M + r].x);
-    float lsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < ns; ++s) {
-      const long pr = (static_cast<long>(start + s) * a.Hkv + kvh) * a.M + r;
-      const float2 ml = a.ws_ml[pr];
-      const float w = __builtin_amdgcn_exp2f(ml.x - mstar);
-      lsum += w * ml.y;
-      const float4 v = *reinterpret_cast<const float4*>(a.ws_o + pr * DH + d4);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    if constexpr (sizeof(elem) == 2) {
-      const uint32_t lo = f32_to_bf16_rne(acc.x * inv) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.y * inv)) << 16);
-      const uint32_t hi = f32_to_bf16_rne(acc.z * inv) | (static_cast<uint32_t>(f32_to_bf16_rne(acc.w * inv)) << 16);
-      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-    } else {
-      *reinterpret_cast<float4*>(dst) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
-    if (a.lse && d4 == 0) a.lse[orow] = (mstar + __log2f(lsum)) * kLn2;
+    return;
   }
+  const long pr0 = static_cast<long>(start) * a.Hkv + kvh;
+  auto prow = [&](int sp) { return (pr0 + static_cast<long>(sp) * a.Hkv) * a.M + r; };
+  // this wave's splits: wave, wave + 4, ...
+  float mw = kNegBig;
+  for (int sp = wave + 4 * lane; sp < ns; sp += 256) mw = max(mw, a.ws_ml[prow(sp)].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mw = max(mw, shfl_xor_f32(mw, o));
+  float lw = 0.f;
+  for (int sp = wave + 4 * lane; sp < ns; sp += 256) {
+    const float2 ml = a.ws_ml[prow(sp)];
+    lw += __builtin_amdgcn_exp2f(ml.x - mw) * ml.y;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor_f32(lw, o);
+  float acc[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) acc[k] = 0.f;
+#pragma unroll 4
+  for (int sp = wave; sp < ns; sp += 4) {
+    const long pr = prow(sp);
+    const float w = __builtin_amdgcn_exp2f(a.ws_ml[pr].x - mw);
+    const float* src = a.ws_o + pr * DH + lane * PER;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+  }
+  if (lane == 0) {
+    s_m[wave] = mw;
+    s_l[wave] = lw;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) s_acc[wave][lane * PER + k] = acc[k];
+  __syncthreads();
+  if (wave != 0) return;
+  const float mstar = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+  float f[4], lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = __builtin_amdgcn_exp2f(s_m[w] - mstar);
+    lsum += f[w] * s_l[w];
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int d = lane * PER + k;
+    const float o = (f[0] * s_acc[0][d] + f[1] * s_acc[1][d] + f[2] * s_acc[2][d] +
+                     f[3] * s_acc[3][d]) * inv;
+    if constexpr (sizeof(elem) == 2) dst[d] = f32_to_bf16_rne(o); else dst[d] = o;
+  }
+  if (a.lse && lane == 0) a.lse[orow] = (mstar + __log2f(lsum)) * kLn2;
 }
 
 // ------------------------------------------------------------------ host side
@@ -454,13 +770,16 @@ int keys_per_tile(ddtree_dtype dt, int Dh, int /*qb*/) {
   return 1024 / ch;
 }
 
-// Keys per split: about `target` workgroups over the whole context, whole tiles.
+// Keys per split: about `target` workgroups over the whole context (two per CU),
+// at least 256 keys (a few tiles, so each workgroup keeps loads in flight) and
+// at most 2048 (bounds the imbalance of ragged batches); whole tiles.
 int plan_split_keys(const int32_t* offs_host, int B, int Hkv, int kt) {
   long total = static_cast<long>(offs_host[B]) - offs_host[0];
-  int target = 768;
+  int target = 512;
   if (const char* env = std::getenv("DDTREE_ATTN_TARGET_WGS")) target = std::max(1, atoi(env));
   long sk = (total * Hkv + target - 1) / target;
-  sk = std::max<long>(sk, 2 * kt);
+  sk = std::min<long>(std::max<long>(sk, 256), 2048);
+  sk = std::max<long>(sk, kt);
   sk = (sk + kt - 1) / kt * kt;
   if (const char* env = std::getenv("DDTREE_ATTN_SPLIT_KEYS")) {
     const long v = atol(env);
@@ -501,6 +820,36 @@ void launch_qb(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
     case 6: launch_main<P, 6>(a, total_splits, st); break;
     case 7: launch_main<P, 7>(a, total_splits, st); break;
     default: launch_main<P, 8>(a, total_splits, st); break;
+  }
+}
+
+template <int QB, int NS>
+void launch_dma_ns(const AttnArgs& a, int total_splits, hipStream_t st) {
+  constexpr int NW = QB <= 4 ? 4 : 8;
+  const size_t lds = static_cast<size_t>(NS) * 2 * 64 * 128 * 2;
+  const dim3 grid(total_splits, a.Hkv, (a.M + 127) / 128);
+  hipLaunchKernelGGL((attn_dma_kernel<QB, NW, NS>), grid, dim3(NW * 64), lds, st, a);
+}
+
+template <int QB>
+void launch_dma_qb(const AttnArgs& a, int total_splits, hipStream_t st) {
+  const char* e = std::getenv("DDTREE_ATTN_STAGES");
+  const int ns = e ? std::atoi(e) : 2;
+  if (ns == 2) launch_dma_ns<QB, 2>(a, total_splits, st);
+  else if (ns == 3) launch_dma_ns<QB, 3>(a, total_splits, st);
+  else launch_dma_ns<QB, 4>(a, total_splits, st);
+}
+
+void launch_dma(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
+  switch (qb) {
+    case 1: launch_dma_qb<1>(a, total_splits, st); break;
+    case 2: launch_dma_qb<2>(a, total_splits, st); break;
+    case 3: launch_dma_qb<3>(a, total_splits, st); break;
+    case 4: launch_dma_qb<4>(a, total_splits, st); break;
+    case 5: launch_dma_qb<5>(a, total_splits, st); break;
+    case 6: launch_dma_qb<6>(a, total_splits, st); break;
+    case 7: launch_dma_qb<7>(a, total_splits, st); break;
+    default: launch_dma_qb<8>(a, total_splits, st); break;
   }
 }
 
@@ -562,6 +911,8 @@ extern "C" ddtree_status ddtree_tree_attention(
       (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)))
     return fail(DDTREE_EINVAL, "ddtree_tree_attention: tensors must be 16-byte aligned");
   const int qb = (std::min(M, 128) + 15) / 16;   // 16-row query blocks per slice
+  const char* dma_env = std::getenv("DDTREE_ATTN_DMA");
+  const bool use_dma = !(dma_env && dma_env[0] == '0');
   const int kt = keys_per_tile(dtype, Dh, qb);
   const int sk = plan_split_keys(ctx_offsets_host, B, Hkv, kt);
   bool multi;
@@ -598,14 +949,15 @@ extern "C" ddtree_status ddtree_tree_attention(
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + need);
   }
   if (dtype == DDTREE_BF16) {
-    if (Dh == 128) launch_qb<PolicyBF16<128>>(qb, a, total, stream);
+    if (Dh == 128 && use_dma) launch_dma(qb, a, total, stream);
+    else if (Dh == 128) launch_qb<PolicyBF16<128>>(qb, a, total, stream);
     else launch_qb<PolicyBF16<64>>(qb, a, total, stream);
   } else {
     if (Dh == 128) launch_qb<PolicyF32<128>>(qb, a, total, stream);
     else launch_qb<PolicyF32<64>>(qb, a, total, stream);
   }
   if (multi) {
-    const dim3 g(B, Hkv);
+    const dim3 g(B * Hkv, M);
     if (dtype == DDTREE_BF16) {
       if (Dh == 128) hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), g, dim3(256), 0, stream, a);
       else hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), g, dim3(256), 0, stream, a);

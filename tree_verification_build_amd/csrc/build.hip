@@ -7,123 +7,246 @@
 // The tree's visibility rows are ancestor-or-self sets; positions are
 // prefix_len + depth ("The Tree That Couldn't Branch", "Hypothesis 3").
 //
-// Design: the frontier never holds more than budget + 1 <= 128 entries, so it
-// lives in registers, two 64-bit keys per lane.  A key orders entries exactly
-// as required (score desc, parent asc, rank asc) and carries the entry:
+// Design: the frontier is kept sorted (best first) across the 64 lanes of the
+// wavefront, entry j in lane j, as 64-bit keys that order entries exactly as
+// required (score desc, parent asc, rank asc) and carry the entry:
 //   [63:32] order-preserving bits of the fp32 score
 //   [31:24] 255 - parent   [23:16] 255 - rank   [15:8] depth   [7:0] pusher
 // ("pusher" is the node whose taking offered this entry: the parent for a
-// rank-0 child, the rank-1 sibling otherwise), so the best entry is one
-// wave-wide 64-bit max.  A taken slot is refilled by the new child (or the
-// new sibling); only when both exist does the sibling take a fresh slot.
-// Node records accumulate in LDS and are written out coalesced at the end.
+// rank-0 child, the rank-1 sibling otherwise).  64 slots are enough for any
+// N <= 128: with r pops left, an entry at position >= r can never be taken,
+// and after k pops the frontier holds at most k + 1 entries, so at most
+// min(k + 1, N - 1 - k) <= N / 2 entries matter; entries pushed past slot 63
+// are dropped.  One step of the loop takes lane 0 (the best entry), forms the
+// best child and the next sibling (key 0 for "none"), and rebuilds the list in
+// one lane-parallel select from three copies of it: shifted down one lane, as
+// is, and shifted up one lane (DPP wave_shl:1 / wave_shr:1), at the two
+// insertion points found by ballots; the lane masks are built with scalar
+// shifts.  Empty slots hold 0, below every real key, so the loop has no
+// data-dependent branch.  The taken key is itself node i's record (kept in lane i % 64).  A single wave pays ~15 cycles per dependent vector op,
+// so the loop does nothing else: tokens, positions, child / sibling links and
+// visibility rows are rebuilt afterwards, all lanes in parallel (visibility by
+// pointer jumping over parent links).  The draft top-k table (D*K <= 256
+// entries) is spread over the lanes and read with v_readlane.
 #include "common.hpp"
 
 namespace ddt {
 namespace {
 
-constexpr int kMaxN = DDTREE_MAX_NODES;
+__device__ __forceinline__ uint64_t make_key_bits(uint32_t ord_score, int parent, int rank,
+                                                  int depth, int pusher) {
+  const uint32_t lo = (static_cast<uint32_t>(255 - parent) << 24) |
+                      (static_cast<uint32_t>(255 - rank) << 16) |
+                      (static_cast<uint32_t>(depth) << 8) | static_cast<uint32_t>(pusher);
+  return (static_cast<uint64_t>(ord_score) << 32) | lo;
+}
 
 __device__ __forceinline__ uint64_t make_key(float score, int parent, int rank, int depth,
                                              int pusher) {
-  uint32_t lo = (static_cast<uint32_t>(255 - parent) << 24) |
-                (static_cast<uint32_t>(255 - rank) << 16) |
-                (static_cast<uint32_t>(depth) << 8) | static_cast<uint32_t>(pusher);
-  return (static_cast<uint64_t>(ord_f32(score)) << 32) | lo;
+  return make_key_bits(ord_f32(score), parent, rank, depth, pusher);
 }
 
+// ord_f32 of raw float bits held in a (uniform) integer: stays in scalar registers
+__device__ __forceinline__ uint32_t ord_f32_s(uint32_t u) {
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// value of a per-lane register table at flat index idx (uniform): one readlane
+// when the table fits one register (D*K <= 64), else a scalar select of four
+template <int REGS>
+__device__ __forceinline__ uint32_t table_at(const uint32_t (&r)[4], int idx) {
+  if (REGS == 1) return __builtin_amdgcn_readlane(r[0], idx);
+  const int w = idx >> 6, l = idx & 63;
+  const uint32_t a0 = __builtin_amdgcn_readlane(r[0], l), a1 = __builtin_amdgcn_readlane(r[1], l);
+  const uint32_t a2 = __builtin_amdgcn_readlane(r[2], l), a3 = __builtin_amdgcn_readlane(r[3], l);
+  return w == 0 ? a0 : w == 1 ? a1 : w == 2 ? a2 : a3;
+}
+
+// whole-wave lane shifts (DPP): down(v)[i] = v[i+1], up(v)[i] = v[i-1]; 0 shifted in
+__device__ __forceinline__ uint32_t lanes_down(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x130, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t lanes_up(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x138, 0xF, 0xF, false));
+}
+
+// v[l] = val for one uniform lane l
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t val, int l) {
+  return static_cast<int>(threadIdx.x) == l ? val : v;
+}
+
+// lane-varying gather from the per-lane table (ds_bpermute)
+template <int REGS>
+__device__ __forceinline__ uint32_t table_gather(const uint32_t (&r)[4], int idx) {
+  const int l = idx & 63, w = idx >> 6;
+  uint32_t v = __shfl(r[0], l, 64);
+  if (REGS > 1) {
+    const uint32_t v1 = __shfl(r[1], l, 64), v2 = __shfl(r[2], l, 64), v3 = __shfl(r[3], l, 64);
+    v = w == 1 ? v1 : w == 2 ? v2 : w == 3 ? v3 : v;
+  }
+  return v;
+}
+
+template <int REGS, bool TWO>
 __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ draft_lp,
                                                    const int32_t* __restrict__ draft_tok,
                                                    const int32_t* __restrict__ root_tok,
                                                    const int32_t* __restrict__ prefix_len,
                                                    int D, int K, int budget, ddtree_tree t) {
-  extern __shared__ unsigned char smem[];
-  float* s_lp = reinterpret_cast<float*>(smem);                    // [D*K]
-  int32_t* s_tok = reinterpret_cast<int32_t*>(s_lp + D * K);      // [D*K]
-  __shared__ float s_score[kMaxN];
-  __shared__ int32_t s_token[kMaxN], s_parent[kMaxN], s_depth[kMaxN], s_rank[kMaxN];
-  __shared__ int32_t s_fc[kMaxN], s_ns[kMaxN];
-  __shared__ uint64_t s_vis[kMaxN][2];
-
+  __shared__ int32_t s_fc[DDTREE_MAX_NODES], s_ns[DDTREE_MAX_NODES];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int N = budget + 1;
   const int DK = D * K;
-  for (int i = lane; i < DK; i += kWave) {
-    s_lp[i] = draft_lp[static_cast<long>(b) * DK + i];
-    s_tok[i] = draft_tok[static_cast<long>(b) * DK + i];
+  // draft table: entry i = d * K + r in register i / 64 of lane i % 64
+  uint32_t lp_r[4], tok_r[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int i = w * 64 + lane;
+    lp_r[w] = (w < REGS && i < DK) ? __float_as_uint(draft_lp[static_cast<long>(b) * DK + i]) : 0u;
+    tok_r[w] = (w < REGS && i < DK) ? static_cast<uint32_t>(draft_tok[static_cast<long>(b) * DK + i]) : 0u;
   }
-  for (int i = lane; i < kMaxN; i += kWave) {
-    s_fc[i] = -1;
-    s_ns[i] = -1;
+  s_fc[lane] = -1;
+  s_ns[lane] = -1;
+  if (TWO) {
+    s_fc[lane + 64] = -1;
+    s_ns[lane + 64] = -1;
   }
-  if (lane == 0) {
-    s_score[0] = 0.0f;
-    s_token[0] = root_tok[b];
-    s_parent[0] = -1;
-    s_depth[0] = 0;
-    s_rank[0] = -1;
-    s_vis[0][0] = 1ull;
-    s_vis[0][1] = 0ull;
-  }
-  __syncthreads();
 
-  uint64_t key0 = 0, key1 = 0;  // slots lane and lane + 64
-  int nslots = 1;
-  if (lane == 0) key0 = make_key(0.0f + s_lp[0], 0, 0, 1, 0);
+  // records: the taken key of node i sits in lane i % 64 of (rh0, rl0) or (rh1, rl1);
+  // the root's record carries score +0.0 (its other fields are never read)
+  uint32_t rh0 = lane == 0 ? ord_f32(0.0f) : 0u, rl0 = 0u, rh1 = 0u, rl1 = 0u;
+  // frontier: entry `lane` as (fh, fl); 0 = empty
+  const uint64_t first = make_key(0.0f + __uint_as_float(table_at<REGS>(lp_r, 0)), 0, 0, 1, 0);
+  uint32_t fh = lane == 0 ? static_cast<uint32_t>(first >> 32) : 0u;
+  uint32_t fl = lane == 0 ? static_cast<uint32_t>(first) : 0u;
+
   int count = 1;
-  while (count < N) {
-    uint64_t best = wave_max_u64(key0 > key1 ? key0 : key1);
-    if (best == 0) break;  // frontier empty
-    const uint32_t lo = static_cast<uint32_t>(best);
-    const float score = unord_f32(static_cast<uint32_t>(best >> 32));
+  for (; count < N; ++count) {
+    // readlane yields a signed int: cast before widening, or the low word sign-extends
+    const uint32_t bh = static_cast<uint32_t>(__builtin_amdgcn_readlane(fh, 0));
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(fl, 0));
+    if (bh == 0) break;  // frontier empty
     const int parent = 255 - static_cast<int>(lo >> 24);
     const int rank = 255 - static_cast<int>((lo >> 16) & 0xFF);
     const int depth = static_cast<int>((lo >> 8) & 0xFF);
-    const int pusher = static_cast<int>(lo & 0xFF);
-    const int i = count++;
+    const int i = count;
+    // the three shifted copies do not depend on this step's offers
+    const uint32_t dh = lanes_down(fh), dl = lanes_down(fl);
+    const uint32_t uh = lanes_up(fh), ul = lanes_up(fl);
+    // record node i
+    if (!TWO || i < 64) {
+      rh0 = write_lane(rh0, bh, i & 63);
+      rl0 = write_lane(rl0, lo, i & 63);
+    } else {
+      rh1 = write_lane(rh1, bh, i & 63);
+      rl1 = write_lane(rl1, lo, i & 63);
+    }
 
-    uint64_t child = 0, sib = 0;
-    if (depth < D) child = make_key(score + s_lp[depth * K], i, 0, depth + 1, i);
-    if (rank + 1 < K)
-      sib = make_key(s_score[parent] + s_lp[(depth - 1) * K + rank + 1], parent, rank + 1, depth, i);
-    const uint64_t refill = child ? child : sib;
-    if (key0 == best) key0 = refill;
-    if (key1 == best) key1 = refill;
-    if (child && sib) {
-      if (lane == (nslots & 63)) {
-        if (nslots < 64) key0 = sib; else key1 = sib;
-      }
-      ++nslots;
-    }
-    if (lane == 0) {
-      s_score[i] = score;
-      s_token[i] = s_tok[(depth - 1) * K + rank];
-      s_parent[i] = parent;
-      s_depth[i] = depth;
-      s_rank[i] = rank;
-      uint64_t v0 = s_vis[parent][0], v1 = s_vis[parent][1];
-      if (i < 64) v0 |= 1ull << i; else v1 |= 1ull << (i - 64);
-      s_vis[i][0] = v0;
-      s_vis[i][1] = v1;
-      if (rank == 0) s_fc[parent] = i; else s_ns[pusher] = i;
-    }
+    // offers: best child and next sibling (key 0 when there is none)
+    const float score = unord_f32(bh);
+    const float lpc = __uint_as_float(table_at<REGS>(lp_r, min(depth, D - 1) * K));
+    const uint32_t cs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(__float_as_uint(score + lpc)));
+    const uint64_t kc = depth < D ? make_key_bits(ord_f32_s(cs), i, 0, depth + 1, i) : 0ull;
+    const uint32_t pr = static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(TWO && parent >= 64 ? rh1 : rh0, parent & 63));
+    const float lps = __uint_as_float(table_at<REGS>(lp_r, (depth - 1) * K + min(rank + 1, K - 1)));
+    const uint32_t ss = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(__float_as_uint(unord_f32(pr) + lps)));
+    const uint64_t ks = rank + 1 < K ? make_key_bits(ord_f32_s(ss), parent, rank + 1, depth, i) : 0ull;
+    const uint64_t k1 = kc > ks ? kc : ks, k2 = kc > ks ? ks : kc;
+    // both offers rank below the entry just taken, so they land after slot 0
+    const uint64_t mine = (static_cast<uint64_t>(fh) << 32) | fl;
+    const int q1 = __builtin_popcountll(__ballot(mine > k1)) - 1;
+    const int q2 = __builtin_popcountll(__ballot(mine > k2));
+    const uint64_t lt1 = (1ull << q1) - 1ull, lt2 = q2 >= 64 ? ~0ull : (1ull << q2) - 1ull;
+    const bool below1 = (lt1 >> lane) & 1ull, at1 = lane == q1;
+    const bool below2 = (lt2 >> lane) & 1ull, at2 = lane == q2;
+    const uint32_t k1h = static_cast<uint32_t>(k1 >> 32), k1l = static_cast<uint32_t>(k1);
+    const uint32_t k2h = static_cast<uint32_t>(k2 >> 32), k2l = static_cast<uint32_t>(k2);
+    fh = below1 ? dh : at1 ? k1h : below2 ? fh : at2 ? k2h : uh;
+    fl = below1 ? dl : at1 ? k1l : below2 ? fl : at2 ? k2l : ul;
   }
-  __syncthreads();
 
+  // rebuild the node arrays from the records, every lane in parallel
   const long base = static_cast<long>(b) * N;
   const int W = t.W;
-  for (int i = lane; i < N; i += kWave) {
-    const bool ok = i < count;
-    t.token[base + i] = ok ? s_token[i] : -1;
-    t.parent[base + i] = ok ? s_parent[i] : -1;
-    t.depth[base + i] = ok ? s_depth[i] : -1;
-    t.rank[base + i] = ok ? s_rank[i] : -1;
-    t.position[base + i] = ok ? prefix_len[b] + s_depth[i] : -1;
-    t.first_child[base + i] = ok ? s_fc[i] : -1;
-    t.next_sibling[base + i] = ok ? s_ns[i] : -1;
-    t.score[base + i] = ok ? s_score[i] : -__builtin_huge_valf();
-    for (int w = 0; w < W; ++w) t.vis[(base + i) * W + w] = ok ? s_vis[i][w] : 0ull;
+  int par[2], dep[2], rnk[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int i = s * 64 + lane;
+    const uint32_t lo = s == 0 ? rl0 : rl1;
+    const bool ok = i < count && (s == 0 || TWO);
+    par[s] = ok && i > 0 ? 255 - static_cast<int>(lo >> 24) : -1;
+    rnk[s] = ok && i > 0 ? 255 - static_cast<int>((lo >> 16) & 0xFF) : -1;
+    dep[s] = ok ? (i > 0 ? static_cast<int>((lo >> 8) & 0xFF) : 0) : -1;
+    if (ok && i > 0) {
+      const int pusher = static_cast<int>(lo & 0xFF);
+      if (rnk[s] == 0) s_fc[par[s]] = i; else s_ns[pusher] = i;
+    }
+  }
+  // visibility rows by pointer jumping: after round k each row holds the node's
+  // 2^k nearest ancestors (and itself); depth <= 64 needs at most 7 rounds
+  uint32_t va[2][4], anc[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int i = s * 64 + lane;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) va[s][w] = 0u;
+    if (dep[s] >= 0) {
+      va[s][i >> 5] |= 1u << (i & 31);
+      if (par[s] >= 0) va[s][par[s] >> 5] |= 1u << (par[s] & 31);
+    }
+    anc[s] = par[s] >= 0 ? static_cast<uint32_t>(par[s]) : 0xFFFFFFFFu;
+  }
+  for (int jump = 1; jump < D; jump <<= 1) {
+    uint32_t nv[2][4], na[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t a = anc[s];
+      const int src = static_cast<int>(a & 63);
+      const bool hi = TWO && a != 0xFFFFFFFFu && a >= 64;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t g0 = __shfl(va[0][w], src, 64);
+        const uint32_t g1 = TWO ? __shfl(va[1][w], src, 64) : 0u;
+        nv[s][w] = va[s][w] | (a == 0xFFFFFFFFu ? 0u : (hi ? g1 : g0));
+      }
+      const uint32_t a0 = __shfl(anc[0], src, 64);
+      const uint32_t a1 = TWO ? __shfl(anc[1], src, 64) : 0xFFFFFFFFu;
+      na[s] = a == 0xFFFFFFFFu ? a : (hi ? a1 : a0);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      anc[s] = na[s];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) va[s][w] = nv[s][w];
+    }
+  }
+  // tokens: gathered with every lane active
+  int tg[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+    tg[s] = static_cast<int>(table_gather<REGS>(tok_r, max(0, (dep[s] - 1) * K + rnk[s])));
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int i = s * 64 + lane;
+    if (i < N) {
+      const bool ok = dep[s] >= 0;
+      const uint32_t hi = s == 0 ? rh0 : rh1;
+      t.token[base + i] = !ok ? -1 : i == 0 ? root_tok[b] : tg[s];
+      t.parent[base + i] = par[s];
+      t.depth[base + i] = dep[s];
+      t.rank[base + i] = rnk[s];
+      t.position[base + i] = ok ? prefix_len[b] + dep[s] : -1;
+      t.first_child[base + i] = ok ? s_fc[i] : -1;
+      t.next_sibling[base + i] = ok ? s_ns[i] : -1;
+      t.score[base + i] = ok ? unord_f32(hi) : -__builtin_huge_valf();
+      t.vis[(base + i) * W] = (static_cast<uint64_t>(va[s][1]) << 32) | va[s][0];
+      if (W > 1) t.vis[(base + i) * W + 1] = (static_cast<uint64_t>(va[s][3]) << 32) | va[s][2];
+    }
   }
   if (lane == 0) t.num_nodes[b] = count;
 }
@@ -158,8 +281,21 @@ extern "C" ddtree_status ddtree_build(const float* draft_lp, const int32_t* draf
                 DDTREE_MAX_NODES - 1);
   if (tree->N != budget + 1 || tree->B != B || tree->D != D || tree->K != K)
     return fail(DDTREE_EINVAL, "ddtree_build: tree sizes do not match B/D/K/budget");
-  const size_t smem = static_cast<size_t>(D) * K * (sizeof(float) + sizeof(int32_t));
-  hipLaunchKernelGGL(build_kernel, dim3(B), dim3(kWave), smem, stream, draft_lp, draft_tok,
-                     root_tok, prefix_len, D, K, budget, *tree);
+  if (D * K > 256)
+    return fail(DDTREE_EUNSUPPORTED, "ddtree_build: depth * top-k = %d exceeds 256", D * K);
+  const bool small_table = D * K <= 64, one_list = budget + 1 <= 64;
+  const dim3 g(B), blk(kWave);
+  if (small_table && one_list)
+    hipLaunchKernelGGL((build_kernel<1, false>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+                       prefix_len, D, K, budget, *tree);
+  else if (small_table)
+    hipLaunchKernelGGL((build_kernel<1, true>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+                       prefix_len, D, K, budget, *tree);
+  else if (one_list)
+    hipLaunchKernelGGL((build_kernel<4, false>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+                       prefix_len, D, K, budget, *tree);
+  else
+    hipLaunchKernelGGL((build_kernel<4, true>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+                       prefix_len, D, K, budget, *tree);
   return check_launch("ddtree_build");
 }

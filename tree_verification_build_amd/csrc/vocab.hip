@@ -7,9 +7,12 @@
 // its slice with 16-byte coalesced loads and reduces a packed 64-bit key
 // (order-preserving value bits << 32 | ~token id), whose maximum is the
 // largest logit at the lowest id; it also keeps a running (max, sum exp) for
-// the optional log-sum-exp.  When a row is split (S > 1) a small finalize
-// kernel merges the S partial results.  Integer keys make the merge order
-// irrelevant, so the argmax is the same for any S.
+// the optional log-sum-exp.  When a row is split (S > 1) each slice merges its
+// key into the row's slot with a 64-bit atomic max and takes a ticket; the
+// slice that draws the last ticket writes the row's results and clears the
+// slot and the ticket counter, so the workspace is zero again after every
+// call.  Integer keys make the merge order irrelevant: the argmax is the same
+// for any S.
 //
 // Sampling mode needs the row maximum before any weight can be formed, so one
 // 1024-thread workgroup owns a row and keeps it in registers: one HBM read,
@@ -104,11 +107,14 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 template <typename T, bool kLse>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes, int S,
-    int chunk, uint64_t* __restrict__ ws_key, float2* __restrict__ ws_ms,
-    int32_t* __restrict__ argmax, float* __restrict__ maxv, float* __restrict__ lse) {
+    int chunk, uint64_t* __restrict__ ws_key, uint32_t* __restrict__ ws_cnt,
+    float2* __restrict__ ws_ms, int32_t* __restrict__ argmax, float* __restrict__ maxv,
+    float* __restrict__ lse) {
   constexpr int E = Vec<T>::E;
-  __shared__ uint64_t s_key[kSplitThreads / kWave];
-  __shared__ float2 s_ms[kSplitThreads / kWave];
+  constexpr int kWaves = kSplitThreads / kWave;
+  __shared__ uint64_t s_key[kWaves];
+  __shared__ float2 s_ms[kWaves];
+  __shared__ int s_last;
   const int row = blockIdx.y;
   const int s = blockIdx.x;
   const int b = row / N, n = row % N;
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kSplitThreads / kWave; ++w) {
+    for (int w = 1; w < kWaves; ++w) {
       key = s_key[w] > key ? s_key[w] : key;
       if (kLse) lse_merge(m, sum, s_ms[w].x, s_ms[w].y);
     }
@@ -162,42 +168,56 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
       argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
       maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
       if (kLse) lse[row] = valid ? m + __logf(sum) : -__builtin_huge_valf();
+      s_last = 0;
     } else {
-      ws_key[static_cast<long>(row) * S + s] = valid ? key : 0ull;
-      if (kLse) ws_ms[static_cast<long>(row) * S + s] = make_float2(m, sum);
+      // Publish this slice with device-scope atomics (coherent across the XCDs'
+      // L2s without flushing them), wait for their results, then take a ticket:
+      // the slice holding the last ticket finishes the row.
+      unsigned long long done = 0;
+      if (valid)
+        done += atomicMax(reinterpret_cast<unsigned long long*>(ws_key + row),
+                          static_cast<unsigned long long>(key));
+      if (kLse) {
+        const unsigned long long ms =
+            (static_cast<unsigned long long>(__float_as_uint(sum)) << 32) | __float_as_uint(m);
+        done += atomicExch(reinterpret_cast<unsigned long long*>(ws_ms) + static_cast<long>(row) * S + s, ms);
+      }
+      uint32_t one = 1u;
+      __asm__ volatile("" : "+v"(one) : "v"(done));   // the ticket waits for both returns
+      const uint32_t ticket = atomicAdd(ws_cnt + row, one);
+      s_last = ticket == static_cast<uint32_t>(S - 1);
     }
   }
-}
-
-template <bool kLse>
-__global__ __launch_bounds__(256) void finalize_kernel(int rows, int N, const int32_t* __restrict__ num_nodes,
-                                                       int S, const uint64_t* __restrict__ ws_key,
-                                                       const float2* __restrict__ ws_ms,
-                                                       int32_t* __restrict__ argmax,
-                                                       float* __restrict__ maxv,
-                                                       float* __restrict__ lse) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
-  const int b = row / N, n = row % N;
-  if (n >= num_nodes[b]) {
-    argmax[row] = -1;
-    maxv[row] = -__builtin_huge_valf();
-    if (kLse) lse[row] = -__builtin_huge_valf();
-    return;
-  }
-  uint64_t key = 0;
-  float m = -__builtin_huge_valf(), sum = 0.0f;
-  for (int s = 0; s < S; ++s) {
-    const uint64_t k = ws_key[static_cast<long>(row) * S + s];
-    key = k > key ? k : key;
-    if (kLse) {
-      const float2 ms = ws_ms[static_cast<long>(row) * S + s];
-      lse_merge(m, sum, ms.x, ms.y);
+  __syncthreads();
+  if (!s_last) return;
+  if (kLse) {
+    // merge the S (max, sum) pairs of the row with the whole workgroup (atomic reads)
+    float mm = -__builtin_huge_valf(), ss = 0.0f;
+    for (int k = tid; k < S; k += kSplitThreads) {
+      const unsigned long long ms = atomicAdd(
+          reinterpret_cast<unsigned long long*>(ws_ms) + static_cast<long>(row) * S + k, 0ull);
+      lse_merge(mm, ss, __uint_as_float(static_cast<uint32_t>(ms)),
+                __uint_as_float(static_cast<uint32_t>(ms >> 32)));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float m2 = shfl_xor_f32(mm, o), s2 = shfl_xor_f32(ss, o);
+      lse_merge(mm, ss, m2, s2);
+    }
+    if (lane == 0) s_ms[wave] = make_float2(mm, ss);
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < kWaves; ++w) lse_merge(mm, ss, s_ms[w].x, s_ms[w].y);
+      lse[row] = valid ? mm + __logf(ss) : -__builtin_huge_valf();
     }
   }
-  argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-  maxv[row] = unord_f32(static_cast<uint32_t>(key >> 32));
-  if (kLse) lse[row] = m + __logf(sum);
+  if (tid == 0) {
+    // read and clear the row's key and ticket counter (the workspace is left zeroed)
+    const uint64_t k = atomicExch(reinterpret_cast<unsigned long long*>(ws_key + row), 0ull);
+    atomicExch(ws_cnt + row, 0u);
+    argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k)) : -1;
+    maxv[row] = valid ? unord_f32(static_cast<uint32_t>(k >> 32)) : -__builtin_huge_valf();
+  }
 }
 
 // Sampling mode: one workgroup per row, row held in registers (MAXP 16-byte
@@ -421,27 +441,31 @@ void launch_sampling(int rows, hipStream_t st, const void* logits, int N, int V,
                        static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
 }
 
+// Greedy workspace: [rows] uint64 keys, [rows] uint32 tickets (zero between calls),
+// then [rows * S] float2 log-sum-exp partials.
+size_t greedy_ws_bytes(int rows, int S) {
+  if (S <= 1) return 0;
+  const size_t keys = static_cast<size_t>(rows) * sizeof(uint64_t);
+  const size_t cnt = (static_cast<size_t>(rows) * sizeof(uint32_t) + 15) / 16 * 16;
+  return keys + cnt + static_cast<size_t>(rows) * S * sizeof(float2);
+}
+
 template <typename T>
 void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
                    int S, int chunk, void* ws, int32_t* am, float* mx, float* lse) {
   uint64_t* ws_key = static_cast<uint64_t*>(ws);
-  float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<long>(rows) * S);
+  uint32_t* ws_cnt = reinterpret_cast<uint32_t*>(ws_key + rows);
+  float2* ws_ms = reinterpret_cast<float2*>(
+      reinterpret_cast<char*>(ws_cnt) + (static_cast<size_t>(rows) * sizeof(uint32_t) + 15) / 16 * 16);
   const dim3 grid(S, rows);
   if (lse)
     hipLaunchKernelGGL((split_kernel<T, true>), grid, dim3(kSplitThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx, lse);
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_cnt, ws_ms,
+                       am, mx, lse);
   else
     hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx, lse);
-  if (S > 1) {
-    const dim3 g2((rows + 255) / 256);
-    if (lse)
-      hipLaunchKernelGGL(finalize_kernel<true>, g2, dim3(256), 0, st, rows, N, nn, S, ws_key,
-                         ws_ms, am, mx, lse);
-    else
-      hipLaunchKernelGGL(finalize_kernel<false>, g2, dim3(256), 0, st, rows, N, nn, S, ws_key,
-                         ws_ms, am, mx, lse);
-  }
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_cnt, ws_ms,
+                       am, mx, lse);
 }
 
 }  // namespace
@@ -453,8 +477,7 @@ extern "C" size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32
   ddt::split_plan(B * N, V, 2, &S2, &chunk);
   ddt::split_plan(B * N, V, 4, &S4, &chunk);
   const int S = S2 > S4 ? S2 : S4;               // covers both element sizes
-  if (S <= 1) return 0;
-  return static_cast<size_t>(B) * N * S * (sizeof(uint64_t) + 2 * sizeof(float));
+  return ddt::greedy_ws_bytes(B * N, S);
 }
 
 extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_t B,
@@ -484,8 +507,8 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
   int S, chunk;
   split_plan(rows, V, dtype == DDTREE_BF16 ? 2 : 4, &S, &chunk);
   if (S > 1) {
-    const size_t need = static_cast<size_t>(rows) * S * (sizeof(uint64_t) + 2 * sizeof(float));
-    if (!workspace || workspace_bytes < need)
+    const size_t need = greedy_ws_bytes(rows, S);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
       return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: workspace of %zu bytes needed, got %zu",
                   need, workspace_bytes);
   }
