@@ -82,18 +82,19 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
 
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(rotate - 1)]
     tree = lib.alloc_tree(cfg.B, cfg.budget, cfg.D, cfg.K, dev)
-    outputs = {"accept_len": torch.empty(cfg.B, dtype=torch.int32, device=dev),
+    # accept_len and bonus side by side, so that one copy brings both to the host
+    result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
+    outputs = {"accept_len": result[0],
                "path_nodes": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
                "out_tokens": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
-               "bonus": torch.empty(cfg.B, dtype=torch.int32, device=dev)}
+               "bonus": result[1]}
     attn_out = torch.empty_like(base["q"])
     ws_a = torch.empty(max(16, lib.ddtree_tree_attention_workspace_size(
         cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, inp["ctx_offsets"])), dtype=torch.uint8,
         device=dev)
     ws_v = torch.zeros(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
                        dtype=torch.uint8, device=dev)
-    host_acc = torch.empty(cfg.B, dtype=torch.int32, pin_memory=True)
-    host_bonus = torch.empty(cfg.B, dtype=torch.int32, pin_memory=True)
+    host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
     stream = torch.cuda.current_stream()
     T = cfg.temperature
 
@@ -116,8 +117,7 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
                                      small["uniforms"], outputs=outputs)
         else:
             lib.ddtree_verify_greedy(tree, v["argmax"], outputs=outputs)
-        host_acc.copy_(outputs["accept_len"], non_blocking=True)
-        host_bonus.copy_(outputs["bonus"], non_blocking=True)
+        host_result.copy_(result, non_blocking=True)
 
     for i in range(warmup):
         step(i)
@@ -173,7 +173,54 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
     attn_ms = timed_calls(attention, reps)
     vocab_ms = timed_calls(vocab, reps)
     return {"t_sync": t_sync, "t_pipe": t_pipe, "attn_ms": attn_ms, "vocab_ms": vocab_ms,
-            "total_ctx": tot_ctx, "accept_len_mean": float(host_acc.float().mean())}
+            "total_ctx": tot_ctx, "accept_len_mean": float(host_result[0].float().mean())}
+
+
+def run_copy_calibration(mib, reps=20):
+    """A plain device-to-device copy of a known size (for scaling HBM counters)
+    and its bandwidth, the practical ceiling of a streaming kernel here."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"copy_bytes_read": n, "copy_bytes_written": n, "copies": reps + 1,
+            "copy_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tree_attention_single_hbm_traffic.md")
+
+
+def attention_source_digest():
+    import hashlib
+    p = os.path.join(ROOT, "tree_verification_build_amd", "csrc", "attention.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(cfg_name):
+    """HBM bytes per tree-attention call from the committed counter summary, or
+    None when it covers another workload or an older attention source."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    vals = dict(line.split(":", 1) for line in text.splitlines()
+                if line.startswith(("workload:", "source_digest:", "traffic_bytes_per_call:")))
+    vals = {k.strip(): v.strip() for k, v in vals.items()}
+    if vals.get("workload") != cfg_name or vals.get("source_digest") != attention_source_digest():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def run_cpu_baseline(cfg, seconds):
@@ -223,7 +270,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter scaling) and print it")
     args = ap.parse_args()
+    if args.copy_calibration:
+        print(json.dumps(run_copy_calibration(args.copy_calibration)), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the verify path here is built and timed on a "
               "single MI355X (no collectives); run with --gpus 1", file=sys.stderr)
@@ -259,7 +311,7 @@ def main():
                    "launch": "eager" if args.eager else "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "ddtree_tree_attention",
+                     "traffic": measured_traffic(cfg.name), "kernel": "ddtree_tree_attention",
                      "bytes_per_launch": ab["attention"], "avg_ms": round(r["attn_ms"], 5)},
         "pipelined_steps_per_s": round(args.steps / r["t_pipe"], 2),
         "vocab_reduce": {"achieved_GBs": round(vocab_gbs, 1), "avg_ms": round(r["vocab_ms"], 5),
