@@ -45,6 +45,8 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of masked keys is 0
 
+constexpr int kTabMax = 16;
+
 struct AttnArgs {
   const void* q;
   const void* k_ctx;
@@ -61,6 +63,11 @@ struct AttnArgs {
   float* lse;
   float* ws_o;        // [total_splits * Hkv, M, Dh] unnormalised partial outputs
   float2* ws_ml;      // [total_splits * Hkv, M] (running max in log2 units, sum)
+  // split plan for B <= kTabMax (tab_n = B, else 0): request b owns splits
+  // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b+1])
+  int tab_n;
+  int tab_split0[kTabMax + 1];
+  int tab_off[kTabMax + 1];
 };
 
 // ------------------------------------------------------------------ dtype policies
@@ -200,6 +207,70 @@ struct PolicyF32 {
   }
 };
 
+// ------------------------------------------------------------------ split lookup
+// Work item of a workgroup: request b, split index and count, context range.
+struct SplitItem {
+  int b, split, nsplit, ctx0, len;
+};
+
+// Which request owns split `sid` (splits are numbered request by request,
+// ceil(L_b / SK) of them, at least one).  For up to kTabMax requests the host
+// passes the split and context offsets in the kernel arguments; otherwise
+// wave 0 searches ctx_offsets and publishes the result in LDS.
+__device__ __forceinline__ void find_split(const AttnArgs& a, int sid, int SK, int lane,
+                                           SplitItem* out);
+
+__device__ __forceinline__ SplitItem lookup_split(const AttnArgs& a, int sid, int wave, int lane,
+                                                  SplitItem* shared_item) {
+  if (a.tab_n > 0) {
+    int b = 0;
+    while (b + 1 < a.tab_n && sid >= a.tab_split0[b + 1]) ++b;
+    if (sid >= a.tab_split0[a.tab_n]) return SplitItem{-1, 0, 0, 0, 0};
+    return SplitItem{b, sid - a.tab_split0[b], a.tab_split0[b + 1] - a.tab_split0[b], a.tab_off[b],
+                     a.tab_off[b + 1] - a.tab_off[b]};
+  }
+  if (wave == 0) find_split(a, sid, a.split_keys, lane, shared_item);
+  __syncthreads();
+  return *shared_item;
+}
+
+__device__ __forceinline__ void find_split(const AttnArgs& a, int sid, int SK, int lane,
+                                           SplitItem* out) {
+  int acc = 0, fb = -1, fs = 0, fn = 0, fo = 0, fl = 0;
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int bb = b0 + lane;
+    int nb = 0, off = 0, L = 0;
+    if (bb < a.B) {
+      off = a.ctx_offsets[bb];
+      L = a.ctx_offsets[bb + 1] - off;
+      nb = L > 0 ? (L + SK - 1) / SK : 1;
+    }
+    int incl = nb;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    const int excl = acc + incl - nb;
+    if (bb < a.B && sid >= excl && sid < excl + nb) {
+      fb = bb;
+      fs = sid - excl;
+      fn = nb;
+      fo = off;
+      fl = L;
+    }
+    acc += __shfl(incl, 63, 64);
+  }
+  const uint64_t hit = __ballot(fb >= 0);
+  if (lane == 0) out->b = -1;
+  if (hit) {
+    const int src = __builtin_ctzll(hit);
+    const int bb = __shfl(fb, src, 64), ss = __shfl(fs, src, 64), nn = __shfl(fn, src, 64);
+    const int oo = __shfl(fo, src, 64), ll = __shfl(fl, src, 64);
+    if (lane == 0) *out = SplitItem{bb, ss, nn, oo, ll};
+  }
+}
+
 // ------------------------------------------------------------------ main kernel
 template <class P, int QB, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
@@ -211,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   elem* k_lds = reinterpret_cast<elem*>(smem);
   elem* v_lds = k_lds + KT * P::template k_stride<KT>();
-  __shared__ int s_b, s_split, s_nsplit;
+  __shared__ SplitItem s_item;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -219,48 +290,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int row0 = blockIdx.z * 128;          // query-row slice of this workgroup
   const int SK = a.split_keys;
 
-  // which request and split this workgroup owns: prefix over per-request split counts
-  if (wave == 0) {
-    int acc = 0, fb = -1, fs = 0, fn = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-      const int b = b0 + lane;
-      int nb = 0;
-      if (b < a.B) {
-        const int L = a.ctx_offsets[b + 1] - a.ctx_offsets[b];
-        nb = L > 0 ? (L + SK - 1) / SK : 1;
-      }
-      int incl = nb;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-      }
-      const int excl = acc + incl - nb;
-      if (b < a.B && sid >= excl && sid < excl + nb) {
-        fb = b;
-        fs = sid - excl;
-        fn = nb;
-      }
-      acc += __shfl(incl, 63, 64);
-    }
-    const uint64_t hit = __ballot(fb >= 0);
-    if (lane == 0) s_b = -1;
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      const int b = __shfl(fb, src, 64), s = __shfl(fs, src, 64), n = __shfl(fn, src, 64);
-      if (lane == 0) {
-        s_b = b;
-        s_split = s;
-        s_nsplit = n;
-      }
-    }
-  }
-  __syncthreads();
-  const int b = s_b;
+  const SplitItem it = lookup_split(a, sid, wave, lane, &s_item);
+  const int b = it.b;
   if (b < 0) return;
-  const int split = s_split, nsplit = s_nsplit;
-  const int ctx0 = a.ctx_offsets[b];
-  const int L = a.ctx_offsets[b + 1] - ctx0;
+  const int split = it.split, nsplit = it.nsplit;
+  const int ctx0 = it.ctx0;
+  const int L = it.len;
   const int k0 = split * SK, k1 = min(L, k0 + SK);
   const bool last = split == nsplit - 1;
   const int nctx_tiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
@@ -414,7 +449,10 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 // row 4g + j/4, column d0 + 4 (j % 4) -- exactly the key order of the S^T
 // accumulator.  The DMA is issued from inline asm with explicit vmcnt waits,
 // because the compiler's own tracking would wait for every DMA before each
-// LDS read.
+// LDS read.  Per tile, only the last context tile of a split and the tree
+// tiles are masked, and the running maximum may lag (kLagLog2), so the common
+// tile is two MFMA products, one cross-row max, the exponentials and one
+// accumulation.
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
@@ -433,84 +471,67 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// max / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48): the gfx950
+// lane swaps return {x, x of the partner lane} in some order
+__device__ __forceinline__ float rows_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Rows keep a running maximum that may lag the true one by up to this many
+// log2 units: the accumulators are rescaled only when a score exceeds it by
+// more, so p = 2^(s - m) stays <= 2^8 and the rescale is rare.
+constexpr float kLagLog2 = 8.0f;
+
 template <int QB, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   using elem = uint16_t;
-  constexpr int DH = 128, KT = 64, KB = KT / 16, QF = DH / 32;
-  constexpr int TILE = 2 * KT * DH * 2;           // bytes: K then V
+  constexpr int DH = 128, KT = 64, KB = KT / 16, QF = DH / 32, DB = DH / 16;
+  constexpr int HALF = KT * DH * 2;               // 16 KB: the K (or V) rows of a tile
+  constexpr int TILE = 2 * HALF;
   constexpr int DPW = 32 / NW;                    // 1 KB DMA instructions per wave per tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int s_b, s_split, s_nsplit, s_ctx0, s_len;
+  __shared__ SplitItem s_item;
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<size_t>(
       (__attribute__((address_space(3))) unsigned char*)(smem)));
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int sid = blockIdx.x, kvh = blockIdx.y;
   const int row0 = blockIdx.z * 128;
   const int SK = a.split_keys;
 
-  if (wave == 0) {
-    int acc = 0, fb = -1, fs = 0, fn = 0, fo = 0, fl = 0;
-    for (int b0 = 0; b0 < a.B; b0 += 64) {
-      const int bb = b0 + lane;
-      int nb = 0, off = 0, L = 0;
-      if (bb < a.B) {
-        off = a.ctx_offsets[bb];
-        L = a.ctx_offsets[bb + 1] - off;
-        nb = L > 0 ? (L + SK - 1) / SK : 1;
-      }
-      int incl = nb;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += o;
-      }
-      const int excl = acc + incl - nb;
-      if (bb < a.B && sid >= excl && sid < excl + nb) {
-        fb = bb;
-        fs = sid - excl;
-        fn = nb;
-        fo = off;
-        fl = L;
-      }
-      acc += __shfl(incl, 63, 64);
-    }
-    const uint64_t hit = __ballot(fb >= 0);
-    if (lane == 0) s_b = -1;
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      const int bb = __shfl(fb, src, 64), ss = __shfl(fs, src, 64), nn2 = __shfl(fn, src, 64);
-      const int oo = __shfl(fo, src, 64), ll = __shfl(fl, src, 64);
-      if (lane == 0) {
-        s_b = bb;
-        s_split = ss;
-        s_nsplit = nn2;
-        s_ctx0 = oo;
-        s_len = ll;
-      }
-    }
-  }
-  __syncthreads();
-  const int b = s_b;
+  const SplitItem it = lookup_split(a, sid, wave, lane, &s_item);
+  const int b = it.b;
   if (b < 0) return;
-  const int split = s_split, nsplit = s_nsplit;
-  const int ctx0 = s_ctx0, L = s_len;
-  const int k0 = split * SK, k1 = min(L, k0 + SK);
-  const bool last = split == nsplit - 1;
+  const int k0 = it.split * SK, k1 = min(it.len, k0 + SK);
+  const bool last = it.split == it.nsplit - 1;
   const int nctx_tiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
   const int ntiles = nctx_tiles + (last ? (a.N + KT - 1) / KT : 0);
-  const elem* kc = static_cast<const elem*>(a.k_ctx);
-  const elem* vc = static_cast<const elem*>(a.v_ctx);
-  const elem* kt = static_cast<const elem*>(a.k_tree);
-  const elem* vt = static_cast<const elem*>(a.v_tree);
 
   // DMA of tile t into ring slot t % NS: this wave's DPW groups of four rows
+  // (groups 0..15 are K rows, 16..31 V rows)
   const int rstride = a.Hkv * DH;   // elements between consecutive keys
-  const elem* kc0 = kc + (static_cast<long>(ctx0) * a.Hkv + kvh) * DH;
-  const elem* vc0 = vc + (static_cast<long>(ctx0) * a.Hkv + kvh) * DH;
-  const elem* kt0 = kt + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
-  const elem* vt0 = vt + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
+  const elem* kc0 = static_cast<const elem*>(a.k_ctx) + (static_cast<long>(it.ctx0) * a.Hkv + kvh) * DH;
+  const elem* vc0 = static_cast<const elem*>(a.v_ctx) + (static_cast<long>(it.ctx0) * a.Hkv + kvh) * DH;
+  const elem* kt0 = static_cast<const elem*>(a.k_tree) + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
+  const elem* vt0 = static_cast<const elem*>(a.v_tree) + (static_cast<long>(b) * a.N * a.Hkv + kvh) * DH;
+  const int lrow = lane >> 4, lchunk = lane & 15;
+  int loff[DPW];
+#pragma unroll
+  for (int j = 0; j < DPW; ++j) {
+    const int r = 4 * ((wave * DPW + j) & 15) + lrow;
+    loff[j] = r * rstride + ((lchunk ^ (r & 7)) * 8);
+  }
 #define DDT_DMA_TILE(T_)                                                                        \
   do {                                                                                          \
     const int t_ = (T_);                                                                        \
@@ -518,14 +539,23 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const int base_ = ctx_ ? k0 + t_ * KT : (t_ - nctx_tiles) * KT;                             \
     const int lim_ = (ctx_ ? k1 : a.N) - 1;                                                     \
     const uint32_t slot_ = smem_base + static_cast<uint32_t>((t_ % NS) * TILE);                 \
-    _Pragma("unroll") for (int j_ = 0; j_ < DPW; ++j_) {                                        \
-      const int rg_ = wave * DPW + j_; /* 0..15: K rows, 16..31: V rows */                      \
-      const int vp_ = rg_ >> 4, rq_ = rg_ & 15;                                                 \
-      const int r_ = 4 * rq_ + (lane >> 4);                                                     \
-      const int key_ = min(base_ + r_, lim_);                                                   \
-      const elem* src_ = (vp_ ? (ctx_ ? vc0 : vt0) : (ctx_ ? kc0 : kt0)) +                      \
-                         static_cast<long>(key_) * rstride + (((lane & 15) ^ (r_ & 7)) * 8);    \
-      dma16(src_, slot_ + static_cast<uint32_t>(vp_ * (KT * DH * 2) + rq_ * 1024));             \
+    if (base_ + KT - 1 <= lim_) {                                                               \
+      _Pragma("unroll") for (int j_ = 0; j_ < DPW; ++j_) {                                      \
+        const int rg_ = wave * DPW + j_;                                                        \
+        const elem* p_ = (rg_ >> 4 ? (ctx_ ? vc0 : vt0) : (ctx_ ? kc0 : kt0)) +                 \
+                         static_cast<long>(base_) * rstride;                                    \
+        dma16(p_ + loff[j_], slot_ + static_cast<uint32_t>((rg_ >> 4) * HALF + (rg_ & 15) * 1024)); \
+      }                                                                                         \
+    } else {                                                                                    \
+      _Pragma("unroll") for (int j_ = 0; j_ < DPW; ++j_) {                                      \
+        const int rg_ = wave * DPW + j_;                                                        \
+        const int vp_ = rg_ >> 4, rq_ = rg_ & 15;                                               \
+        const int r_ = 4 * rq_ + lrow;                                                          \
+        const int key_ = min(base_ + r_, lim_);                                                 \
+        const elem* src_ = (vp_ ? (ctx_ ? vc0 : vt0) : (ctx_ ? kc0 : kt0)) +                    \
+                           static_cast<long>(key_) * rstride + ((lchunk ^ (r_ & 7)) * 8);       \
+        dma16(src_, slot_ + static_cast<uint32_t>(vp_ * HALF + rq_ * 1024));                    \
+      }                                                                                         \
     }                                                                                           \
   } while (0)
 
@@ -558,10 +588,11 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   // compiler's own wait tracking see this wait.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  f32x4_t o[DH / 16];
+  f32x4_t o[DB];
 #pragma unroll
-  for (int db = 0; db < DH / 16; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig, l_run = 0.f;
+  const float c = a.scale_log2;
 
   for (int t = 0; t < ntiles; ++t) {
     // tiles issued after t and possibly still in flight: min(ntiles - 1, t + NS - 2) - t
@@ -574,19 +605,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     if (t + NS - 1 < ntiles) DDT_DMA_TILE(t + NS - 1);
     if (!computes) continue;
     const unsigned char* kbuf = smem + (t % NS) * TILE;
-    const unsigned char* vbuf = kbuf + KT * DH * 2;
-    // key mask of this tile for this lane's query row: context keys below k1,
-    // tree keys by the visibility word (tree tiles are the 64-key words)
-    uint64_t mask;
-    if (t < nctx_tiles) {
-      const int n = k1 - (k0 + t * KT);
-      mask = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
-    } else {
-      mask = t == nctx_tiles ? vis0 : vis1;
-    }
-    const uint64_t mg = mask >> (4 * g);
+    const unsigned char* vbuf = kbuf + HALF;
     f32x4_t sv[KB];
-    float tmax = kNegBig;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int row = kb * 16 + l16;
@@ -597,43 +617,59 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
             kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & 7)) * 16));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (mg >> (kb * 16 + i)) & 1ull;
-        const float sc = ok ? acc[i] * a.scale_log2 : -__builtin_huge_valf();
-        acc[i] = sc;
-        tmax = max(tmax, sc);
-      }
       sv[kb] = acc;
     }
-    tmax = max(tmax, shfl_xor_f32(tmax, 16));
-    tmax = max(tmax, shfl_xor_f32(tmax, 32));
-    const float m_new = max(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // masks: only the last context tile of a split and the tree tiles have any
+    if (!(t < nctx_tiles && k0 + (t + 1) * KT <= k1)) {
+      uint64_t mask;
+      if (t < nctx_tiles) {
+        const int n = k1 - (k0 + t * KT);   // < 64 here
+        mask = (1ull << n) - 1ull;
+      } else {
+        mask = t == nctx_tiles ? vis0 : vis1;
+      }
+      const uint64_t mg = mask >> (4 * g);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!((mg >> (kb * 16 + e)) & 1ull)) sv[kb][e] = -__builtin_huge_valf();
+    }
+    // online softmax in base 2 with a lagging maximum
+    float t0 = max(max(sv[0][0], sv[0][1]), max(sv[0][2], sv[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < KB; ++kb)
+      t0 = max(t0, max(max(sv[kb][0], sv[kb][1]), max(sv[kb][2], sv[kb][3])));
+    const float mc = rows_max(t0) * c;
+    const bool up = mc > m_run + kLagLog2;
+    if (__builtin_amdgcn_ballot_w64(up)) {
+      const float m_new = up ? mc : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(sv[kb][i] - m_new);
-        sv[kb][i] = pv;
+      for (int e = 0; e < 4; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[kb][e], c, -m_run));
+        sv[kb][e] = pv;
         psum += pv;
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DH / 16; ++db) o[db] *= alpha;
+    l_run += psum;
 #pragma unroll
     for (int j = 0; j < KT / 32; ++j) {
       bf16x8_t pf;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pf[i] = static_cast<__bf16>(sv[2 * j][i]);
-        pf[4 + i] = static_cast<__bf16>(sv[2 * j + 1][i]);
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = static_cast<__bf16>(sv[2 * j][e]);
+        pf[4 + e] = static_cast<__bf16>(sv[2 * j + 1][e]);
       }
 #pragma unroll
-      for (int db = 0; db < DH / 16; ++db) {
+      for (int db = 0; db < DB; ++db) {
         i16x4_t h[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -651,17 +687,17 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       }
     }
   }
+#undef DDT_DMA_TILE
   if (!computes) return;
 
-  float l_tot = l_run + shfl_xor_f32(l_run, 16);
-  l_tot += shfl_xor_f32(l_tot, 32);
+  const float l_tot = rows_sum(l_run);
   if (r >= a.M) return;
-  if (nsplit == 1) {
+  if (it.nsplit == 1) {
     elem* orow = static_cast<elem*>(a.out) + ((static_cast<long>(b) * a.N + node) * a.Hq + head) * DH;
     const bool valid = node < nn;
     const float inv = valid && l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db) PolicyBF16<DH>::store_out(orow + db * 16 + 4 * g, o[db] * inv);
+    for (int db = 0; db < DB; ++db) PolicyBF16<DH>::store_out(orow + db * 16 + 4 * g, o[db] * inv);
     if (a.lse && g == 0)
       a.lse[(static_cast<long>(b) * a.N + node) * a.Hq + head] =
           valid ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
@@ -669,7 +705,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const long pr = (static_cast<long>(sid) * a.Hkv + kvh) * a.M + r;
     float* dst = a.ws_o + pr * DH;
 #pragma unroll
-    for (int db = 0; db < DH / 16; ++db)
+    for (int db = 0; db < DB; ++db)
       *reinterpret_cast<float4*>(dst + db * 16 + 4 * g) =
           make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
     if (g == 0) a.ws_ml[pr] = make_float2(m_run, l_tot);
@@ -935,6 +971,19 @@ extern "C" ddtree_status ddtree_tree_attention(
   a.M = M;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.split_keys = sk;
+  a.tab_n = 0;
+  if (B <= kTabMax) {
+    a.tab_n = B;
+    int acc = 0;
+    for (int b = 0; b < B; ++b) {
+      const int L = ctx_offsets_host[b + 1] - ctx_offsets_host[b];
+      a.tab_split0[b] = acc;
+      a.tab_off[b] = ctx_offsets_host[b];
+      acc += L > 0 ? (L + sk - 1) / sk : 1;
+    }
+    a.tab_split0[B] = acc;
+    a.tab_off[B] = ctx_offsets_host[B];
+  }
   a.out = out;
   a.lse = lse;
   a.ws_o = nullptr;
