@@ -92,7 +92,7 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
     ws_a = torch.empty(max(16, lib.ddtree_tree_attention_workspace_size(
         cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, inp["ctx_offsets"])), dtype=torch.uint8,
         device=dev)
-    ws_v = torch.zeros(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
+    ws_v = torch.empty(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
                        dtype=torch.uint8, device=dev)
     host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
     stream = torch.cuda.current_stream()

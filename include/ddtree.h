@@ -158,9 +158,9 @@ ddtree_status ddtree_tree_attention(const void* q, const void* k_ctx, const void
  *             recomputes the same w.
  *   lse       [B, N] fp32 natural-log log-sum-exp of the raw logits, or NULL
  *   workspace ddtree_vocab_reduce_workspace_size(B, N, V) bytes (may be 0),
- *             16-byte aligned.  It must be zero-filled before its first use;
- *             every call leaves it zero-filled again, so one zeroed buffer can
- *             serve any number of calls (calls sharing it must not overlap).
+ *             16-byte aligned device scratch; contents need no
+ *             initialisation and are garbage afterwards (calls sharing it
+ *             must not overlap).
  * Errors: DDTREE_EINVAL (null pointers, sizes, temperature < 0 or NaN).
  */
 size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32_t V);

@@ -199,8 +199,7 @@ def ddtree_vocab_reduce(logits, num_nodes, temperature=0.0, want_lse=False, work
     lse = torch.empty((B, N), dtype=torch.float32, device=dev) if want_lse else None
     need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
     if workspace is None or workspace.numel() < need:
-        # must start zeroed; the library leaves it zeroed after every call
-        workspace = torch.zeros((max(need, 16),), dtype=torch.uint8, device=dev)
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _check(lib.ddtree_vocab_reduce(_ptr(logits), _dtype_code(logits), B, N, V, _ptr(num_nodes),
                                    float(temperature), _ptr(argmax), _ptr(maxv), _ptr(R),
                                    _ptr(lse), _ptr(workspace), workspace.numel(),

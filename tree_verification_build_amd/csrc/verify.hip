@@ -31,15 +31,24 @@ __global__ __launch_bounds__(64) void greedy_kernel(ddtree_tree t, const int32_t
   const int lane = threadIdx.x;
   const int N = t.N, D = t.D;
   const long base = static_cast<long>(b) * N;
+  // the tree and argmax rows are read before num_nodes is known (all N
+  // entries exist), so that the loads do not wait for it
+  int par[2], tok[2], am[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int j = lane + s * kWave;
+    par[s] = j < N ? t.parent[base + j] : -2;
+    tok[s] = j < N ? t.token[base + j] : -2;
+    am[s] = j < N ? argmax[base + j] : -1;
+  }
   const int nn = t.num_nodes[b];
-  int par[2], tok[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int j = lane + s * kWave;
     const bool ok = j < nn;
-    par[s] = ok ? t.parent[base + j] : -2;
-    tok[s] = ok ? t.token[base + j] : -2;
-    if (j < N) s_am[j] = ok ? argmax[base + j] : -1;
+    par[s] = ok ? par[s] : -2;
+    tok[s] = ok ? tok[s] : -2;
+    if (j < N) s_am[j] = ok ? am[s] : -1;
   }
   __syncthreads();
   int32_t* path = path_nodes + static_cast<long>(b) * (D + 1);

@@ -7,12 +7,12 @@
 // its slice with 16-byte coalesced loads and reduces a packed 64-bit key
 // (order-preserving value bits << 32 | ~token id), whose maximum is the
 // largest logit at the lowest id; it also keeps a running (max, sum exp) for
-// the optional log-sum-exp.  When a row is split (S > 1) each slice merges its
-// key into the row's slot with a 64-bit atomic max and takes a ticket; the
-// slice that draws the last ticket writes the row's results and clears the
-// slot and the ticket counter, so the workspace is zero again after every
-// call.  Integer keys make the merge order irrelevant: the argmax is the same
-// for any S.
+// the optional log-sum-exp.  When a row is split (S > 1) each slice stores its
+// key (and max, sum) in the workspace and a second, one-wave-per-row kernel
+// merges the S slices: a kernel boundary orders the two without device-scope
+// atomics, whose round trips and per-row contention cost more than the extra
+// launch.  Integer keys make the merge order irrelevant: the argmax is the
+// same for any S.
 //
 // Sampling mode needs the row maximum before any weight can be formed, so one
 // 1024-thread workgroup owns a row and keeps it in registers: one HBM read,
@@ -107,44 +107,70 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 template <typename T, bool kLse>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes, int S,
-    int chunk, uint64_t* __restrict__ ws_key, uint32_t* __restrict__ ws_cnt,
-    float2* __restrict__ ws_ms, int32_t* __restrict__ argmax, float* __restrict__ maxv,
+    int chunk, uint64_t* __restrict__ ws_key, float2* __restrict__ ws_ms,
+    int32_t* __restrict__ argmax, float* __restrict__ maxv,
     float* __restrict__ lse) {
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kSplitThreads / kWave;
   __shared__ uint64_t s_key[kWaves];
   __shared__ float2 s_ms[kWaves];
-  __shared__ int s_last;
   const int row = blockIdx.y;
   const int s = blockIdx.x;
   const int b = row / N, n = row % N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool valid = n < num_nodes[b];
+  // The slice is read whatever num_nodes says (rows of padding nodes exist in
+  // memory), so that its loads do not wait for that value; padding rows are
+  // discarded afterwards.  U vectors per thread are in flight at a time.
+  constexpr int U = 4;
   uint64_t key = 0;
   float m = -__builtin_huge_valf(), sum = 0.0f;
-  if (valid) {
+  {
     const T* rp = logits + static_cast<long>(row) * V;
     const bool vec = aligned16(rp);
+    const bool fast = vec && V % E == 0;   // every in-range vector is whole (chunk % E == 0)
     const int lo = s * chunk, hi = min(V, lo + chunk);
-    for (int i = lo + tid * E; i < hi; i += kSplitThreads * E) {
-      float v[E];
-      load_e<T>(rp, i, hi, vec, v);
-      float vm = v[0];
-      int vi = 0;
+    for (int i0 = lo + tid * E; i0 < hi; i0 += U * kSplitThreads * E) {
+      u32x4_t raw[U];
+      if (fast) {
+        // whole 16-byte vectors: plain predicated loads, all U in flight
+        constexpr uint32_t z = Vec<T>::kNegInfWord;
 #pragma unroll
-      for (int k = 1; k < E; ++k)
-        if (v[k] > vm) { vm = v[k]; vi = k; }
-      const uint64_t kk = pack_key(vm, i + vi);
-      key = kk > key ? kk : key;
-      if (kLse) {
-        float es = 0.0f;
-        const float mm = max(m, vm);
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * kSplitThreads * E;
+          raw[u] = i < hi ? *reinterpret_cast<const u32x4_t*>(rp + i) : u32x4_t{z, z, z, z};
+        }
+      } else {
 #pragma unroll
-        for (int k = 0; k < E; ++k) es += __expf(v[k] - mm);
-        sum = (m > -__builtin_huge_valf() ? sum * __expf(m - mm) : 0.0f) + es;
-        m = mm;
+        for (int u = 0; u < U; ++u) raw[u] = load_raw<T>(rp, i0 + u * kSplitThreads * E, hi, vec);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * kSplitThreads * E;
+        float v[E];
+        Vec<T>::unpack(raw[u], v);
+        float vm = v[0];
+        int vi = 0;
+#pragma unroll
+        for (int k = 1; k < E; ++k)
+          if (v[k] > vm) { vm = v[k]; vi = k; }
+        const uint64_t kk = i < hi ? pack_key(vm, i + vi) : 0ull;
+        key = kk > key ? kk : key;
+        if (kLse && i < hi) {
+          float es = 0.0f;
+          const float mm = max(m, vm);
+#pragma unroll
+          for (int k = 0; k < E; ++k) es += __expf(v[k] - mm);
+          sum = (m > -__builtin_huge_valf() ? sum * __expf(m - mm) : 0.0f) + es;
+          m = mm;
+        }
       }
     }
+  }
+  const bool valid = n < num_nodes[b];
+  if (!valid) {
+    key = 0;
+    m = -__builtin_huge_valf();
+    sum = 0.0f;
   }
   key = wave_max_u64(key);
   if (kLse) {
@@ -168,55 +194,47 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
       argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
       maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
       if (kLse) lse[row] = valid ? m + __logf(sum) : -__builtin_huge_valf();
-      s_last = 0;
     } else {
-      // Publish this slice with device-scope atomics (coherent across the XCDs'
-      // L2s without flushing them), wait for their results, then take a ticket:
-      // the slice holding the last ticket finishes the row.
-      unsigned long long done = 0;
-      if (valid)
-        done += atomicMax(reinterpret_cast<unsigned long long*>(ws_key + row),
-                          static_cast<unsigned long long>(key));
-      if (kLse) {
-        const unsigned long long ms =
-            (static_cast<unsigned long long>(__float_as_uint(sum)) << 32) | __float_as_uint(m);
-        done += atomicExch(reinterpret_cast<unsigned long long*>(ws_ms) + static_cast<long>(row) * S + s, ms);
-      }
-      uint32_t one = 1u;
-      __asm__ volatile("" : "+v"(one) : "v"(done));   // the ticket waits for both returns
-      const uint32_t ticket = atomicAdd(ws_cnt + row, one);
-      s_last = ticket == static_cast<uint32_t>(S - 1);
+      // this slice's partial result; finalize_kernel merges the row's slices
+      ws_key[static_cast<long>(row) * S + s] = key;
+      if (kLse) ws_ms[static_cast<long>(row) * S + s] = make_float2(m, sum);
     }
   }
-  __syncthreads();
-  if (!s_last) return;
-  if (kLse) {
-    // merge the S (max, sum) pairs of the row with the whole workgroup (atomic reads)
-    float mm = -__builtin_huge_valf(), ss = 0.0f;
-    for (int k = tid; k < S; k += kSplitThreads) {
-      const unsigned long long ms = atomicAdd(
-          reinterpret_cast<unsigned long long*>(ws_ms) + static_cast<long>(row) * S + k, 0ull);
-      lse_merge(mm, ss, __uint_as_float(static_cast<uint32_t>(ms)),
-                __uint_as_float(static_cast<uint32_t>(ms >> 32)));
+}
+
+// Merge the S slices of each row (one wave per row): the largest packed key
+// gives argmax and max; the (max, sum) pairs give the log-sum-exp.
+template <bool kLse>
+__global__ __launch_bounds__(kWave) void finalize_kernel(int N, const int32_t* __restrict__ num_nodes,
+                                                         int S, const uint64_t* __restrict__ ws_key,
+                                                         const float2* __restrict__ ws_ms,
+                                                         int32_t* __restrict__ argmax,
+                                                         float* __restrict__ maxv,
+                                                         float* __restrict__ lse) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  uint64_t key = 0;
+  float m = -__builtin_huge_valf(), sum = 0.0f;
+  for (int k = lane; k < S; k += kWave) {
+    const uint64_t kk = ws_key[static_cast<long>(row) * S + k];
+    key = kk > key ? kk : key;
+    if (kLse) {
+      const float2 ms = ws_ms[static_cast<long>(row) * S + k];
+      lse_merge(m, sum, ms.x, ms.y);
     }
+  }
+  key = wave_max_u64(key);
+  if (kLse) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
-      float m2 = shfl_xor_f32(mm, o), s2 = shfl_xor_f32(ss, o);
-      lse_merge(mm, ss, m2, s2);
-    }
-    if (lane == 0) s_ms[wave] = make_float2(mm, ss);
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < kWaves; ++w) lse_merge(mm, ss, s_ms[w].x, s_ms[w].y);
-      lse[row] = valid ? mm + __logf(ss) : -__builtin_huge_valf();
+      float m2 = shfl_xor_f32(m, o), s2 = shfl_xor_f32(sum, o);
+      lse_merge(m, sum, m2, s2);
     }
   }
-  if (tid == 0) {
-    // read and clear the row's key and ticket counter (the workspace is left zeroed)
-    const uint64_t k = atomicExch(reinterpret_cast<unsigned long long*>(ws_key + row), 0ull);
-    atomicExch(ws_cnt + row, 0u);
-    argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(k)) : -1;
-    maxv[row] = valid ? unord_f32(static_cast<uint32_t>(k >> 32)) : -__builtin_huge_valf();
+  if (lane == 0) {
+    const bool valid = row % N < num_nodes[row / N];
+    argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
+    maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
+    if (kLse) lse[row] = valid ? m + __logf(sum) : -__builtin_huge_valf();
   }
 }
 
@@ -441,31 +459,35 @@ void launch_sampling(int rows, hipStream_t st, const void* logits, int N, int V,
                        static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
 }
 
-// Greedy workspace: [rows] uint64 keys, [rows] uint32 tickets (zero between calls),
-// then [rows * S] float2 log-sum-exp partials.
+// Greedy workspace: [rows * S] uint64 slice keys, then [rows * S] float2
+// (max, sum) slice partials; no initialisation needed.
 size_t greedy_ws_bytes(int rows, int S) {
   if (S <= 1) return 0;
-  const size_t keys = static_cast<size_t>(rows) * sizeof(uint64_t);
-  const size_t cnt = (static_cast<size_t>(rows) * sizeof(uint32_t) + 15) / 16 * 16;
-  return keys + cnt + static_cast<size_t>(rows) * S * sizeof(float2);
+  return static_cast<size_t>(rows) * S * (sizeof(uint64_t) + sizeof(float2));
 }
 
 template <typename T>
 void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
                    int S, int chunk, void* ws, int32_t* am, float* mx, float* lse) {
   uint64_t* ws_key = static_cast<uint64_t*>(ws);
-  uint32_t* ws_cnt = reinterpret_cast<uint32_t*>(ws_key + rows);
-  float2* ws_ms = reinterpret_cast<float2*>(
-      reinterpret_cast<char*>(ws_cnt) + (static_cast<size_t>(rows) * sizeof(uint32_t) + 15) / 16 * 16);
+  float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<size_t>(rows) * S);
   const dim3 grid(S, rows);
   if (lse)
     hipLaunchKernelGGL((split_kernel<T, true>), grid, dim3(kSplitThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_cnt, ws_ms,
-                       am, mx, lse);
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
+                       lse);
   else
     hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_cnt, ws_ms,
-                       am, mx, lse);
+                       static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
+                       lse);
+  if (S > 1) {
+    if (lse)
+      hipLaunchKernelGGL((finalize_kernel<true>), dim3(rows), dim3(kWave), 0, st, N, nn, S, ws_key,
+                         ws_ms, am, mx, lse);
+    else
+      hipLaunchKernelGGL((finalize_kernel<false>), dim3(rows), dim3(kWave), 0, st, N, nn, S, ws_key,
+                         ws_ms, am, mx, lse);
+  }
 }
 
 }  // namespace
