@@ -7,27 +7,24 @@
 // The tree's visibility rows are ancestor-or-self sets; positions are
 // prefix_len + depth ("The Tree That Couldn't Branch", "Hypothesis 3").
 //
-// Design: the frontier is kept sorted (best first) across the 64 lanes of the
-// wavefront, entry j in lane j, as 64-bit keys that order entries exactly as
-// required (score desc, parent asc, rank asc) and carry the entry:
+// Design: one wavefront per request.  Every taken node p has at most one
+// pending offer, its next child not yet taken (the rank-0 child when p is
+// taken, then each next sibling as the previous one is taken), so the
+// frontier is a set of slots, slot p in lane p % 64 (two register pairs for
+// N > 64), each holding a 64-bit key that orders entries exactly as required
+// (score desc, parent asc, rank asc) and carries the entry:
 //   [63:32] order-preserving bits of the fp32 score
 //   [31:24] 255 - parent   [23:16] 255 - rank   [15:8] depth   [7:0] pusher
 // ("pusher" is the node whose taking offered this entry: the parent for a
-// rank-0 child, the rank-1 sibling otherwise).  64 slots are enough for any
-// N <= 128: with r pops left, an entry at position >= r can never be taken,
-// and after k pops the frontier holds at most k + 1 entries, so at most
-// min(k + 1, N - 1 - k) <= N / 2 entries matter; entries pushed past slot 63
-// are dropped.  One step of the loop takes lane 0 (the best entry), forms the
-// best child and the next sibling (key 0 for "none"), and rebuilds the list in
-// one lane-parallel select from three copies of it: shifted down one lane, as
-// is, and shifted up one lane (DPP wave_shl:1 / wave_shr:1), at the two
-// insertion points found by ballots; the lane masks are built with scalar
-// shifts.  Empty slots hold 0, below every real key, so the loop has no
-// data-dependent branch.  The taken key is itself node i's record (kept in lane i % 64).  A single wave pays ~15 cycles per dependent vector op,
-// so the loop does nothing else: tokens, positions, child / sibling links and
-// visibility rows are rebuilt afterwards, all lanes in parallel (visibility by
-// pointer jumping over parent links).  The draft top-k table (D*K <= 256
-// entries) is spread over the lanes and read with v_readlane.
+// rank-0 child, the previous sibling otherwise).  A step takes the slot with
+// the largest key (a DPP maximum of the high words; the low words only break
+// score ties), records it as node i, and writes two keys: node i's best child
+// into slot i and the parent's next child into slot parent (0 for "none").
+// The step is a serial chain of ~85 instructions in one wave, so the loop
+// does nothing else: tokens, positions, child / sibling links and visibility
+// rows are rebuilt afterwards, all lanes in parallel (visibility by pointer
+// jumping over parent links).  The draft top-k table (D*K <= 256 entries) is
+// spread over the lanes and read with v_readlane.
 #include "common.hpp"
 
 namespace ddt {
@@ -46,10 +43,16 @@ __device__ __forceinline__ uint64_t make_key(float score, int parent, int rank, 
   return make_key_bits(ord_f32(score), parent, rank, depth, pusher);
 }
 
-// ord_f32 of raw float bits held in a (uniform) integer: stays in scalar registers
-__device__ __forceinline__ uint32_t ord_f32_s(uint32_t u) {
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// fp32 bits of the value an order-preserving key word encodes
+__device__ __forceinline__ uint32_t unord_f32_bits(uint32_t o) {
+  return (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+}
+
+// order-preserving bits of fp32 bits (-0 as +0), as plain integer operations
+__device__ __forceinline__ uint32_t ord_bits(uint32_t u) {
+  u = u == 0x80000000u ? 0u : u;
+  const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+  return u ^ (m | 0x80000000u);
 }
 
 // value of a per-lane register table at flat index idx (uniform): one readlane
@@ -63,17 +66,17 @@ __device__ __forceinline__ uint32_t table_at(const uint32_t (&r)[4], int idx) {
   return w == 0 ? a0 : w == 1 ? a1 : w == 2 ? a2 : a3;
 }
 
-// whole-wave lane shifts (DPP): down(v)[i] = v[i+1], up(v)[i] = v[i-1]; 0 shifted in
-__device__ __forceinline__ uint32_t lanes_down(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x130, 0xF, 0xF, false));
-}
-__device__ __forceinline__ uint32_t lanes_up(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x138, 0xF, 0xF, false));
-}
-
-// v[l] = val for one uniform lane l
-__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t val, int l) {
-  return static_cast<int>(threadIdx.x) == l ? val : v;
+// Maximum over the wavefront with DPP: within each row of 16 lanes (quad_perm
+// swaps, row_ror 4 and 8), then row_bcast15 / row_bcast31 carry the running
+// maximum into the last row; lane 63 ends with the total.
+__device__ __forceinline__ uint32_t wave_max_bcast_u32(uint32_t v) {
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x142, 0xA, 0xF, false)));
+  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x143, 0xC, 0xF, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63));
 }
 
 // lane-varying gather from the per-lane table (ds_bpermute)
@@ -117,56 +120,63 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
   // records: the taken key of node i sits in lane i % 64 of (rh0, rl0) or (rh1, rl1);
   // the root's record carries score +0.0 (its other fields are never read)
   uint32_t rh0 = lane == 0 ? ord_f32(0.0f) : 0u, rl0 = 0u, rh1 = 0u, rl1 = 0u;
-  // frontier: entry `lane` as (fh, fl); 0 = empty
+  // frontier slots: every taken node p has at most one pending offer, its
+  // next child not yet taken, and that offer sits in slot p (lane p % 64 of
+  // (sh0, sl0) or (sh1, sl1)); key 0 = none.  The root's first child starts
+  // in slot 0.
   const uint64_t first = make_key(0.0f + __uint_as_float(table_at<REGS>(lp_r, 0)), 0, 0, 1, 0);
-  uint32_t fh = lane == 0 ? static_cast<uint32_t>(first >> 32) : 0u;
-  uint32_t fl = lane == 0 ? static_cast<uint32_t>(first) : 0u;
+  uint32_t sh0 = lane == 0 ? static_cast<uint32_t>(first >> 32) : 0u;
+  uint32_t sl0 = lane == 0 ? static_cast<uint32_t>(first) : 0u;
+  uint32_t sh1 = 0u, sl1 = 0u;
 
   int count = 1;
   for (; count < N; ++count) {
+    // the best slot: largest key; the high word (score) decides unless tied
+    uint32_t mh = sh0, ml = sl0;
+    if (TWO) {
+      const bool in1 = ((static_cast<uint64_t>(sh1) << 32) | sl1) > ((static_cast<uint64_t>(sh0) << 32) | sl0);
+      mh = in1 ? sh1 : sh0;
+      ml = in1 ? sl1 : sl0;
+    }
+    const uint32_t bh = wave_max_bcast_u32(mh);
+    if (bh == 0) break;  // no offers left
+    const uint64_t tied = __ballot(mh == bh);
+    int w = __builtin_ctzll(tied);
+    if (tied & (tied - 1)) w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32(mh == bh ? ml : 0u)));
     // readlane yields a signed int: cast before widening, or the low word sign-extends
-    const uint32_t bh = static_cast<uint32_t>(__builtin_amdgcn_readlane(fh, 0));
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(fl, 0));
-    if (bh == 0) break;  // frontier empty
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(ml, w));
     const int parent = 255 - static_cast<int>(lo >> 24);
     const int rank = 255 - static_cast<int>((lo >> 16) & 0xFF);
     const int depth = static_cast<int>((lo >> 8) & 0xFF);
     const int i = count;
-    // the three shifted copies do not depend on this step's offers
-    const uint32_t dh = lanes_down(fh), dl = lanes_down(fl);
-    const uint32_t uh = lanes_up(fh), ul = lanes_up(fl);
-    // record node i
-    if (!TWO || i < 64) {
-      rh0 = write_lane(rh0, bh, i & 63);
-      rl0 = write_lane(rl0, lo, i & 63);
-    } else {
-      rh1 = write_lane(rh1, bh, i & 63);
-      rl1 = write_lane(rl1, lo, i & 63);
+    const uint32_t pscore = unord_f32_bits(static_cast<uint32_t>(
+        __builtin_amdgcn_readlane(TWO && parent >= 64 ? rh1 : rh0, parent & 63)));
+    // record node i (branch-free: lane i of the low registers or lane i - 64
+    // of the high ones)
+    const bool at_i0 = lane == i, at_i1 = TWO && lane + 64 == i;
+    const bool at_p0 = lane == parent, at_p1 = TWO && lane + 64 == parent;
+    rh0 = at_i0 ? bh : rh0;
+    rl0 = at_i0 ? lo : rl0;
+    if (TWO) {
+      rh1 = at_i1 ? bh : rh1;
+      rl1 = at_i1 ? lo : rl1;
     }
-
-    // offers: best child and next sibling (key 0 when there is none)
-    const float score = unord_f32(bh);
+    // offers: node i's best child goes to slot i, the parent's next child
+    // replaces the taken one in slot parent (key 0 when there is none)
     const float lpc = __uint_as_float(table_at<REGS>(lp_r, min(depth, D - 1) * K));
-    const uint32_t cs = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(__float_as_uint(score + lpc)));
-    const uint64_t kc = depth < D ? make_key_bits(ord_f32_s(cs), i, 0, depth + 1, i) : 0ull;
-    const uint32_t pr = static_cast<uint32_t>(
-        __builtin_amdgcn_readlane(TWO && parent >= 64 ? rh1 : rh0, parent & 63));
     const float lps = __uint_as_float(table_at<REGS>(lp_r, (depth - 1) * K + min(rank + 1, K - 1)));
-    const uint32_t ss = static_cast<uint32_t>(
-        __builtin_amdgcn_readfirstlane(__float_as_uint(unord_f32(pr) + lps)));
-    const uint64_t ks = rank + 1 < K ? make_key_bits(ord_f32_s(ss), parent, rank + 1, depth, i) : 0ull;
-    const uint64_t k1 = kc > ks ? kc : ks, k2 = kc > ks ? ks : kc;
-    // both offers rank below the entry just taken, so they land after slot 0
-    const uint64_t mine = (static_cast<uint64_t>(fh) << 32) | fl;
-    const int q1 = __builtin_popcountll(__ballot(mine > k1)) - 1;
-    const int q2 = __builtin_popcountll(__ballot(mine > k2));
-    const uint64_t lt1 = (1ull << q1) - 1ull, lt2 = q2 >= 64 ? ~0ull : (1ull << q2) - 1ull;
-    const bool below1 = (lt1 >> lane) & 1ull, at1 = lane == q1;
-    const bool below2 = (lt2 >> lane) & 1ull, at2 = lane == q2;
-    const uint32_t k1h = static_cast<uint32_t>(k1 >> 32), k1l = static_cast<uint32_t>(k1);
-    const uint32_t k2h = static_cast<uint32_t>(k2 >> 32), k2l = static_cast<uint32_t>(k2);
-    fh = below1 ? dh : at1 ? k1h : below2 ? fh : at2 ? k2h : uh;
-    fl = below1 ? dl : at1 ? k1l : below2 ? fl : at2 ? k2l : ul;
+    const uint32_t cs = __float_as_uint(__uint_as_float(unord_f32_bits(bh)) + lpc);
+    const uint32_t ss = __float_as_uint(__uint_as_float(pscore) + lps);
+    const uint64_t kc = depth < D ? make_key_bits(ord_bits(cs), i, 0, depth + 1, i) : 0ull;
+    const uint64_t ks = rank + 1 < K ? make_key_bits(ord_bits(ss), parent, rank + 1, depth, i) : 0ull;
+    const uint32_t kch = static_cast<uint32_t>(kc >> 32), kcl = static_cast<uint32_t>(kc);
+    const uint32_t ksh = static_cast<uint32_t>(ks >> 32), ksl = static_cast<uint32_t>(ks);
+    sh0 = at_i0 ? kch : at_p0 ? ksh : sh0;
+    sl0 = at_i0 ? kcl : at_p0 ? ksl : sl0;
+    if (TWO) {
+      sh1 = at_i1 ? kch : at_p1 ? ksh : sh1;
+      sl1 = at_i1 ? kcl : at_p1 ? ksl : sl1;
+    }
   }
 
   // rebuild the node arrays from the records, every lane in parallel
