@@ -859,21 +859,16 @@ void launch_qb(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
   }
 }
 
-template <int QB, int NS>
-void launch_dma_ns(const AttnArgs& a, int total_splits, hipStream_t st) {
-  constexpr int NW = QB <= 4 ? 4 : 8;
-  const size_t lds = static_cast<size_t>(NS) * 2 * 64 * 128 * 2;
-  const dim3 grid(total_splits, a.Hkv, (a.M + 127) / 128);
-  hipLaunchKernelGGL((attn_dma_kernel<QB, NW, NS>), grid, dim3(NW * 64), lds, st, a);
-}
+// Two LDS stages (64 KB): two workgroups per CU, each with one tile in flight
+// while it computes the other; deeper rings measured no faster.
+constexpr int kDmaStages = 2;
 
 template <int QB>
 void launch_dma_qb(const AttnArgs& a, int total_splits, hipStream_t st) {
-  const char* e = std::getenv("DDTREE_ATTN_STAGES");
-  const int ns = e ? std::atoi(e) : 2;
-  if (ns == 2) launch_dma_ns<QB, 2>(a, total_splits, st);
-  else if (ns == 3) launch_dma_ns<QB, 3>(a, total_splits, st);
-  else launch_dma_ns<QB, 4>(a, total_splits, st);
+  constexpr int NW = QB <= 4 ? 4 : 8;
+  const size_t lds = static_cast<size_t>(kDmaStages) * 2 * 64 * 128 * 2;
+  const dim3 grid(total_splits, a.Hkv, (a.M + 127) / 128);
+  hipLaunchKernelGGL((attn_dma_kernel<QB, NW, kDmaStages>), grid, dim3(NW * 64), lds, st, a);
 }
 
 void launch_dma(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
@@ -947,8 +942,6 @@ extern "C" ddtree_status ddtree_tree_attention(
       (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)))
     return fail(DDTREE_EINVAL, "ddtree_tree_attention: tensors must be 16-byte aligned");
   const int qb = (std::min(M, 128) + 15) / 16;   // 16-row query blocks per slice
-  const char* dma_env = std::getenv("DDTREE_ATTN_DMA");
-  const bool use_dma = !(dma_env && dma_env[0] == '0');
   const int kt = keys_per_tile(dtype, Dh, qb);
   const int sk = plan_split_keys(ctx_offsets_host, B, Hkv, kt);
   bool multi;
@@ -998,8 +991,7 @@ extern "C" ddtree_status ddtree_tree_attention(
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + need);
   }
   if (dtype == DDTREE_BF16) {
-    if (Dh == 128 && use_dma) launch_dma(qb, a, total, stream);
-    else if (Dh == 128) launch_qb<PolicyBF16<128>>(qb, a, total, stream);
+    if (Dh == 128) launch_dma(qb, a, total, stream);
     else launch_qb<PolicyBF16<64>>(qb, a, total, stream);
   } else {
     if (Dh == 128) launch_qb<PolicyF32<128>>(qb, a, total, stream);
