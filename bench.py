@@ -113,7 +113,7 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
         attention(s)
         v = vocab(s)
         if T > 0:
-            lib.ddtree_verify_sample(tree, s["logits"], v["maxv"], v["R"], T,
+            lib.ddtree_verify_sample(tree, s["logits"], v["maxv"], v["R"], v["R_blocks"], T,
                                      small["uniforms"], outputs=outputs)
         else:
             lib.ddtree_verify_greedy(tree, v["argmax"], outputs=outputs)

@@ -57,6 +57,7 @@ typedef enum { DDTREE_F32 = 0, DDTREE_BF16 = 1 } ddtree_dtype;
 #define DDTREE_MAX_NODES 128  /* N = budget + 1 */
 #define DDTREE_MAX_DEPTH 64   /* D */
 #define DDTREE_MAX_TOPK 64    /* K */
+#define DDTREE_R_BLOCK 32768  /* tokens per block of the sampling weight sums (R_blocks) */
 
 /*
  * The token tree of a batch: structure-of-arrays, one row of N = budget + 1
@@ -155,20 +156,27 @@ ddtree_status ddtree_tree_attention(const void* q, const void* k_ctx, const void
  *             separately rounded multiplies and adds, coefficients
  *             fp32((ln 2)^n / n!), and w = 0 when y < -32.  w/R is the
  *             temperature-T softmax to ~1e-6 relative; ddtree_verify_sample
- *             recomputes the same w.
+ *             recomputes the same w.  Sampling rows need V <= 64 * DDTREE_R_BLOCK.
+ *   R_blocks  [B, N, ceil(V / DDTREE_R_BLOCK)] uint64 or NULL: the same weights
+ *             summed over each block of DDTREE_R_BLOCK consecutive tokens
+ *             (R is their sum); ddtree_verify_sample uses them to find the
+ *             block of its residual draw without re-weighing the whole row.
+ *             Written only when temperature > 0 (padding rows: 0).
  *   lse       [B, N] fp32 natural-log log-sum-exp of the raw logits, or NULL
  *   workspace ddtree_vocab_reduce_workspace_size(B, N, V) bytes (may be 0),
  *             16-byte aligned device scratch; contents need no
  *             initialisation and are garbage afterwards (calls sharing it
  *             must not overlap).
- * Errors: DDTREE_EINVAL (null pointers, sizes, temperature < 0 or NaN).
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature < 0 or NaN),
+ *         DDTREE_EUNSUPPORTED (sampling with V > 64 * DDTREE_R_BLOCK).
  */
 size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32_t V);
 
 ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_t B, int32_t N,
                                   int32_t V, const int32_t* num_nodes, float temperature,
-                                  int32_t* argmax, float* maxv, uint64_t* R, float* lse,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  int32_t* argmax, float* maxv, uint64_t* R, uint64_t* R_blocks,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * ddtree_verify_greedy -- greedy verified-tree walk.
@@ -198,14 +206,19 @@ ddtree_status ddtree_verify_greedy(const ddtree_tree* tree, const int32_t* argma
  * excluded.  Children are tried in rank order.  When no child is accepted (or
  * the node is a leaf), the bonus is the smallest token x whose running sum of
  * non-excluded weights exceeds floor(u' * R_res / 2^64).
- *   logits [B, N, V] dtype, maxv [B, N], R [B, N] from ddtree_vocab_reduce with
- *   the same temperature; uniforms [B, N, 2] uint64: slot 0 = the node's
- *   accept test, slot 1 = its bonus draw.  Outputs as ddtree_verify_greedy.
- * Errors: DDTREE_EINVAL (null pointers, sizes, temperature <= 0 or NaN).
+ *   logits [B, N, V] dtype, maxv [B, N], R [B, N] and R_blocks
+ *   [B, N, ceil(V / DDTREE_R_BLOCK)] from ddtree_vocab_reduce with the same
+ *   temperature; uniforms [B, N, 2] uint64: slot 0 = the node's accept test,
+ *   slot 1 = its bonus draw.  Outputs as ddtree_verify_greedy.
+ *   The residual draw subtracts the rejected tokens' weights from their
+ *   blocks, picks the block holding the draw, and weighs only that block.
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature <= 0 or NaN),
+ *         DDTREE_EUNSUPPORTED (V > 64 * DDTREE_R_BLOCK).
  */
 ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const void* logits,
                                    ddtree_dtype dtype, int32_t V, const float* maxv,
-                                   const uint64_t* R, float temperature, const uint64_t* uniforms,
+                                   const uint64_t* R, const uint64_t* R_blocks, float temperature,
+                                   const uint64_t* uniforms,
                                    int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
                                    int32_t* bonus, hipStream_t stream);
 

@@ -21,6 +21,9 @@ import numpy as np
 
 # 1/ln(2) as the nearest double (C's M_LOG2E)
 LOG2E = float.fromhex("0x1.71547652b82fep+0")
+# tokens per block of the per-block weight sums (a layout choice of the
+# interface, not of the pages: any partition of the row sums to R)
+R_BLOCK = 32768
 
 
 def weight_constants(temperature: float):
@@ -60,14 +63,19 @@ def vocab_reduce(logits, num_nodes, temperature: float = 0.0, dtype: str = "f32"
     """logits [B, N, V] (bf16 bits as uint16, or float32); num_nodes [B].
 
     Returns argmax i32 [B, N], maxv f32 [B, N], lse f64 [B, N] and, if T > 0,
-    R u64 [B, N].  Padding rows (n >= num_nodes[b]): argmax -1, maxv -inf,
-    lse -inf, R 0.  `rows` optionally restricts the work to a list of (b, n)."""
+    R u64 [B, N] and R_blocks u64 [B, N, ceil(V / R_BLOCK)]: the same weights
+    summed over each run of R_BLOCK consecutive tokens (a partition of R, used
+    to locate a residual draw).  Padding rows (n >= num_nodes[b]): argmax -1,
+    maxv -inf, lse -inf, R 0, R_blocks 0.  `rows` optionally restricts the work
+    to a list of (b, n)."""
     x = np.asarray(logits)
     B, N, V = x.shape
     argmax = np.full((B, N), -1, dtype=np.int32)
     maxv = np.full((B, N), -np.inf, dtype=np.float32)
     lse = np.full((B, N), -np.inf, dtype=np.float64)
     R = np.zeros((B, N), dtype=np.uint64)
+    nb = -(-V // R_BLOCK)
+    R_blocks = np.zeros((B, N, nb), dtype=np.uint64)
     if temperature > 0:
         c, a = weight_constants(temperature)
     todo = [(b, n) for b in range(B) for n in range(int(num_nodes[b]))] if rows is None else rows
@@ -82,5 +90,8 @@ def vocab_reduce(logits, num_nodes, temperature: float = 0.0, dtype: str = "f32"
         r64 = row.astype(np.float64)
         lse[b, n] = np.logaddexp.reduce(r64)
         if temperature > 0:
-            R[b, n] = int(weights(row, maxv[b, n], c, a).sum(dtype=np.uint64))
-    return {"argmax": argmax, "maxv": maxv, "lse": lse, "R": R}
+            w = weights(row, maxv[b, n], c, a)
+            R[b, n] = int(w.sum(dtype=np.uint64))
+            for k in range(nb):
+                R_blocks[b, n, k] = int(w[k * R_BLOCK:(k + 1) * R_BLOCK].sum(dtype=np.uint64))
+    return {"argmax": argmax, "maxv": maxv, "lse": lse, "R": R, "R_blocks": R_blocks}

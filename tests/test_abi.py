@@ -77,21 +77,27 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 8, ctypes.byref(bad), None) == 1
     assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 8, None, None) == 1
     # vocab
-    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 0, fake, 0.0, fake, fake, None, None, None, 0,
-                                   None) == 1
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 0, fake, 0.0, fake, fake, None, None, None,
+                                   None, 0, None) == 1
     assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 100, fake, -1.0, fake, fake, None, None, None,
-                                   0, None) == 1
+                                   None, 0, None) == 1
     assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 100, fake, 0.5, fake, fake, None, None, None,
-                                   0, None) == 1                     # R missing with T > 0
+                                   None, 0, None) == 1               # R missing with T > 0
+    assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 64 * 32768 + 1, fake, 0.5, fake, fake, fake,
+                                   fake, None, None, 0, None) == 2   # sampling row too long
     assert lib.ddtree_vocab_reduce(fake, 7, 1, 9, 100, fake, 0.0, fake, fake, None, None, None,
-                                   0, None) == 1                     # unknown dtype
+                                   None, 0, None) == 1               # unknown dtype
     # greedy split pass needs its workspace at this size
     assert lib.ddtree_vocab_reduce(fake, 1, 1, 9, 163840, fake, 0.0, fake, fake, None, None,
-                                   None, 0, None) == 1
+                                   None, None, 0, None) == 1
     # walks
     assert lib.ddtree_verify_greedy(ctypes.byref(t), None, fake, fake, fake, fake, None) == 1
-    assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, 0.0, fake, fake,
-                                    fake, fake, fake, None) == 1
+    assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, fake, 0.0, fake,
+                                    fake, fake, fake, fake, None) == 1      # T <= 0
+    assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, None, 0.7, fake,
+                                    fake, fake, fake, fake, None) == 1      # R_blocks missing
+    assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 64 * 32768 + 1, fake, fake, fake,
+                                    0.7, fake, fake, fake, fake, fake, None) == 2
     # attention
     offs = (ctypes.c_int32 * 2)(0, 64)
     args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]

@@ -78,6 +78,7 @@ def test_vocab_reduce(name):
         assert np.abs(lse[fin] - ref["lse"][fin]).max() <= 1e-4
         if T > 0:
             assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
+            assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -106,7 +107,8 @@ def test_verify_sample(name):
     say("verify_sample", name, "T", T)
     t = c.gpu_tree()
     v = lib.ddtree_vocab_reduce(c.d("logits"), t.num_nodes, T)
-    o = lib.ddtree_verify_sample(t, c.d("logits"), v["maxv"], v["R"], T, c.d("uniforms"))
+    o = lib.ddtree_verify_sample(t, c.d("logits"), v["maxv"], v["R"], v["R_blocks"], T,
+                                 c.d("uniforms"))
     torch.cuda.synchronize()
     ref_v = oracle.vocab_reduce(c.logits, c.tree["num_nodes"], T, dtype=c.cfg.dtype)
     ref = oracle.verify_sample(c.tree, c.logits, ref_v["maxv"], ref_v["R"], T,

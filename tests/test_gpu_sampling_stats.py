@@ -34,7 +34,8 @@ def test_gpu_sampling_chi_square(T):
     logits = dev_tensor(np.broadcast_to(row_logits, (B, N, V)).copy(), None)
     u = rng.integers(0, 2 ** 64, size=(B, N, 2), dtype=np.uint64)
     v = lib.ddtree_vocab_reduce(logits, t.num_nodes, T)
-    o = lib.ddtree_verify_sample(t, logits, v["maxv"], v["R"], T, dev_tensor(u, None))
+    o = lib.ddtree_verify_sample(t, logits, v["maxv"], v["R"], v["R_blocks"], T,
+                                 dev_tensor(u, None))
     torch.cuda.synchronize()
     tree1 = oracle.build_tree(lp[None], tok[None], np.array([0]), np.array([0]), 5)
     vr = oracle.vocab_reduce(row_logits[None], tree1["num_nodes"], T)

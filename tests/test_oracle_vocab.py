@@ -116,3 +116,22 @@ def test_lse_and_R_against_independent_sums():
         for v in range(V):
             total += int(weights(row[v:v + 1], m, c, a)[0])
         assert int(res["R"][0, n]) == total
+
+
+def test_block_sums_partition_R():
+    """R_blocks[k] is the exact sum over tokens [k*R_BLOCK, (k+1)*R_BLOCK) and the
+    blocks add up to R (checked with Python integers, token by token)."""
+    from oracle.vocab import R_BLOCK
+    rng = np.random.default_rng(13)
+    B, N, V = 1, 2, 2 * R_BLOCK + 1000
+    xb = f32_to_bf16_bits((rng.standard_normal((B, N, V)) * 3).astype(np.float32))
+    res = vocab_reduce(xb, np.array([1]), 1.0, dtype="bf16")
+    c, a = weight_constants(1.0)
+    row = (xb[0, 0].astype(np.uint32) << 16).view(np.float32)
+    w = [int(x) for x in weights(row, row.max(), c, a)]
+    nb = res["R_blocks"].shape[2]
+    assert nb == 3
+    for k in range(nb):
+        assert int(res["R_blocks"][0, 0, k]) == sum(w[k * R_BLOCK:(k + 1) * R_BLOCK])
+    assert sum(int(x) for x in res["R_blocks"][0, 0]) == int(res["R"][0, 0])
+    assert not res["R_blocks"][0, 1].any()          # padding row

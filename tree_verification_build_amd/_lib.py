@@ -15,6 +15,7 @@ lib = ctypes.CDLL(library_path)
 
 DDTREE_OK, DDTREE_EINVAL, DDTREE_EUNSUPPORTED, DDTREE_EDEVICE = 0, 1, 2, 3
 DDTREE_F32, DDTREE_BF16 = 0, 1
+R_BLOCK = 32768   # DDTREE_R_BLOCK: tokens per block of the sampling weight sums
 _STATUS = {1: "EINVAL", 2: "EUNSUPPORTED", 3: "EDEVICE"}
 
 
@@ -40,10 +41,10 @@ lib.ddtree_tree_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i
                                       ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp]
 lib.ddtree_vocab_reduce_workspace_size.argtypes = [_i32, _i32, _i32]
 lib.ddtree_vocab_reduce_workspace_size.restype = _sz
-lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp,
+lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp]
 lib.ddtree_verify_greedy.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _vp]
-lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _f32, _vp, _vp, _vp,
+lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                      _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce", "ddtree_verify_greedy",
@@ -187,8 +188,8 @@ def ddtree_vocab_reduce_workspace_size(B, N, V) -> int:
 
 def ddtree_vocab_reduce(logits, num_nodes, temperature=0.0, want_lse=False, workspace=None,
                         stream=None):
-    """Returns dict(argmax [B,N] i32, maxv [B,N] f32, R [B,N] int64 bits of uint64 or None,
-    lse [B,N] f32 or None)."""
+    """Returns dict(argmax [B,N] i32, maxv [B,N] f32, R [B,N] and R_blocks
+    [B,N,ceil(V/R_BLOCK)] int64 bits of uint64 (or None when greedy), lse [B,N] f32 or None)."""
     B, N, V = logits.shape
     _dev(logits, "logits", (torch.bfloat16, torch.float32))
     _dev(num_nodes, "num_nodes", torch.int32, (B,))
@@ -196,15 +197,17 @@ def ddtree_vocab_reduce(logits, num_nodes, temperature=0.0, want_lse=False, work
     argmax = torch.empty((B, N), dtype=torch.int32, device=dev)
     maxv = torch.empty((B, N), dtype=torch.float32, device=dev)
     R = torch.empty((B, N), dtype=torch.int64, device=dev) if temperature > 0 else None
+    nb = (V + R_BLOCK - 1) // R_BLOCK
+    Rb = torch.empty((B, N, nb), dtype=torch.int64, device=dev) if temperature > 0 else None
     lse = torch.empty((B, N), dtype=torch.float32, device=dev) if want_lse else None
     need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _check(lib.ddtree_vocab_reduce(_ptr(logits), _dtype_code(logits), B, N, V, _ptr(num_nodes),
                                    float(temperature), _ptr(argmax), _ptr(maxv), _ptr(R),
-                                   _ptr(lse), _ptr(workspace), workspace.numel(),
+                                   _ptr(Rb), _ptr(lse), _ptr(workspace), workspace.numel(),
                                    _stream(stream)))
-    return {"argmax": argmax, "maxv": maxv, "R": R, "lse": lse}
+    return {"argmax": argmax, "maxv": maxv, "R": R, "R_blocks": Rb, "lse": lse}
 
 
 def _walk_outputs(tree):
@@ -224,16 +227,18 @@ def ddtree_verify_greedy(tree, argmax, outputs=None, stream=None):
     return o
 
 
-def ddtree_verify_sample(tree, logits, maxv, R, temperature, uniforms, outputs=None,
+def ddtree_verify_sample(tree, logits, maxv, R, R_blocks, temperature, uniforms, outputs=None,
                          stream=None):
     B, N, V = logits.shape
     _dev(logits, "logits", (torch.bfloat16, torch.float32))
     _dev(maxv, "maxv", torch.float32, (B, N))
     _dev(R, "R", torch.int64, (B, N))
+    _dev(R_blocks, "R_blocks", torch.int64, (B, N, (V + R_BLOCK - 1) // R_BLOCK))
     _dev(uniforms, "uniforms", torch.int64, (B, N, 2))
     o = outputs or _walk_outputs(tree)
     _check(lib.ddtree_verify_sample(tree.cstruct, _ptr(logits), _dtype_code(logits), V,
-                                    _ptr(maxv), _ptr(R), float(temperature), _ptr(uniforms),
+                                    _ptr(maxv), _ptr(R), _ptr(R_blocks), float(temperature),
+                                    _ptr(uniforms),
                                     _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
                                     _ptr(o["out_tokens"]), _ptr(o["bonus"]), _stream(stream)))
     return o

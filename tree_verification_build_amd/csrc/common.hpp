@@ -66,6 +66,12 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 __device__ __forceinline__ float shfl_xor_f32(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+  return v;
+}
+
 __device__ __forceinline__ uint64_t shfl_up_u64(uint64_t v, int d) {
   return __shfl_up(v, d, kWave);
 }
@@ -104,9 +110,9 @@ __device__ __forceinline__ uint64_t weight(float l, float m, const WeightConsts&
 #pragma clang fp contract(off)
   const float y0 = (l - m) * wc.c;
   const bool keep = y0 >= -32.0f;
-  const float y = keep ? y0 : -32.0f;
-  float k = __builtin_rintf(y);
-  float f = y - k;
+  const float y = max(y0, -32.0f);   // only the kept range matters below
+  const float k = __builtin_rintf(y);
+  const float f = y - k;
   float p = wc.a[6];
   p = p * f; p = p + wc.a[5];
   p = p * f; p = p + wc.a[4];
@@ -114,10 +120,14 @@ __device__ __forceinline__ uint64_t weight(float l, float m, const WeightConsts&
   p = p * f; p = p + wc.a[2];
   p = p * f; p = p + wc.a[1];
   p = p * f; p = p + wc.a[0];
-  uint32_t P = static_cast<uint32_t>(p * 16777216.0f);
-  const int e = 8 + static_cast<int>(k);
-  const uint64_t w = e >= 0 ? (static_cast<uint64_t>(P) << e) : static_cast<uint64_t>(P >> (-e));
-  return keep ? w : 0ull;
+  // p in [0.7, 1.42] has at most 24 significant bits above 2^-24, so
+  // P = p * 2^24 is an exact integer < 2^25, and floor(p * 2^(32 + k)) =
+  // floor(P * 2^(8 + k)) = (P * 2^24) >> (16 - k) with 16 - k in [16, 48];
+  // a shift of 63 gives the 0 of a dropped (y < -32) weight
+  const uint32_t P = static_cast<uint32_t>(p * 16777216.0f);
+  const uint32_t sh = keep ? static_cast<uint32_t>(16.0f - k) : 63u;
+  const uint64_t P24 = (static_cast<uint64_t>(P >> 8) << 32) | (P << 24);
+  return P24 >> sh;
 }
 
 // ---------------------------------------------------------------- element access

@@ -83,19 +83,46 @@ __global__ __launch_bounds__(64) void greedy_kernel(ddtree_tree t, const int32_t
 constexpr int kSampleThreads = 1024;
 constexpr int kSampleWaves = kSampleThreads / kWave;
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 32 consecutive tokens of a row, as floats (16-byte loads when the row is
+// aligned and whole, element loads otherwise); tokens past V read as -inf
+template <typename T>
+__device__ __forceinline__ void load32(const T* row, long x0, int V, float (&v)[32]) {
+  constexpr int P = Elem<T>::kPer16;   // elements per 16 bytes
+  if (aligned16(row + x0) && x0 + 32 <= V) {
+#pragma unroll
+    for (int q = 0; q < 32 / P; ++q) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + x0 + q * P);
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        if (P == 8) v[q * P + e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+        else v[q * P + e] = __uint_as_float(w[e]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e)
+      v[e] = x0 + e < V ? Elem<T>::get(row, x0 + e) : -__builtin_huge_valf();
+  }
+}
+
+constexpr int kTokPerThread = DDTREE_R_BLOCK / kSampleThreads;
+static_assert(kTokPerThread == 32, "one weight block = 32 tokens per thread");
+
 template <typename T>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     ddtree_tree t, const T* __restrict__ logits, int V, const float* __restrict__ maxv,
-    const uint64_t* __restrict__ R, WeightConsts wc, const uint64_t* __restrict__ uniforms,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ path_nodes,
-    int32_t* __restrict__ out_tokens, int32_t* __restrict__ bonus) {
-  __shared__ uint64_t s_w[kMaxN];
+    const uint64_t* __restrict__ R, const uint64_t* __restrict__ Rb, WeightConsts wc,
+    const uint64_t* __restrict__ uniforms, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path_nodes, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ bonus) {
+  __shared__ uint64_t s_w[kMaxN], s_R[kMaxN], s_u0[kMaxN], s_u1[kMaxN];
   __shared__ int32_t s_tok[kMaxN], s_fc[kMaxN], s_ns[kMaxN];
   __shared__ int32_t s_rej[DDTREE_MAX_TOPK];
   __shared__ uint64_t s_wave[kSampleWaves];
-  __shared__ int s_nrej, s_cur, s_a;
-  __shared__ uint64_t s_t, s_found_excl;
-  __shared__ int s_found_thread;
+  __shared__ int s_nrej, s_cur, s_a, s_blk, s_found_thread;
+  __shared__ uint64_t s_trem, s_found_excl;
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -104,44 +131,49 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const int N = t.N, D = t.D;
   const long base = static_cast<long>(b) * N;
   const int nn = t.num_nodes[b];
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+
+  // every node's token, links, totals, uniforms and the weight of its token
+  // under its parent's row, one thread per node
+  for (int j = tid; j < N; j += kSampleThreads) {
+    uint64_t w = 0;
+    int tk = -1, fc = -1, ns = -1;
+    if (j < nn) {
+      tk = t.token[base + j];
+      fc = t.first_child[base + j];
+      ns = t.next_sibling[base + j];
+      if (j > 0 && tk >= 0 && tk < V) {
+        const int p = t.parent[base + j];
+        const float l = Elem<T>::get(logits, (base + p) * static_cast<long>(V) + tk);
+        w = weight(l, maxv[base + p], wc);
+      }
+    }
+    s_w[j] = w;
+    s_tok[j] = tk;
+    s_fc[j] = fc;
+    s_ns[j] = ns;
+    s_R[j] = R[base + j];
+    s_u0[j] = uniforms[(base + j) * 2 + 0];
+    s_u1[j] = uniforms[(base + j) * 2 + 1];
+  }
+  if (tid == 0) s_found_thread = -1;
+  __syncthreads();
 
   if (wave == 0) {
-    // weights of every node's token under its parent's row
-    for (int j = lane; j < N; j += kWave) {
-      uint64_t w = 0;
-      int tk = -1, fc = -1, ns = -1;
-      if (j < nn) {
-        tk = t.token[base + j];
-        fc = t.first_child[base + j];
-        ns = t.next_sibling[base + j];
-        if (j > 0 && tk >= 0 && tk < V) {
-          const int p = t.parent[base + j];
-          const float l = Elem<T>::get(logits, (base + p) * static_cast<long>(V) + tk);
-          w = weight(l, maxv[base + p], wc);
-        }
-      }
-      s_w[j] = w;
-      s_tok[j] = tk;
-      s_fc[j] = fc;
-      s_ns[j] = ns;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    // the walk (every lane follows the same uniform path)
+    // the walk (every lane follows the same uniform path); both loops are
+    // capped (depth <= D, children <= K), so a malformed tree cannot hang
     int32_t* path = path_nodes + static_cast<long>(b) * (D + 1);
     int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
     int cur = 0, a = 0, nrej = 0;
     uint64_t rres = 0;
-    // both loops are capped (depth <= D, children <= K), so a malformed tree cannot hang
     while (true) {
-      rres = R[base + cur];
+      rres = s_R[cur];
       nrej = 0;
       int c = s_fc[cur];
       bool moved = false;
       while (c >= 0 && c < N && nrej < t.K) {
-        const uint64_t tt = __umul64hi(uniforms[(base + c) * 2 + 0], rres);
         const uint64_t wcur = s_w[c];
-        if (tt < wcur) {
+        if (__umul64hi(s_u0[c], rres) < wcur) {
           moved = true;
           break;
         }
@@ -156,13 +188,31 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
       ++a;
       if (lane == 0) path[a] = c;
     }
+    // residual draw: which weight block holds it (the rejected tokens'
+    // weights come off their blocks), one block per lane
+    const uint64_t tdraw = __umul64hi(s_u1[cur], rres);
+    uint64_t bs = 0;   // nb <= 64 (checked on the host)
+    if (lane < nb) {
+      bs = Rb[(base + cur) * nb + lane];
+      int c = s_fc[cur];
+      for (int r = 0; r < nrej && c >= 0; ++r) {   // the rejected children, in order
+        if (s_tok[c] / DDTREE_R_BLOCK == lane) bs -= s_w[c];
+        c = s_ns[c];
+      }
+    }
+    const uint64_t incl = wave_incl_scan_u64(bs, lane);
+    const uint64_t hit = __ballot(lane < nb && incl > tdraw);
+    const int blk = hit ? __builtin_ctzll(hit) : nb - 1;
+    const uint64_t ex = incl - bs;
+    const uint32_t exl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex), blk));
+    const uint32_t exh = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex >> 32), blk));
     if (lane == 0) {
       path[0] = 0;
-      s_found_thread = -1;
       s_nrej = nrej;
       s_cur = cur;
       s_a = a;
-      s_t = __umul64hi(uniforms[(base + cur) * 2 + 1], rres);
+      s_blk = blk;
+      s_trem = tdraw - ((static_cast<uint64_t>(exh) << 32) | exl);
       accept_len[b] = a;
     }
     for (int k = a + 1 + lane; k <= D; k += kWave) {
@@ -172,44 +222,38 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   }
   __syncthreads();
 
-  // residual draw over the stopping node's row
-  const int cur = s_cur;
-  const int nrej = s_nrej;
-  const uint64_t tdraw = s_t;
+  // within the block: 32 consecutive tokens per thread, an exclusive scan of
+  // the per-thread sums in token order, then the thread holding the draw
+  // walks its tokens
+  const int cur = s_cur, nrej = s_nrej;
+  const uint64_t trem = s_trem;
   const float m = maxv[base + cur];
   const T* row = logits + (base + cur) * static_cast<long>(V);
-  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
-  const int lo = min(V, tid * seg), hi = min(V, lo + seg);
+  const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
+  float v[32];
+  load32<T>(row, x0, V, v);
   uint64_t sum = 0;
-  for (int x = lo; x < hi; ++x) sum += weight(Elem<T>::get(row, x), m, wc);
+#pragma unroll
+  for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);   // -inf past V weighs 0
   for (int r = 0; r < nrej; ++r) {
-    const int x = s_rej[r];
-    if (x >= lo && x < hi) sum -= weight(Elem<T>::get(row, x), m, wc);
+    const long x = s_rej[r];
+    if (x >= x0 && x < x0 + 32) sum -= weight(v[x - x0], m, wc);   // rejected: excluded
   }
-  // exclusive prefix of per-thread sums over the workgroup
   const uint64_t incl = wave_incl_scan_u64(sum, lane);
   if (lane == kWave - 1) s_wave[wave] = incl;
   __syncthreads();
   uint64_t before = 0;
-  for (int w = 0; w < wave; ++w) before += s_wave[w];
+  for (int k = 0; k < wave; ++k) before += s_wave[k];
   const uint64_t excl = before + incl - sum;
-  if (excl <= tdraw && tdraw < excl + sum) {
-    s_found_thread = tid;
-    s_found_excl = excl;
-  }
-  __syncthreads();
-  if (tid == s_found_thread) {
-    uint64_t acc = s_found_excl;
+  if (excl <= trem && trem < excl + sum) {
+    uint64_t acc = excl;
     int pick = -1;
-    for (int x = lo; x < hi; ++x) {
+    for (int e = 0; e < 32 && pick < 0; ++e) {
       bool rej = false;
-      for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x);
+      for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x0 + e);
       if (rej) continue;
-      acc += weight(Elem<T>::get(row, x), m, wc);
-      if (acc > tdraw) {
-        pick = x;
-        break;
-      }
+      acc += weight(Elem<T>::get(row, x0 + e), m, wc);
+      if (acc > trem) pick = static_cast<int>(x0) + e;
     }
     int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
     outt[s_a] = pick;
@@ -236,26 +280,31 @@ extern "C" ddtree_status ddtree_verify_greedy(const ddtree_tree* tree, const int
 
 extern "C" ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const void* logits,
                                               ddtree_dtype dtype, int32_t V, const float* maxv,
-                                              const uint64_t* R, float temperature,
-                                              const uint64_t* uniforms, int32_t* accept_len,
+                                              const uint64_t* R, const uint64_t* R_blocks,
+                                              float temperature, const uint64_t* uniforms,
+                                              int32_t* accept_len,
                                               int32_t* path_nodes, int32_t* out_tokens,
                                               int32_t* bonus, hipStream_t stream) {
   using namespace ddt;
   ddtree_status st = check_tree(tree, "ddtree_verify_sample");
   if (st != DDTREE_OK) return st;
-  if (!logits || !maxv || !R || !uniforms || !accept_len || !path_nodes || !out_tokens || !bonus)
+  if (!logits || !maxv || !R || !R_blocks || !uniforms || !accept_len || !path_nodes ||
+      !out_tokens || !bonus)
     return fail(DDTREE_EINVAL, "ddtree_verify_sample: null pointer");
   if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf()))
     return fail(DDTREE_EINVAL, "ddtree_verify_sample: temperature must be > 0 and finite");
   if (V < 1) return fail(DDTREE_EINVAL, "ddtree_verify_sample: V must be >= 1");
+  if (V > kWave * DDTREE_R_BLOCK)
+    return fail(DDTREE_EUNSUPPORTED, "ddtree_verify_sample: V = %d exceeds %d", V,
+                kWave * DDTREE_R_BLOCK);
   const WeightConsts wc = weight_consts(temperature);
   if (dtype == DDTREE_BF16) {
     hipLaunchKernelGGL(sample_kernel<uint16_t>, dim3(tree->B), dim3(kSampleThreads), 0, stream,
-                       *tree, static_cast<const uint16_t*>(logits), V, maxv, R, wc, uniforms,
+                       *tree, static_cast<const uint16_t*>(logits), V, maxv, R, R_blocks, wc, uniforms,
                        accept_len, path_nodes, out_tokens, bonus);
   } else if (dtype == DDTREE_F32) {
     hipLaunchKernelGGL(sample_kernel<float>, dim3(tree->B), dim3(kSampleThreads), 0, stream,
-                       *tree, static_cast<const float*>(logits), V, maxv, R, wc, uniforms,
+                       *tree, static_cast<const float*>(logits), V, maxv, R, R_blocks, wc, uniforms,
                        accept_len, path_nodes, out_tokens, bonus);
   } else {
     return fail(DDTREE_EINVAL, "ddtree_verify_sample: unknown dtype %d", static_cast<int>(dtype));

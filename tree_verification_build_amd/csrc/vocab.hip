@@ -28,6 +28,8 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSplitThreads = 256;
+// blocks of DDTREE_R_BLOCK tokens a sampling row may have (V <= 64 blocks)
+constexpr int kMaxRowBlocks = 64;
 constexpr int kRowThreads = 1024;
 
 // 16 bytes of logits (E = 8 bf16 or 4 fp32 values): raw bits and their floats.
@@ -244,11 +246,15 @@ template <typename T, int MAXP, bool kLse>
 __global__ __launch_bounds__(kRowThreads) void row_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
     WeightConsts wc, int32_t* __restrict__ argmax, float* __restrict__ maxv,
-    uint64_t* __restrict__ R, float* __restrict__ lse) {
+    uint64_t* __restrict__ R, uint64_t* __restrict__ Rb, float* __restrict__ lse) {
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kRowThreads / kWave;
-  __shared__ uint64_t s_u[kWaves];
+  constexpr int kPassPerBlock = DDTREE_R_BLOCK / (kRowThreads * E);   // passes per weight block
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  __shared__ uint64_t s_u[kMaxRowBlocks];
+  __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
   __shared__ float s_f[kWaves];
+  __shared__ uint32_t s_i[kWaves];
   const int row = blockIdx.x;
   const int b = row / N, n = row % N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -259,6 +265,8 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
       R[row] = 0;
       if (kLse) lse[row] = -__builtin_huge_valf();
     }
+    if (Rb)
+      for (int k = tid; k < nb; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
     return;
   }
   // rows are 16-byte aligned and V is a multiple of E here (checked on the host)
@@ -270,28 +278,52 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
     const uint32_t z = Vec<T>::kNegInfWord;
     raw[p] = i < V ? *reinterpret_cast<const u32x4_t*>(rp + i) : u32x4_t{z, z, z, z};
   }
-  uint64_t key = 0;
+  // the row maximum as a plain float maximum (one op per element), then the
+  // lowest index holding it, searched only by the threads that hold it;
+  // float equality treats -0 and +0 alike, as the packed keys of the greedy
+  // pass do
+  float vmax = -__builtin_huge_valf();
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     float v[E];
     Vec<T>::unpack(raw[p], v);
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      const uint64_t kk = pack_key(v[k], p * kRowThreads * E + tid * E + k);
-      key = kk > key ? kk : key;
-    }
+    for (int k = 0; k < E; ++k) vmax = max(vmax, v[k]);
     __builtin_amdgcn_sched_barrier(0);   // one pass at a time: bounds live registers
   }
-  key = wave_max_u64(key);
-  if (lane == 0) s_u[wave] = key;
-  __syncthreads();
-  key = s_u[0];
+  float bm = vmax;
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) key = s_u[w] > key ? s_u[w] : key;
-  const float m = unord_f32(static_cast<uint32_t>(key >> 32));
+  for (int o = 32; o >= 1; o >>= 1) bm = max(bm, shfl_xor_f32(bm, o));
+  if (lane == 0) s_f[wave] = bm;
   __syncthreads();
+  float m = s_f[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = max(m, s_f[w]);
+  m = m + 0.0f;   // -0 -> +0
+  uint32_t first = 0xFFFFFFFFu;
+  if (vmax == m) {
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+      float v[E];
+      Vec<T>::unpack(raw[p], v);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        const uint32_t idx = static_cast<uint32_t>(p * kRowThreads * E + tid * E + k);
+        first = (v[k] == m && idx < first) ? idx : first;
+      }
+    }
+  }
+  first = wave_min_u32(first);
+  __syncthreads();
+  if (lane == 0) s_i[wave] = first;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
 
-  uint64_t wsum = 0;
+  // weights, summed per block of DDTREE_R_BLOCK tokens (kPassPerBlock passes):
+  // each wave's share of a block goes to LDS, the row total is the sum of
+  // the blocks
+  uint64_t bsum = 0;
   float esum = 0.0f;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
@@ -302,29 +334,36 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
     Vec<T>::unpack(raw[p], v);
 #pragma unroll
     for (int k = 0; k < E; ++k) {
-      wsum += weight(v[k], m, wc);
+      bsum += weight(v[k], m, wc);
       if (kLse) esum += __expf(v[k] - m);
+    }
+    if ((p + 1) % kPassPerBlock == 0 || p == MAXP - 1) {
+      const uint64_t ws = wave_sum_u64(bsum);
+      if (lane == 0) s_blk[p / kPassPerBlock][wave] = ws;
+      bsum = 0;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  wsum = wave_sum_u64(wsum);
   if (kLse) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) esum += shfl_xor_f32(esum, o);
   }
-  if (lane == 0) {
-    s_u[wave] = wsum;
-    s_f[wave] = esum;
+  if (lane == 0) s_f[wave] = esum;
+  __syncthreads();
+  if (tid < nb) {
+    uint64_t bt = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) bt += s_blk[tid][w];
+    if (Rb) Rb[static_cast<long>(row) * nb + tid] = bt;
+    s_u[tid] = bt;
   }
   __syncthreads();
   if (tid == 0) {
     uint64_t tot = 0;
     float et = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      tot += s_u[w];
-      et += s_f[w];
-    }
-    argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+    for (int k = 0; k < nb; ++k) tot += s_u[k];
+    for (int w = 0; w < kWaves; ++w) et += s_f[w];
+    argmax[row] = static_cast<int32_t>(first);
     maxv[row] = m;
     R[row] = tot;
     if (kLse) lse[row] = m + __logf(et);
@@ -336,10 +375,13 @@ template <typename T, bool kLse>
 __global__ __launch_bounds__(kRowThreads) void row2_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
     WeightConsts wc, int32_t* __restrict__ argmax, float* __restrict__ maxv,
-    uint64_t* __restrict__ R, float* __restrict__ lse) {
+    uint64_t* __restrict__ R, uint64_t* __restrict__ Rb, float* __restrict__ lse) {
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kRowThreads / kWave;
-  __shared__ uint64_t s_u[kWaves];
+  constexpr int kPassPerBlock = DDTREE_R_BLOCK / (kRowThreads * E);   // passes per weight block
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  __shared__ uint64_t s_u[kMaxRowBlocks > kWaves ? kMaxRowBlocks : kWaves];
+  __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
   __shared__ float s_f[kWaves];
   const int row = blockIdx.x;
   const int b = row / N, n = row % N;
@@ -351,6 +393,8 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
       R[row] = 0;
       if (kLse) lse[row] = -__builtin_huge_valf();
     }
+    if (Rb)
+      for (int k = tid; k < nb; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
     return;
   }
   const T* rp = logits + static_cast<long>(row) * V;
@@ -372,33 +416,41 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
   for (int w = 1; w < kWaves; ++w) key = s_u[w] > key ? s_u[w] : key;
   const float m = unord_f32(static_cast<uint32_t>(key >> 32));
   __syncthreads();
-  uint64_t wsum = 0;
+  // per-block weight sums as in row_kernel, one block of passes at a time
   float esum = 0.0f;
-  for (long i = static_cast<long>(tid) * E; i < V; i += kRowThreads * E) {
-    float v[E];
-    load_e<T>(rp, i, V, vec, v);
+  for (int blk = 0; blk < nb; ++blk) {
+    uint64_t bsum = 0;
+    for (int p = blk * kPassPerBlock; p < (blk + 1) * kPassPerBlock; ++p) {
+      const long i = static_cast<long>(p) * kRowThreads * E + static_cast<long>(tid) * E;
+      if (i >= V) break;
+      float v[E];
+      load_e<T>(rp, i, V, vec, v);
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      wsum += weight(v[k], m, wc);
-      if (kLse) esum += __expf(v[k] - m);
+      for (int k = 0; k < E; ++k) {
+        bsum += weight(v[k], m, wc);
+        if (kLse) esum += __expf(v[k] - m);
+      }
     }
+    const uint64_t ws = wave_sum_u64(bsum);
+    if (lane == 0) s_blk[blk][wave] = ws;
   }
-  wsum = wave_sum_u64(wsum);
   if (kLse) {
     for (int o = 32; o >= 1; o >>= 1) esum += shfl_xor_f32(esum, o);
   }
-  if (lane == 0) {
-    s_u[wave] = wsum;
-    s_f[wave] = esum;
+  if (lane == 0) s_f[wave] = esum;
+  __syncthreads();
+  if (tid < nb) {
+    uint64_t bt = 0;
+    for (int w = 0; w < kWaves; ++w) bt += s_blk[tid][w];
+    if (Rb) Rb[static_cast<long>(row) * nb + tid] = bt;
+    s_u[tid] = bt;
   }
   __syncthreads();
   if (tid == 0) {
     uint64_t tot = 0;
     float et = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      tot += s_u[w];
-      et += s_f[w];
-    }
+    for (int k = 0; k < nb; ++k) tot += s_u[k];
+    for (int w = 0; w < kWaves; ++w) et += s_f[w];
     argmax[row] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key));
     maxv[row] = m;
     R[row] = tot;
@@ -420,19 +472,20 @@ void split_plan(int rows, int V, int elem_bytes, int* S_out, int* chunk_out) {
 
 template <typename T, int MAXP>
 void launch_row(dim3 grid, hipStream_t st, const void* logits, int N, int V, const int32_t* nn,
-                const WeightConsts& wc, int32_t* am, float* mx, uint64_t* R, float* lse) {
+                const WeightConsts& wc, int32_t* am, float* mx, uint64_t* R, uint64_t* Rb,
+                float* lse) {
   if (lse)
     hipLaunchKernelGGL((row_kernel<T, MAXP, true>), grid, dim3(kRowThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
   else
     hipLaunchKernelGGL((row_kernel<T, MAXP, false>), grid, dim3(kRowThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
 }
 
 template <typename T>
 void launch_sampling(int rows, hipStream_t st, const void* logits, int N, int V,
                      const int32_t* nn, const WeightConsts& wc, int32_t* am, float* mx,
-                     uint64_t* R, float* lse) {
+                     uint64_t* R, uint64_t* Rb, float* lse) {
   const int per_pass = kRowThreads * Vec<T>::E;
   const int passes = (V + per_pass - 1) / per_pass;
   const bool fits = V % Vec<T>::E == 0 && aligned16(logits);
@@ -440,23 +493,23 @@ void launch_sampling(int rows, hipStream_t st, const void* logits, int N, int V,
   if (!fits) {
     if (lse)
       hipLaunchKernelGGL((row2_kernel<T, true>), g, dim3(kRowThreads), 0, st,
-                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
     else
       hipLaunchKernelGGL((row2_kernel<T, false>), g, dim3(kRowThreads), 0, st,
-                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
-  } else if (passes <= 1) launch_row<T, 1>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 2) launch_row<T, 2>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 4) launch_row<T, 4>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 8) launch_row<T, 8>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 12) launch_row<T, 12>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 16) launch_row<T, 16>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
-  else if (passes <= 20) launch_row<T, 20>(g, st, logits, N, V, nn, wc, am, mx, R, lse);
+                         static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
+  } else if (passes <= 1) launch_row<T, 1>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 2) launch_row<T, 2>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 4) launch_row<T, 4>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 8) launch_row<T, 8>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 12) launch_row<T, 12>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 16) launch_row<T, 16>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
+  else if (passes <= 20) launch_row<T, 20>(g, st, logits, N, V, nn, wc, am, mx, R, Rb, lse);
   else if (lse)
     hipLaunchKernelGGL((row2_kernel<T, true>), g, dim3(kRowThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
   else
     hipLaunchKernelGGL((row2_kernel<T, false>), g, dim3(kRowThreads), 0, st,
-                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, lse);
+                       static_cast<const T*>(logits), N, V, nn, wc, am, mx, R, Rb, lse);
 }
 
 // Greedy workspace: [rows * S] uint64 slice keys, then [rows * S] float2
@@ -505,7 +558,8 @@ extern "C" size_t ddtree_vocab_reduce_workspace_size(int32_t B, int32_t N, int32
 extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_t B,
                                              int32_t N, int32_t V, const int32_t* num_nodes,
                                              float temperature, int32_t* argmax, float* maxv,
-                                             uint64_t* R, float* lse, void* workspace,
+                                             uint64_t* R, uint64_t* R_blocks, float* lse,
+                                             void* workspace,
                                              size_t workspace_bytes, hipStream_t stream) {
   using namespace ddt;
   if (!logits || !num_nodes || !argmax || !maxv)
@@ -519,11 +573,16 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
   const int rows = B * N;
   if (temperature > 0.0f) {
     if (!R) return fail(DDTREE_EINVAL, "ddtree_vocab_reduce: R is required when temperature > 0");
+    if (V > kMaxRowBlocks * DDTREE_R_BLOCK)
+      return fail(DDTREE_EUNSUPPORTED, "ddtree_vocab_reduce: V = %d exceeds %d for sampling", V,
+                  kMaxRowBlocks * DDTREE_R_BLOCK);
     const WeightConsts wc = weight_consts(temperature);
     if (dtype == DDTREE_BF16)
-      launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, lse);
+      launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R,
+                                R_blocks, lse);
     else
-      launch_sampling<float>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, lse);
+      launch_sampling<float>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, R_blocks,
+                             lse);
     return check_launch("ddtree_vocab_reduce");
   }
   int S, chunk;
