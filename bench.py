@@ -2,8 +2,11 @@
 
 One step = ddtree_build -> ddtree_tree_attention -> ddtree_vocab_reduce ->
 ddtree_verify_greedy (or ddtree_verify_sample when the workload samples), then
-a device-to-host copy of accept_len and bonus and a stream synchronisation
-(the serving loop's per-step sync).  By default each step is a captured HIP
+accept_len and bonus reaching the host and a stream synchronisation (the
+serving loop's per-step sync).  By default the walk kernel stores the two
+results straight into pinned host memory and the host busy-polls for the
+synchronisation; --result-copy adds an explicit device-to-host copy instead,
+--host-wait auto sleeps until signalled.  By default each step is a captured HIP
 graph replayed once per step (--eager launches every call from Python).  Inputs are seeded synthetic tensors of
 the workload's shapes, resident in HBM before timing starts; several copies
 of the input set are rotated so that consecutive steps do not find their
@@ -53,7 +56,22 @@ def attention_flops(cfg, total_ctx):
     return 4.0 * cfg.N * total_ctx * cfg.Hq * cfg.Dh
 
 
-def run_gpu(cfg, steps, warmup, rotate, graph=True):
+def set_host_wait(mode):
+    """Before the HIP runtime starts: 'spin' makes host waits on the device (the
+    per-step stream synchronisation) busy-poll instead of sleeping until an
+    interrupt, the usual setting of a latency-bound serving loop.  Returns the
+    mode in effect."""
+    if mode != "spin":
+        return "auto"
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        return "spin" if hip.hipSetDeviceFlags(ctypes.c_uint(1)) == 0 else "auto"
+    except OSError:
+        return "auto"
+
+
+def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     import torch
     import tree_verification_build_amd as lib
     import workloads
@@ -82,8 +100,13 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
 
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(rotate - 1)]
     tree = lib.alloc_tree(cfg.B, cfg.budget, cfg.D, cfg.K, dev)
-    # accept_len and bonus side by side, so that one copy brings both to the host
-    result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
+    # accept_len and bonus land in pinned host memory, written by the walk
+    # kernel itself (the device-to-host transfer is its stores); with
+    # --result-copy they stay on the device and one copy per step brings them over
+    if result_copy:
+        result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
+    else:
+        result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
     outputs = {"accept_len": result[0],
                "path_nodes": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
                "out_tokens": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
@@ -94,7 +117,8 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
         device=dev)
     ws_v = torch.empty(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
                        dtype=torch.uint8, device=dev)
-    host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
+    host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True) if result_copy \
+        else result
     stream = torch.cuda.current_stream()
     T = cfg.temperature
 
@@ -117,7 +141,8 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True):
                                      small["uniforms"], outputs=outputs)
         else:
             lib.ddtree_verify_greedy(tree, v["argmax"], outputs=outputs)
-        host_result.copy_(result, non_blocking=True)
+        if result_copy:
+            host_result.copy_(result, non_blocking=True)
 
     for i in range(warmup):
         step(i)
@@ -270,6 +295,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
+    ap.add_argument("--host-wait", choices=("spin", "auto"), default="spin",
+                    help="how the host waits for each step: busy-poll (spin) or the runtime's "
+                         "default sleep-until-signalled (auto)")
+    ap.add_argument("--result-copy", action="store_true",
+                    help="keep accept_len/bonus in device memory and copy them to the host "
+                         "each step (default: the walk writes them to pinned host memory)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter scaling) and print it")
     args = ap.parse_args()
@@ -280,12 +311,14 @@ def main():
         print("bench.py measures one GPU only: the verify path here is built and timed on a "
               "single MI355X (no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    host_wait = set_host_wait(args.host_wait)
     import workloads
     cfg = workloads.config(args.config)
     offs = np.concatenate([[0], np.cumsum(workloads.ctx_lengths(cfg))])
     ab = algorithmic_bytes(cfg, int(offs[-1]))
     rotate = args.rotate or int(max(1, min(32, np.ceil(2 ** 30 / ab["total"]))))
-    r = run_gpu(cfg, args.steps, args.warmup, rotate, graph=not args.eager)
+    r = run_gpu(cfg, args.steps, args.warmup, rotate, graph=not args.eager,
+                result_copy=args.result_copy)
     steps_s = args.steps / r["t_sync"]
     attn_gbs = ab["attention"] / (r["attn_ms"] * 1e-3) / 1e9
     vocab_gbs = ab["vocab"] / (r["vocab_ms"] * 1e-3) / 1e9
@@ -308,7 +341,8 @@ def main():
                    "heads_q": cfg.Hq, "heads_kv": cfg.Hkv, "head_dim": cfg.Dh, "depth": cfg.D,
                    "budget": cfg.budget, "topk_cap": cfg.K, "vocab": cfg.V,
                    "temperature": cfg.temperature, "input_sets_rotated": rotate,
-                   "launch": "eager" if args.eager else "hip_graph"},
+                   "launch": "eager" if args.eager else "hip_graph", "host_wait": host_wait,
+                   "result_to_host": "copy" if args.result_copy else "pinned_store"},
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(cfg.name), "kernel": "ddtree_tree_attention",

@@ -18,8 +18,10 @@
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
  *
  * Conventions shared by every call
- *   - Every data pointer is DEVICE memory owned by the caller (unless named
- *     *_host).  The library allocates nothing and keeps no state between
+ *   - Every data pointer is device-accessible memory owned by the caller
+ *     (unless named *_host): device memory, or pinned host memory mapped for
+ *     the device (e.g. the walks' accept_len / bonus, which the host reads
+ *     every step).  The library allocates nothing and keeps no state between
  *     calls; workspaces are passed in and sized by the *_workspace_size calls.
  *   - Every call enqueues its kernels on `stream` and returns without waiting.
  *   - The returned status covers argument validation (done on the host before
