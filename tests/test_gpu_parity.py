@@ -175,3 +175,35 @@ def test_attention_split_size_invariance(monkeypatch):
         d = (o.float() - base.float()).abs().max().item()
         assert d <= 2e-2 * base.float().abs().max().item(), (sk, d)
     monkeypatch.delenv("DDTREE_ATTN_SPLIT_KEYS")
+
+
+@pytest.mark.parametrize("name", ["bf16_gqa", "batched"])
+def test_walk_outputs_in_pinned_host_memory(name):
+    """The walks' outputs may live in pinned host memory (what a serving loop
+    reads each step): same results as device outputs, visible after a sync."""
+    import tree_verification_build_amd as lib
+    c = case(name)
+    say("pinned walk outputs", name)
+    t = c.gpu_tree()
+    T = c.cfg.temperature
+    v = lib.ddtree_vocab_reduce(c.d("logits"), t.num_nodes, T)
+
+    def outputs(pinned):
+        kw = dict(dtype=torch.int32, pin_memory=True) if pinned else \
+            dict(dtype=torch.int32, device="cuda:0")
+        B, D = c.cfg.B, c.cfg.D
+        return {"accept_len": torch.full((B,), -7, **kw), "bonus": torch.full((B,), -7, **kw),
+                "path_nodes": torch.full((B, D + 1), -7, **kw),
+                "out_tokens": torch.full((B, D + 1), -7, **kw)}
+    res = []
+    for pinned in (False, True):
+        o = outputs(pinned)
+        if T > 0:
+            lib.ddtree_verify_sample(t, c.d("logits"), v["maxv"], v["R"], v["R_blocks"], T,
+                                     c.d("uniforms"), outputs=o)
+        else:
+            lib.ddtree_verify_greedy(t, v["argmax"], outputs=o)
+        torch.cuda.synchronize()
+        res.append({k: x.cpu().numpy().copy() for k, x in o.items()})
+    for k in res[0]:
+        assert np.array_equal(res[0][k], res[1][k]), k
