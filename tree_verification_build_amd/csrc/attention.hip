@@ -61,7 +61,8 @@ struct AttnArgs {
   int split_keys;
   void* out;
   float* lse;
-  float* ws_o;        // [total_splits * Hkv, M, Dh] unnormalised partial outputs
+  void* ws_o;         // [total_splits * Hkv, M, Dh] unnormalised partial outputs
+                      // (bf16 from the DMA kernel, fp32 from the register kernel)
   float2* ws_ml;      // [total_splits * Hkv, M] (running max in log2 units, sum)
   // split plan for B <= kTabMax (tab_n = B, else 0): request b owns splits
   // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b+1])
@@ -427,7 +428,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
           valid ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
   } else {
     const long pr = (static_cast<long>(sid) * a.Hkv + kvh) * a.M + r;
-    float* dst = a.ws_o + pr * DH;
+    float* dst = static_cast<float*>(a.ws_o) + pr * DH;
 #pragma unroll
     for (int db = 0; db < DH / 16; ++db)
       *reinterpret_cast<float4*>(dst + db * 16 + 4 * g) =
@@ -702,22 +703,38 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       a.lse[(static_cast<long>(b) * a.N + node) * a.Hq + head] =
           valid ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_huge_valf();
   } else {
+    // bf16 partials: half the round trip of fp32 ones; the combine's result
+    // is rounded to bf16 anyway.
     const long pr = (static_cast<long>(sid) * a.Hkv + kvh) * a.M + r;
-    float* dst = a.ws_o + pr * DH;
+    uint16_t* dst = static_cast<uint16_t*>(a.ws_o) + pr * DH;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      *reinterpret_cast<float4*>(dst + db * 16 + 4 * g) =
-          make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+    for (int db = 0; db < DB; ++db) PolicyBF16<DH>::store_out(dst + db * 16 + 4 * g, o[db]);
     if (g == 0) a.ws_ml[pr] = make_float2(m_run, l_tot);
   }
 }
 
 // ------------------------------------------------------------------ combine
-// One workgroup per (request, KV head, query row): the four waves each take a
-// quarter of the splits (lanes over splits for the running maxima, then every
-// lane over Dh/64 output dims with unrolled loads); the four partial sums meet
-// in LDS.
-template <typename elem, int DH>
+// One workgroup per (request, KV head, query row). Wave w takes splits
+// w, w + 4, w + 8, ...; it issues the loads of up to kCombU of them at once
+// (every lane reads the split's (max, sum) pair and Dh/64 output dims), so a
+// request with up to 4·kCombU splits costs one round trip to memory. The
+// four waves' (max, sum, acc) meet in LDS.
+constexpr int kCombU = 8;
+
+template <typename PT, int PER>
+__device__ __forceinline__ void load_partial(const PT* src, float (&v)[PER]) {
+  if constexpr (sizeof(PT) == 2) {
+    static_assert(PER == 2, "bf16 partials: two dims per lane");
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(src);
+    v[0] = __uint_as_float(w << 16);
+    v[1] = __uint_as_float(w & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) v[k] = src[k];
+  }
+}
+
+template <typename elem, typename PT, int DH>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int PER = DH / 64;                // output dims per lane
   __shared__ float s_m[4], s_l[4];
@@ -725,17 +742,23 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int b = blockIdx.x / a.Hkv, kvh = blockIdx.x % a.Hkv;
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int SK = a.split_keys;
-  auto nsplits = [&](int bb) {
-    const int L = a.ctx_offsets[bb + 1] - a.ctx_offsets[bb];
-    return L > 0 ? (L + SK - 1) / SK : 1;
-  };
-  const int ns = nsplits(b);
-  if (ns == 1) return;
-  int start = 0;
-  for (int bb = lane; bb < b; bb += 64) start += nsplits(bb);
+  int start, ns;
+  if (a.tab_n > 0) {
+    start = a.tab_split0[b];
+    ns = a.tab_split0[b + 1] - start;
+  } else {
+    const int SK = a.split_keys;
+    auto nsplits = [&](int bb) {
+      const int L = a.ctx_offsets[bb + 1] - a.ctx_offsets[bb];
+      return L > 0 ? (L + SK - 1) / SK : 1;
+    };
+    ns = nsplits(b);
+    start = 0;
+    for (int bb = lane; bb < b; bb += 64) start += nsplits(bb);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) start += __shfl_xor(start, o, 64);
+    for (int o = 32; o >= 1; o >>= 1) start += __shfl_xor(start, o, 64);
+  }
+  if (ns == 1) return;
   const int node = r / a.G, head = kvh * a.G + r % a.G;
   const long orow = (static_cast<long>(b) * a.N + node) * a.Hq + head;
   elem* dst = static_cast<elem*>(a.out) + orow * DH;
@@ -751,28 +774,41 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   }
   const long pr0 = static_cast<long>(start) * a.Hkv + kvh;
   auto prow = [&](int sp) { return (pr0 + static_cast<long>(sp) * a.Hkv) * a.M + r; };
-  // this wave's splits: wave, wave + 4, ...
-  float mw = kNegBig;
-  for (int sp = wave + 4 * lane; sp < ns; sp += 256) mw = max(mw, a.ws_ml[prow(sp)].x);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mw = max(mw, shfl_xor_f32(mw, o));
-  float lw = 0.f;
-  for (int sp = wave + 4 * lane; sp < ns; sp += 256) {
-    const float2 ml = a.ws_ml[prow(sp)];
-    lw += __builtin_amdgcn_exp2f(ml.x - mw) * ml.y;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lw += shfl_xor_f32(lw, o);
-  float acc[PER];
+  const PT* ws = static_cast<const PT*>(a.ws_o);
+  float mw = kNegBig, lw = 0.f, acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-#pragma unroll 4
-  for (int sp = wave; sp < ns; sp += 4) {
-    const long pr = prow(sp);
-    const float w = __builtin_amdgcn_exp2f(a.ws_ml[pr].x - mw);
-    const float* src = a.ws_o + pr * DH + lane * PER;
+  for (int sp0 = wave; sp0 < ns; sp0 += 4 * kCombU) {
+    float2 ml[kCombU];
+    float v[kCombU][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] += w * src[k];
+    for (int u = 0; u < kCombU; ++u) {
+      const int sp = sp0 + 4 * u;
+      if (sp < ns) {
+        const long pr = prow(sp);
+        ml[u] = a.ws_ml[pr];
+        load_partial<PT, PER>(ws + pr * DH + lane * PER, v[u]);
+      } else {
+        ml[u] = make_float2(kNegBig, 0.f);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[u][k] = 0.f;
+      }
+    }
+    float mc = mw;
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) mc = max(mc, ml[u].x);
+    const float fr = __builtin_amdgcn_exp2f(mw - mc);
+    lw *= fr;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) acc[k] *= fr;
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+      const float w = __builtin_amdgcn_exp2f(ml[u].x - mc);
+      lw += w * ml[u].y;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) acc[k] += w * v[u][k];
+    }
+    mw = mc;
   }
   if (lane == 0) {
     s_m[wave] = mw;
@@ -987,7 +1023,7 @@ extern "C" ddtree_status ddtree_tree_attention(
     if (!workspace || workspace_bytes < need + need_ml || !aligned16(workspace))
       return fail(DDTREE_EINVAL, "ddtree_tree_attention: workspace of %zu bytes needed, got %zu",
                   need + need_ml, workspace_bytes);
-    a.ws_o = static_cast<float*>(workspace);
+    a.ws_o = workspace;
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + need);
   }
   if (dtype == DDTREE_BF16) {
@@ -1000,11 +1036,12 @@ extern "C" ddtree_status ddtree_tree_attention(
   if (multi) {
     const dim3 g(B * Hkv, M);
     if (dtype == DDTREE_BF16) {
-      if (Dh == 128) hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), g, dim3(256), 0, stream, a);
+      if (Dh == 128)
+        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t, 128>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((combine_kernel<uint16_t, float, 64>), g, dim3(256), 0, stream, a);
     } else {
-      if (Dh == 128) hipLaunchKernelGGL((combine_kernel<float, 128>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((combine_kernel<float, 64>), g, dim3(256), 0, stream, a);
+      if (Dh == 128) hipLaunchKernelGGL((combine_kernel<float, float, 128>), g, dim3(256), 0, stream, a);
+      else hipLaunchKernelGGL((combine_kernel<float, float, 64>), g, dim3(256), 0, stream, a);
     }
   }
   return check_launch("ddtree_tree_attention");
