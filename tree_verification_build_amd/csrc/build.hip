@@ -19,12 +19,15 @@
 // rank-0 child, the previous sibling otherwise).  A step takes the slot with
 // the largest key (a DPP maximum of the high words; the low words only break
 // score ties), records it as node i, and writes two keys: node i's best child
-// into slot i and the parent's next child into slot parent (0 for "none").
-// The step is a serial chain of ~85 instructions in one wave, so the loop
-// does nothing else: tokens, positions, child / sibling links and visibility
-// rows are rebuilt afterwards, all lanes in parallel (visibility by pointer
-// jumping over parent links).  The draft top-k table (D*K <= 256 entries) is
-// spread over the lanes and read with v_readlane.
+// into slot i and the parent's next child into slot parent.  The scores of
+// those two offers are computed beforehand by every lane for its own slot,
+// alongside the maximum, so the step's dependent chain after the maximum is
+// three lane reads and a few lane writes (~70 instructions per step in all).
+// Offers that do not exist score -inf through padding of the log-prob table
+// and are never taken: the loop runs exactly as many steps as the tree can
+// hold nodes.  Tokens, positions, child / sibling links and visibility rows
+// are rebuilt afterwards, all lanes in parallel (visibility by pointer
+// jumping over parent links).
 #include "common.hpp"
 
 namespace ddt {
@@ -36,16 +39,6 @@ __device__ __forceinline__ uint64_t make_key_bits(uint32_t ord_score, int parent
                       (static_cast<uint32_t>(255 - rank) << 16) |
                       (static_cast<uint32_t>(depth) << 8) | static_cast<uint32_t>(pusher);
   return (static_cast<uint64_t>(ord_score) << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t make_key(float score, int parent, int rank, int depth,
-                                             int pusher) {
-  return make_key_bits(ord_f32(score), parent, rank, depth, pusher);
-}
-
-// fp32 bits of the value an order-preserving key word encodes
-__device__ __forceinline__ uint32_t unord_f32_bits(uint32_t o) {
-  return (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
 }
 
 // order-preserving bits of fp32 bits (-0 as +0), as plain integer operations
@@ -91,6 +84,26 @@ __device__ __forceinline__ uint32_t table_gather(const uint32_t (&r)[4], int idx
   return v;
 }
 
+constexpr int kRow = 128;   // LDS row stride of the log-prob table (> DDTREE_MAX_TOPK)
+
+}  // namespace
+}  // namespace ddt
+
+// v_writelane_b32 (write one lane of a VGPR from a scalar), reached through
+// its LLVM intrinsic so that the compiler still handles its hazards
+extern "C" __device__ int ddt_writelane_i32(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+namespace ddt {
+namespace {
+
+__device__ __forceinline__ uint32_t put_lane(uint32_t old, uint32_t val, int lane) {
+  return static_cast<uint32_t>(ddt_writelane_i32(static_cast<int>(val), lane, static_cast<int>(old)));
+}
+__device__ __forceinline__ float put_lane(float old, float val, int lane) {
+  return __builtin_bit_cast(float, ddt_writelane_i32(__builtin_bit_cast(int, val), lane,
+                                                     __builtin_bit_cast(int, old)));
+}
+
 template <int REGS, bool TWO>
 __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ draft_lp,
                                                    const int32_t* __restrict__ draft_tok,
@@ -98,6 +111,7 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
                                                    const int32_t* __restrict__ prefix_len,
                                                    int D, int K, int budget, ddtree_tree t) {
   __shared__ int32_t s_fc[DDTREE_MAX_NODES], s_ns[DDTREE_MAX_NODES];
+  extern __shared__ float s_table[];   // (D + 2) * kRow floats
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const int N = budget + 1;
@@ -117,67 +131,124 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
     s_ns[lane + 64] = -1;
   }
 
-  // records: the taken key of node i sits in lane i % 64 of (rh0, rl0) or (rh1, rl1);
-  // the root's record carries score +0.0 (its other fields are never read)
-  uint32_t rh0 = lane == 0 ? ord_f32(0.0f) : 0u, rl0 = 0u, rh1 = 0u, rl1 = 0u;
-  // frontier slots: every taken node p has at most one pending offer, its
-  // next child not yet taken, and that offer sits in slot p (lane p % 64 of
-  // (sh0, sl0) or (sh1, sl1)); key 0 = none.  The root's first child starts
-  // in slot 0.
-  const uint64_t first = make_key(0.0f + __uint_as_float(table_at<REGS>(lp_r, 0)), 0, 0, 1, 0);
-  uint32_t sh0 = lane == 0 ? static_cast<uint32_t>(first >> 32) : 0u;
-  uint32_t sl0 = lane == 0 ? static_cast<uint32_t>(first) : 0u;
-  uint32_t sh1 = 0u, sl1 = 0u;
+  // The log-prob table in LDS with a fixed row stride: row d - 1 holds depth
+  // d, ranks 0..K-1, then -inf up to kRow; rows D and D + 1 (depths D + 1,
+  // D + 2: children of depth-D nodes and their offers) are all -inf.
+  // An offer that does not exist (a child below depth D, a sibling past rank
+  // K - 1) then simply scores -inf, which no real offer ties or trails, and
+  // the loop stops after the last real node, so such offers are never taken.
+  float* s_T = s_table;
+#pragma unroll 1
+  for (int e = lane; e < (D + 2) * kRow; e += 64) s_T[e] = -__builtin_huge_valf();
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < REGS; ++w) {
+    const int e = w * 64 + lane;
+    if (e < DK) s_T[(e / K) * kRow + e % K] = __uint_as_float(lp_r[w]);
+  }
+  __syncthreads();
 
-  int count = 1;
-  for (; count < N; ++count) {
-    // the best slot: largest key; the high word (score) decides unless tied
-    uint32_t mh = sh0, ml = sl0;
-    if (TWO) {
-      const bool in1 = ((static_cast<uint64_t>(sh1) << 32) | sl1) > ((static_cast<uint64_t>(sh0) << 32) | sl0);
-      mh = in1 ? sh1 : sh0;
-      ml = in1 ? sl1 : sl0;
-    }
-    const uint32_t bh = wave_max_bcast_u32(mh);
-    if (bh == 0) break;  // no offers left
-    const uint64_t tied = __ballot(mh == bh);
-    int w = __builtin_ctzll(tied);
-    if (tied & (tied - 1)) w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32(mh == bh ? ml : 0u)));
-    // readlane yields a signed int: cast before widening, or the low word sign-extends
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(ml, w));
-    const int parent = 255 - static_cast<int>(lo >> 24);
-    const int rank = 255 - static_cast<int>((lo >> 16) & 0xFF);
-    const int depth = static_cast<int>((lo >> 8) & 0xFF);
-    const int i = count;
-    const uint32_t pscore = unord_f32_bits(static_cast<uint32_t>(
-        __builtin_amdgcn_readlane(TWO && parent >= 64 ? rh1 : rh0, parent & 63)));
-    // record node i (branch-free: lane i of the low registers or lane i - 64
-    // of the high ones)
-    const bool at_i0 = lane == i, at_i1 = TWO && lane + 64 == i;
-    const bool at_p0 = lane == parent, at_p1 = TWO && lane + 64 == parent;
-    rh0 = at_i0 ? bh : rh0;
-    rl0 = at_i0 ? lo : rl0;
-    if (TWO) {
-      rh1 = at_i1 ? bh : rh1;
-      rl1 = at_i1 ? lo : rl1;
-    }
-    // offers: node i's best child goes to slot i, the parent's next child
-    // replaces the taken one in slot parent (key 0 when there is none)
-    const float lpc = __uint_as_float(table_at<REGS>(lp_r, min(depth, D - 1) * K));
-    const float lps = __uint_as_float(table_at<REGS>(lp_r, (depth - 1) * K + min(rank + 1, K - 1)));
-    const uint32_t cs = __float_as_uint(__uint_as_float(unord_f32_bits(bh)) + lpc);
-    const uint32_t ss = __float_as_uint(__uint_as_float(pscore) + lps);
-    const uint64_t kc = depth < D ? make_key_bits(ord_bits(cs), i, 0, depth + 1, i) : 0ull;
-    const uint64_t ks = rank + 1 < K ? make_key_bits(ord_bits(ss), parent, rank + 1, depth, i) : 0ull;
-    const uint32_t kch = static_cast<uint32_t>(kc >> 32), kcl = static_cast<uint32_t>(kc);
-    const uint32_t ksh = static_cast<uint32_t>(ks >> 32), ksl = static_cast<uint32_t>(ks);
-    sh0 = at_i0 ? kch : at_p0 ? ksh : sh0;
-    sl0 = at_i0 ? kcl : at_p0 ? ksl : sl0;
-    if (TWO) {
-      sh1 = at_i1 ? kch : at_p1 ? ksh : sh1;
-      sl1 = at_i1 ? kcl : at_p1 ? ksl : sl1;
+  // Per lane, for set 0 (nodes / slots 0..63) and set 1 (64..127):
+  //   records of taken nodes: rh = key high word (order-preserving score
+  //     bits), rl = key low word, rs = score;
+  //   frontier slots: every taken node p has at most one pending offer, its
+  //     next child not yet taken, kept in slot p: kh / kl = key words,
+  //     ks = its score (slots of nodes not taken yet are never read).
+  // The root (node 0, score +0.0) offers its rank-0 child in slot 0.
+  const float root_child = 0.0f + s_T[0];
+  uint32_t rh0 = lane == 0 ? ord_f32(0.0f) : 0u, rl0 = 0u, rh1 = 0u, rl1 = 0u;
+  float rs0 = 0.0f, rs1 = 0.0f;
+  uint32_t kh0 = ord_f32(root_child);
+  uint32_t kl0 = static_cast<uint32_t>(make_key_bits(0u, 0, 0, 1, 0));
+  float ks0 = root_child;
+  uint32_t kh1 = 0u, kl1 = 0u;
+  float ks1 = 0.0f;
+  if (lane != 0) kh0 = 0u, kl0 = 0u;
+
+  // nodes the tree can hold: 1 + K + K^2 + ... + K^D, at most N; until that
+  // many are taken the best offer is a real one
+  int total = 1;
+  {
+    int pw = 1;
+    for (int d = 1; d <= D && total < N; ++d) {
+      pw = min(pw * K, N);
+      total = min(total + pw, N);
     }
   }
+
+  // What taking a slot's offer (parent p, rank r, depth d, score s) would
+  // offer next: its own rank-0 child, score s + lp(d + 1, 0), and p's next
+  // child, score score(p) + lp(d, r + 1).  Every lane computes both for its
+  // own slot; this does not depend on the step's maximum, so it fills the
+  // gaps of the maximum's dependent chain, and after the maximum a step only
+  // reads the winning lane.
+  auto offers = [&](uint32_t kl, float ks, float rs, float& cs, float& ss) {
+    const int d = static_cast<int>((kl >> 8) & 0xFF);          // the offer's depth
+    const int r1 = 256 - static_cast<int>((kl >> 16) & 0xFF);  // its rank + 1
+    cs = ks + s_T[d * kRow];
+    ss = rs + s_T[(d - 1) * kRow + r1];
+  };
+
+  for (int i = 1; i < total; ++i) {
+    float cs0, ss0, cs1 = 0.0f, ss1 = 0.0f;
+    offers(kl0, ks0, rs0, cs0, ss0);
+    if (TWO) offers(kl1, ks1, rs1, cs1, ss1);
+    // the best slot: largest key; the high word (score) decides unless tied
+    uint32_t mh = kh0, ml = kl0;
+    float mcs = cs0, mss = ss0, mks = ks0;
+    bool in1 = false;
+    if (TWO) {
+      in1 = ((static_cast<uint64_t>(kh1) << 32) | kl1) > ((static_cast<uint64_t>(kh0) << 32) | kl0);
+      mh = in1 ? kh1 : kh0;
+      ml = in1 ? kl1 : kl0;
+      mcs = in1 ? cs1 : cs0;
+      mss = in1 ? ss1 : ss0;
+      mks = in1 ? ks1 : ks0;
+    }
+    const uint32_t bh = wave_max_bcast_u32(mh);
+    const uint64_t tied = __ballot(mh == bh);
+    int w = __builtin_ctzll(tied);
+    if (__builtin_expect(__builtin_popcountll(tied) > 1, 0))
+      w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32(mh == bh ? ml : 0u)));
+    // readlane yields a signed int: cast before widening, or the low word sign-extends
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(ml, w));
+    const float cs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mcs), w));
+    const float ss = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mss), w));
+    const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mks), w));
+    const int parent = TWO ? w + 64 * (__builtin_amdgcn_readlane(in1 ? 1 : 0, w) & 1) : w;
+    const int depth = static_cast<int>((lo >> 8) & 0xFF);
+    // node i = the taken offer; slot i gets node i's best child, slot parent
+    // the parent's next child
+    const uint32_t lo_c = static_cast<uint32_t>(make_key_bits(0u, i, 0, depth + 1, i));
+    const uint32_t lo_s = ((lo & 0xFFFFFF00u) - 0x10000u) | static_cast<uint32_t>(i);
+    const uint32_t ch = ord_f32(cs), sh = ord_f32(ss);
+    const int il = i & 63, pl = parent & 63;
+    if (!TWO || i < 64) {
+      rh0 = put_lane(rh0, bh, il);
+      rl0 = put_lane(rl0, lo, il);
+      rs0 = put_lane(rs0, sc, il);
+      kh0 = put_lane(kh0, ch, il);
+      kl0 = put_lane(kl0, lo_c, il);
+      ks0 = put_lane(ks0, cs, il);
+    } else {
+      rh1 = put_lane(rh1, bh, il);
+      rl1 = put_lane(rl1, lo, il);
+      rs1 = put_lane(rs1, sc, il);
+      kh1 = put_lane(kh1, ch, il);
+      kl1 = put_lane(kl1, lo_c, il);
+      ks1 = put_lane(ks1, cs, il);
+    }
+    if (!TWO || parent < 64) {
+      kh0 = put_lane(kh0, sh, pl);
+      kl0 = put_lane(kl0, lo_s, pl);
+      ks0 = put_lane(ks0, ss, pl);
+    } else {
+      kh1 = put_lane(kh1, sh, pl);
+      kl1 = put_lane(kl1, lo_s, pl);
+      ks1 = put_lane(ks1, ss, pl);
+    }
+  }
+  const int count = total;
 
   // rebuild the node arrays from the records, every lane in parallel
   const long base = static_cast<long>(b) * N;
@@ -295,17 +366,18 @@ extern "C" ddtree_status ddtree_build(const float* draft_lp, const int32_t* draf
     return fail(DDTREE_EUNSUPPORTED, "ddtree_build: depth * top-k = %d exceeds 256", D * K);
   const bool small_table = D * K <= 64, one_list = budget + 1 <= 64;
   const dim3 g(B), blk(kWave);
+  const size_t lds = static_cast<size_t>(D + 2) * kRow * sizeof(float);
   if (small_table && one_list)
-    hipLaunchKernelGGL((build_kernel<1, false>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+    hipLaunchKernelGGL((build_kernel<1, false>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
                        prefix_len, D, K, budget, *tree);
   else if (small_table)
-    hipLaunchKernelGGL((build_kernel<1, true>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+    hipLaunchKernelGGL((build_kernel<1, true>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
                        prefix_len, D, K, budget, *tree);
   else if (one_list)
-    hipLaunchKernelGGL((build_kernel<4, false>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+    hipLaunchKernelGGL((build_kernel<4, false>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
                        prefix_len, D, K, budget, *tree);
   else
-    hipLaunchKernelGGL((build_kernel<4, true>), g, blk, 0, stream, draft_lp, draft_tok, root_tok,
+    hipLaunchKernelGGL((build_kernel<4, true>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
                        prefix_len, D, K, budget, *tree);
   return check_launch("ddtree_build");
 }
