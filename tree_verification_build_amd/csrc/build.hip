@@ -41,24 +41,6 @@ __device__ __forceinline__ uint64_t make_key_bits(uint32_t ord_score, int parent
   return (static_cast<uint64_t>(ord_score) << 32) | lo;
 }
 
-// order-preserving bits of fp32 bits (-0 as +0), as plain integer operations
-__device__ __forceinline__ uint32_t ord_bits(uint32_t u) {
-  u = u == 0x80000000u ? 0u : u;
-  const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
-  return u ^ (m | 0x80000000u);
-}
-
-// value of a per-lane register table at flat index idx (uniform): one readlane
-// when the table fits one register (D*K <= 64), else a scalar select of four
-template <int REGS>
-__device__ __forceinline__ uint32_t table_at(const uint32_t (&r)[4], int idx) {
-  if (REGS == 1) return __builtin_amdgcn_readlane(r[0], idx);
-  const int w = idx >> 6, l = idx & 63;
-  const uint32_t a0 = __builtin_amdgcn_readlane(r[0], l), a1 = __builtin_amdgcn_readlane(r[1], l);
-  const uint32_t a2 = __builtin_amdgcn_readlane(r[2], l), a3 = __builtin_amdgcn_readlane(r[3], l);
-  return w == 0 ? a0 : w == 1 ? a1 : w == 2 ? a2 : a3;
-}
-
 // Maximum over the wavefront with DPP: within each row of 16 lanes (quad_perm
 // swaps, row_ror 4 and 8), then row_bcast15 / row_bcast31 carry the running
 // maximum into the last row; lane 63 ends with the total.
