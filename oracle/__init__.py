@@ -1,11 +1,14 @@
 """CPU oracle for the DDTree tree-verify step -- TEST INFRASTRUCTURE ONLY.
 
 Plain, slow, obviously-correct NumPy/Python implementations of the four
-steps of the verify path.  Only the test suite, the smoke check and the
+steps of the verify path and of the draft top-K that feeds it.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package; the product path (the
 HIP library and its Python binding) never does, and shares no code with it.
 
 Sources (blog pages on DDTree speculative decoding):
+  * topk    -- "The Architecture of Speculative Decoding: Dissecting DDTree's
+               Tree-Parallel Evaluation Strategy", Section 1 step 1 (per-depth
+               top-k log-probs of the draft head).
   * build   -- "The Architecture of Speculative Decoding: Dissecting DDTree's
                Tree-Parallel Evaluation Strategy", Section 1 (five-step flow,
                steps 2-3); "The Tree That Couldn't Branch", "Context: The Road
@@ -24,10 +27,11 @@ Parity status: every function here is pinned by tests under tests/ that check
 it against brute force, closed forms, library routines or a statistical test
 (see the test modules' docstrings); none is "parity unpinned".
 """
+from .topk import draft_topk, log_sum_exp
 from .build import build_tree, N_WORDS
 from .attention import tree_attention, to_f64
 from .vocab import vocab_reduce, weight_constants, weights
 from .verify import verify_greedy, verify_sample
 
-__all__ = ["build_tree", "N_WORDS", "tree_attention", "to_f64", "vocab_reduce",
-           "weight_constants", "weights", "verify_greedy", "verify_sample"]
+__all__ = ["draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
+           "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample"]
