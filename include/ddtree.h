@@ -8,6 +8,8 @@
  * Contexts Once"; "Implementing Temperature-Aware Tree Sampling for DDTree",
  * "Path B"; "The Tree That Couldn't Branch", "Hypothesis 3" and "Hypothesis 4"):
  *
+ *   ddtree_draft_topk      draft logits  ->  per-depth top-k tokens and their
+ *                          full-vocabulary log-probs (the input of the build)
  *   ddtree_build           per-depth draft top-k  ->  best-first token tree
  *   ddtree_tree_attention  every tree node attends to its request's context
  *                          (streamed from HBM once, shared by all nodes) and
@@ -81,6 +83,34 @@ typedef struct {
   int32_t* num_nodes;    /* [B] 1 + number of nodes taken (<= N) */
   int32_t B, N, D, K, W; /* W = (N + 63) / 64 */
 } ddtree_tree;
+
+/*
+ * ddtree_draft_topk -- per-depth top-k of the draft head.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1
+ * step 1 (from every depth position of the draft forward, the top-k candidate
+ * tokens and their log-probs, which step 2 turns into cumulative scores).
+ * Readings: the log-prob is the log-softmax of the whole row at temperature 1
+ * (not renormalised over the top-k); candidates are ordered by logit,
+ * descending, equal logits by lower token id.
+ *   logits     [rows, V] bf16 or fp32 (rows = requests x depths, any order;
+ *              typically the [B, D, V] draft outputs viewed as B*D rows)
+ *   K          1 <= K <= min(V, 64)
+ *   tokens     [rows, K] int32   rank-ordered token ids
+ *   logprobs   [rows, K] fp32    logit - log-sum-exp of the row (computed in
+ *              fp32: within ~1e-5 of the exact value for V = 163840)
+ *   workspace  ddtree_draft_topk_workspace_size(rows, V, K) bytes (may be 0),
+ *              16-byte aligned device scratch; contents need no
+ *              initialisation and are garbage afterwards (calls sharing it
+ *              must not overlap).
+ * The tokens are exact (pure comparisons of the given logits).
+ * Errors: DDTREE_EINVAL (null pointers, sizes, K out of range, dtype),
+ *         DDTREE_EUNSUPPORTED (rows > 65535).
+ */
+size_t ddtree_draft_topk_workspace_size(int32_t rows, int32_t V, int32_t K);
+
+ddtree_status ddtree_draft_topk(const void* logits, ddtree_dtype dtype, int32_t rows, int32_t V,
+                                int32_t K, int32_t* tokens, float* logprobs, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ddtree_build -- best-first tree from per-depth top-k draft log-probs.

@@ -69,6 +69,16 @@ def test_host_validation_rejects_bad_arguments():
     from tree_verification_build_amd._lib import lib
     fake = ctypes.c_void_p(16)
     t = _fake_tree()
+    # draft top-k
+    assert lib.ddtree_draft_topk(None, 0, 9, 1024, 2, fake, fake, None, 0, None) == 1
+    assert lib.ddtree_draft_topk(fake, 0, 9, 1024, 0, fake, fake, None, 0, None) == 1   # K < 1
+    assert lib.ddtree_draft_topk(fake, 0, 9, 1024, 65, fake, fake, None, 0, None) == 1  # K > 64
+    assert lib.ddtree_draft_topk(fake, 0, 9, 3, 4, fake, fake, None, 0, None) == 1      # K > V
+    assert lib.ddtree_draft_topk(fake, 5, 9, 1024, 2, fake, fake, None, 0, None) == 1   # dtype
+    assert lib.ddtree_draft_topk(fake, 0, 0, 1024, 2, fake, fake, None, 0, None) == 1   # rows
+    assert lib.ddtree_draft_topk(fake, 0, 70000, 1024, 2, fake, fake, None, 0, None) == 2
+    # split rows need their workspace
+    assert lib.ddtree_draft_topk(fake, 0, 9, 163840, 4, fake, fake, None, 0, None) == 1
     # ddtree_build
     assert lib.ddtree_build(None, fake, fake, fake, 1, 8, 2, 8, ctypes.byref(t), None) == 1
     assert lib.ddtree_build(fake, fake, fake, fake, 1, 8, 2, 200, ctypes.byref(t), None) == 1
@@ -121,3 +131,7 @@ def test_workspace_sizes_are_host_only_and_sane():
     assert t.ddtree_tree_attention_workspace_size(1, 9, 4, 4, 96, offs) == 0
     assert t.ddtree_vocab_reduce_workspace_size(1, 33, 163840) > 0
     assert t.ddtree_vocab_reduce_workspace_size(64, 33, 163840) == 0
+    # draft top-k: slices of 1024..8192 elements, K keys and one (max, sum) pair each
+    assert t.ddtree_draft_topk_workspace_size(9, 163840, 4) > 0
+    assert t.ddtree_draft_topk_workspace_size(9, 1024, 2) == 0
+    assert t.ddtree_draft_topk_workspace_size(9, 1024, 65) == 0

@@ -34,6 +34,9 @@ class _CTree(ctypes.Structure):
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _tp = ctypes.POINTER(_CTree)
+lib.ddtree_draft_topk_workspace_size.argtypes = [_i32, _i32, _i32]
+lib.ddtree_draft_topk_workspace_size.restype = _sz
+lib.ddtree_draft_topk.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 lib.ddtree_build.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _tp, _vp]
 lib.ddtree_tree_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp]
 lib.ddtree_tree_attention_workspace_size.restype = _sz
@@ -47,7 +50,7 @@ lib.ddtree_verify_greedy.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                      _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
-for _f in ("ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce", "ddtree_verify_greedy",
+for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce", "ddtree_verify_greedy",
            "ddtree_verify_sample", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.ddtree_last_error.restype = ctypes.c_char_p
@@ -126,6 +129,32 @@ class Tree:
 
 def alloc_tree(B, budget, D, K, device="cuda") -> Tree:
     return Tree(B, budget + 1, D, K, device)
+
+
+def ddtree_draft_topk_workspace_size(rows, V, K) -> int:
+    return int(lib.ddtree_draft_topk_workspace_size(rows, V, K))
+
+
+def ddtree_draft_topk(logits, K, tokens=None, logprobs=None, workspace=None, stream=None):
+    """Per-row top-K of draft logits [..., V] (bf16 or fp32): returns (tokens
+    [..., K] int32, log-probs [..., K] fp32)."""
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    lead, V = tuple(logits.shape[:-1]), int(logits.shape[-1])
+    rows = int(np.prod(lead)) if lead else 1
+    dev = logits.device
+    if tokens is None:
+        tokens = torch.empty((*lead, K), dtype=torch.int32, device=dev)
+    if logprobs is None:
+        logprobs = torch.empty((*lead, K), dtype=torch.float32, device=dev)
+    _dev(tokens, "tokens", torch.int32, (*lead, K))
+    _dev(logprobs, "logprobs", torch.float32, (*lead, K))
+    need = int(lib.ddtree_draft_topk_workspace_size(rows, V, K))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check(lib.ddtree_draft_topk(_ptr(logits), _dtype_code(logits), rows, V, K, _ptr(tokens),
+                                 _ptr(logprobs), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return tokens, logprobs
 
 
 def ddtree_build(draft_lp, draft_tok, root_tok, prefix_len, budget, tree=None, stream=None):
