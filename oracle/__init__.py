@@ -27,11 +27,11 @@ Parity status: every function here is pinned by tests under tests/ that check
 it against brute force, closed forms, library routines or a statistical test
 (see the test modules' docstrings); none is "parity unpinned".
 """
-from .topk import draft_topk, log_sum_exp
+from .topk import attach_draft_topk, draft_topk, log_sum_exp
 from .build import build_tree, N_WORDS
 from .attention import tree_attention, to_f64
 from .vocab import vocab_reduce, weight_constants, weights
 from .verify import verify_greedy, verify_sample
 
-__all__ = ["draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
+__all__ = ["attach_draft_topk", "draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
            "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample"]

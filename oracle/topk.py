@@ -49,3 +49,15 @@ def draft_topk(draft_logits, K: int):
     for r in range(flat.shape[0]):
         tok[r], lp[r] = topk_row(flat[r], K)
     return tok.reshape(*lead, K), lp.reshape(*lead, K)
+
+
+def attach_draft_topk(inputs: dict, D: int, K: int) -> dict:
+    """Adds the oracle's draft top-K of inputs["draft_logits"] [B, D+1, V]:
+    draft_tok_all [B, D+1, K] (every row; the target-logit planting reads its
+    ranking) and the tree build's inputs draft_tok, draft_lp [B, D, K] (rows
+    0..D-1).  Returns the same dict."""
+    tok, lp = draft_topk(inputs["draft_logits"], K)
+    inputs["draft_tok_all"] = tok
+    inputs["draft_tok"] = np.ascontiguousarray(tok[:, :D])
+    inputs["draft_lp"] = np.ascontiguousarray(lp[:, :D])
+    return inputs

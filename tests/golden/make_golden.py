@@ -21,7 +21,7 @@ import workloads  # noqa: E402
 
 def compute():
     cfg = workloads.config("tiny")
-    inp = workloads.make_inputs(cfg)
+    inp = oracle.attach_draft_topk(workloads.make_inputs(cfg), cfg.D, cfg.K)
     t = oracle.build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"], inp["prefix_len"],
                           cfg.budget)
     logits, _ = workloads.make_target_logits(cfg, inp, t["depth"], t["num_nodes"])

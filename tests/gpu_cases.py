@@ -35,7 +35,8 @@ class Case:
 
     def __init__(self, cfg, with_kv=True):
         self.cfg = cfg
-        self.inp = workloads.make_inputs(cfg, with_kv=with_kv)
+        self.inp = oracle.attach_draft_topk(workloads.make_inputs(cfg, with_kv=with_kv),
+                                            cfg.D, cfg.K)
         i = self.inp
         self.tree = oracle.build_tree(i["draft_lp"], i["draft_tok"], i["root_tok"],
                                       i["prefix_len"], cfg.budget)

@@ -25,7 +25,8 @@ import pytest
 from scipy.stats import chisquare
 
 import workloads
-from oracle import build_tree, verify_greedy, verify_sample, vocab_reduce, weight_constants, weights
+from oracle import (attach_draft_topk, build_tree, verify_greedy, verify_sample, vocab_reduce,
+                    weight_constants, weights)
 
 
 def _rand_tree(rng, B, D, K, budget, V=40):
@@ -111,7 +112,7 @@ def test_tree_accepts_at_least_the_greedy_chain(seed):
 
 def test_planted_targets_give_expected_accept_length():
     cfg = workloads.config("ragged", B=6, ctx=(4, 9), V=512, Hq=1, Hkv=1, Dh=8)
-    inp = workloads.make_inputs(cfg)
+    inp = attach_draft_topk(workloads.make_inputs(cfg), cfg.D, cfg.K)
     t = build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"], inp["prefix_len"], cfg.budget)
     logits, planted = workloads.make_target_logits(cfg, inp, t["depth"], t["num_nodes"])
     am = vocab_reduce(logits, t["num_nodes"], 0.0, dtype="bf16")["argmax"]

@@ -27,19 +27,10 @@ def test_inputs_are_deterministic_and_shaped():
     assert a["k_ctx"].shape == (int(a["ctx_offsets"][-1]), 1, 16)
     assert np.all((a["ctx_lens"] >= 5) & (a["ctx_lens"] <= 20))
     assert a["uniforms"].shape == (B, N, 2) and a["uniforms"].dtype == np.uint64
-    assert np.all(np.diff(a["draft_lp"], axis=-1) <= 0)
-    for b_ in range(B):
-        for d in range(cfg.D):
-            assert len(set(a["draft_tok"][b_, d].tolist())) == cfg.K
-
-
-def test_topk_order_and_tie_break():
-    row = np.array([[0.5, 2.0, 2.0, -1.0, 2.0, 1.0]], dtype=np.float32)
-    tok, lp = workloads.topk_logprobs(row, 4)
-    assert tok.tolist() == [[1, 2, 4, 5]]
-    r = row[0].astype(np.float64)
-    lse = np.log(np.exp(r).sum())
-    assert np.allclose(lp[0], (r[[1, 2, 4, 5]] - lse).astype(np.float32), rtol=0, atol=0)
+    assert a["draft_logits"].shape == (B, cfg.D + 1, cfg.V)
+    assert a["draft_logits"].dtype == np.float32
+    # the generator holds no step arithmetic: no top-K or log-probs in it
+    assert not {"draft_lp", "draft_tok", "draft_tok_all"} & set(a)
 
 
 def test_uniform_streams_are_per_request():

@@ -210,16 +210,32 @@ __global__ __launch_bounds__(kTkThreads) void topk_slice_kernel(
   if (S > 1 && tid == 0) ws_ms[static_cast<long>(row) * S + sl] = make_float2(m, ssum);
 }
 
-// One wave per row: merge the S slices' keys and (max, sum) pairs.
+// One wave per row: merge the S slices' keys and (max, sum) pairs.  With
+// kLds the row's S*K keys and S pairs are first copied into LDS with all their
+// loads in flight at once, so the K selection rounds and the two passes over
+// the pairs cost one round trip to memory instead of one each.
+constexpr int kMergeLdsBytes = 48 * 1024;
+
+template <bool kLds>
 __global__ __launch_bounds__(kWave) void topk_merge_kernel(int K, int S,
                                                             const uint64_t* __restrict__ ws_key,
                                                             const float2* __restrict__ ws_ms,
                                                             int32_t* __restrict__ tok,
                                                             float* __restrict__ lp) {
   __shared__ uint64_t s_top[DDTREE_MAX_TOPK];
+  extern __shared__ uint64_t s_dyn[];   // kLds: S*K keys, then S pairs
   const int row = blockIdx.x, lane = threadIdx.x;
-  const uint64_t* keys = ws_key + static_cast<long>(row) * S * K;
+  const int n = S * K;
+  const uint64_t* keys = ws_key + static_cast<long>(row) * n;
   const float2* ms = ws_ms + static_cast<long>(row) * S;
+  if (kLds) {
+    float2* s_ms = reinterpret_cast<float2*>(s_dyn + n);
+    for (int i = lane; i < n; i += kWave) s_dyn[i] = keys[i];
+    for (int i = lane; i < S; i += kWave) s_ms[i] = ms[i];
+    __syncthreads();
+    keys = s_dyn;
+    ms = s_ms;
+  }
   float m = -__builtin_huge_valf();
   for (int s = lane; s < S; s += kWave) m = max(m, ms[s].x);
   m = wave_max_f32(m);
@@ -230,7 +246,6 @@ __global__ __launch_bounds__(kWave) void topk_merge_kernel(int K, int S,
   }
   sum = wave_sum_f32(sum);
   const float lse = m + __logf(sum);
-  const int n = S * K;
   uint64_t prev = ~0ull;
   for (int j = 0; j < K; ++j) {
     uint64_t best = 0;
@@ -276,8 +291,15 @@ void launch_topk(int ept, const void* logits, int rows, int V, int K, int S, int
     case 16: launch_slices<T, 16>(logits, rows, V, K, S, chunk, wk, wm, tok, lp, st); break;
     default: launch_slices<T, 32>(logits, rows, V, K, S, chunk, wk, wm, tok, lp, st); break;
   }
-  if (S > 1)
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(rows), dim3(kWave), 0, st, K, S, wk, wm, tok, lp);
+  if (S > 1) {
+    const size_t lds = static_cast<size_t>(S) * (K + 1) * sizeof(uint64_t);
+    if (lds <= kMergeLdsBytes)
+      hipLaunchKernelGGL((topk_merge_kernel<true>), dim3(rows), dim3(kWave), lds, st, K, S, wk, wm,
+                         tok, lp);
+    else
+      hipLaunchKernelGGL((topk_merge_kernel<false>), dim3(rows), dim3(kWave), 0, st, K, S, wk, wm,
+                         tok, lp);
+  }
 }
 
 size_t topk_ws_bytes(int rows, int S, int K) {

@@ -32,13 +32,12 @@ Distributions (the standard deviation is the second argument of N(0, s)):
 from __future__ import annotations
 
 import dataclasses
-import math
 
 import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "config", "ctx_lengths", "make_inputs", "make_target_logits",
-    "topk_logprobs", "f32_to_bf16_bits", "bf16_bits_to_f32", "uniforms_for",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "uniforms_for",
 ]
 
 
@@ -135,34 +134,6 @@ def _normal(gen: np.random.Generator, shape, sigma: float, dtype: str,
     return out.reshape(shape)
 
 
-# --- per-depth top-k (harness stand-in for the draft head) --------------------------------
-
-def topk_logprobs(draft_logits: np.ndarray, K: int):
-    """Top-K tokens of each draft row and their full-vocabulary log-probs.
-
-    draft_logits: [..., V] float32.  Tokens are ordered by (logit desc, id asc);
-    log-probs are log_softmax at temperature 1 in float64, rounded to fp32."""
-    x = np.asarray(draft_logits, dtype=np.float32)
-    lead = x.shape[:-1]
-    V = x.shape[-1]
-    flat = x.reshape(-1, V)
-    toks = np.empty((flat.shape[0], K), dtype=np.int32)
-    lps = np.empty((flat.shape[0], K), dtype=np.float32)
-    for r in range(flat.shape[0]):
-        row = flat[r]
-        # candidates: everything >= the K-th largest value (keeps all ties)
-        kth = np.partition(row, V - K)[V - K]
-        cand = np.nonzero(row >= kth)[0]
-        order = np.lexsort((cand, -row[cand].astype(np.float64)))
-        sel = cand[order[:K]]
-        r64 = row.astype(np.float64)
-        m = r64.max()
-        lse = m + math.log(np.exp(r64 - m).sum())
-        toks[r] = sel
-        lps[r] = (r64[sel] - lse).astype(np.float32)
-    return toks.reshape(*lead, K), lps.reshape(*lead, K)
-
-
 # --- workload inputs ----------------------------------------------------------------------
 
 def ctx_lengths(cfg: Config) -> np.ndarray:
@@ -178,12 +149,13 @@ def make_inputs(cfg: Config, with_kv: bool = True) -> dict:
     Returns numpy arrays; bf16 tensors are uint16 bit patterns.
       ctx_lens [B] i32, ctx_offsets [B+1] i32, prefix_len [B] i32
       k_ctx, v_ctx [sum L, Hkv, Dh]; q [B, N, Hq, Dh]; k_tree, v_tree [B, N, Hkv, Dh]
-      draft_logits [B, D+1, V] f32 (row d predicts depth d+1)
-      draft_tok [B, D, K] i32, draft_lp [B, D, K] f32 (inputs of the tree build)
-      draft_tok_all [B, D+1, K] i32 (top-K of every draft row, used for planting)
+      draft_logits [B, D+1, V] f32 (row d predicts depth d+1; rows 0..D-1 feed
+        the draft top-K, row D only gives depth-D nodes a target row)
       root_tok [B] i32, uniforms [B, N, 2] u64
+    The tree build's inputs (draft_tok, draft_lp) are the draft top-K of the
+    first D rows: ddtree_draft_topk on the GPU, or the oracle's draft_topk.
     """
-    B, N, D, K, V = cfg.B, cfg.N, cfg.D, cfg.K, cfg.V
+    B, N, D, V = cfg.B, cfg.N, cfg.D, cfg.V
     lens = ctx_lengths(cfg)
     offs = np.zeros(B + 1, dtype=np.int64)
     offs[1:] = np.cumsum(lens)
@@ -200,10 +172,6 @@ def make_inputs(cfg: Config, with_kv: bool = True) -> dict:
     out["v_tree"] = _normal(_rng(cfg.seed, "v_tree"), (B, N, cfg.Hkv, cfg.Dh), 1.0, dt)
     dl = _normal(_rng(cfg.seed, "draft"), (B, D + 1, V), cfg.sigma_draft, "f32")
     out["draft_logits"] = dl
-    tok_all, lp_all = topk_logprobs(dl, K)
-    out["draft_tok_all"] = tok_all
-    out["draft_tok"] = np.ascontiguousarray(tok_all[:, :D])
-    out["draft_lp"] = np.ascontiguousarray(lp_all[:, :D])
     out["root_tok"] = _rng(cfg.seed, "root").integers(0, V, size=B).astype(np.int32)
     out["uniforms"] = np.stack([uniforms_for(cfg.seed, b, N) for b in range(B)])
     return out
@@ -219,6 +187,9 @@ def make_target_logits(cfg: Config, inputs: dict, depth: np.ndarray, num_nodes: 
     draft's top-1 token for depth d+1, otherwise uniformly one of the draft's
     ranks 2..4 (1-based) or a token outside that depth's top-K; the planted
     logit is the row maximum plus `plant_margin`.
+
+    Planting reads the draft's ranking from inputs["draft_tok_all"] [B, D+1, >= 4]
+    (each draft row's top tokens in rank order, from a draft top-K pass).
 
     Returns (logits, planted) where logits is uint16 bf16 bits or float32 and
     planted [B, N] i32 holds the planted token (-1 when not planting)."""
