@@ -336,6 +336,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
     for (int k = 0; k < E; ++k) {
       bsum += weight(v[k], m, wc);
       if (kLse) esum += __expf(v[k] - m);
+      // two elements in flight at most: more interleaving runs the 1024-thread
+      // workgroup's 128 registers per lane out and spills weights to scratch
+      if (k & 1) __builtin_amdgcn_sched_barrier(0);
     }
     if ((p + 1) % kPassPerBlock == 0 || p == MAXP - 1) {
       const uint64_t ws = wave_sum_u64(bsum);
