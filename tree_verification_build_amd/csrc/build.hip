@@ -255,11 +255,14 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int i = s * 64 + lane;
+    // selects rather than a computed index: a register array indexed at run
+    // time would live in scratch memory
+    const bool own = dep[s] >= 0, hasp = own && par[s] >= 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) va[s][w] = 0u;
-    if (dep[s] >= 0) {
-      va[s][i >> 5] |= 1u << (i & 31);
-      if (par[s] >= 0) va[s][par[s] >> 5] |= 1u << (par[s] & 31);
+    for (int w = 0; w < 4; ++w) {
+      uint32_t x = own && (i >> 5) == w ? 1u << (i & 31) : 0u;
+      x |= hasp && (par[s] >> 5) == w ? 1u << (par[s] & 31) : 0u;
+      va[s][w] = x;
     }
     anc[s] = par[s] >= 0 ? static_cast<uint32_t>(par[s]) : 0xFFFFFFFFu;
   }
