@@ -189,6 +189,36 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     torch.cuda.synchronize()
     t_pipe = time.perf_counter() - t_start
 
+    # sampling workloads: the same step with the lazy walk, which reduces only the
+    # target rows it visits (no vocabulary pass over every node); same sync loop
+    t_lazy = None
+    if T > 0:
+        def step_lazy(i):
+            s = sets[i % rotate]
+            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                             small["prefix_len"], cfg.budget, tree=tree)
+            attention(s)
+            lib.ddtree_verify_sample_lazy(tree, s["logits"], T, small["uniforms"],
+                                          outputs=outputs)
+        run_lazy = step_lazy
+        if graph:
+            lazy_graphs = []
+            for i in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step_lazy(i)
+                lazy_graphs.append(g)
+            run_lazy = lambda i: lazy_graphs[i % rotate].replay()  # noqa: E731
+        for i in range(warmup):
+            run_lazy(i)
+            stream.synchronize()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            run_lazy(i)
+            stream.synchronize()
+        t_lazy = time.perf_counter() - t_start
+
     # kernel durations: a HIP graph of back-to-back calls over the rotated input sets,
     # replayed between two HIP events on this stream (no host gaps fall inside)
     def timed_calls(fn, reps):
@@ -232,7 +262,8 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     e1.record(stream)
     torch.cuda.synchronize()
     topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
-    return {"t_sync": t_sync, "t_pipe": t_pipe, "attn_ms": attn_ms, "vocab_ms": vocab_ms,
+    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "attn_ms": attn_ms,
+            "vocab_ms": vocab_ms,
             "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
             "total_ctx": tot_ctx, "accept_len_mean": float(host_result[0].float().mean())}
 
@@ -396,6 +427,12 @@ def main():
                        "in_step": False},
         "accept_len_mean": r["accept_len_mean"],
     }
+    if r["t_lazy"] is not None:
+        line["lazy_sampling_walk"] = {
+            "steps_per_s": round(args.steps / r["t_lazy"], 2),
+            "ms_per_step": round(r["t_lazy"] / args.steps * 1e3, 4),
+            "step": "build, attention, ddtree_verify_sample_lazy (target rows reduced only "
+                    "where the walk goes; same outputs)"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

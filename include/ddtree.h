@@ -18,6 +18,7 @@
  *                          sampling, the exact integer softmax total R
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
+ *   ddtree_verify_sample_lazy  the same walk, reducing only the rows it visits
  *
  * Conventions shared by every call
  *   - Every data pointer is device-accessible memory owned by the caller
@@ -253,6 +254,28 @@ ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const void* logits,
                                    const uint64_t* uniforms,
                                    int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
                                    int32_t* bonus, hipStream_t stream);
+
+/*
+ * ddtree_verify_sample_lazy -- the sampled walk, with the target rows reduced
+ * only when the walk reaches them.
+ * Source: "Implementing Temperature-Aware Tree Sampling for DDTree", "Path B:
+ * CPU-Side Tree Rejection Sampling" (the target softmax computed lazily, for
+ * the nodes the rejection walk visits only), with the walk of
+ * ddtree_verify_sample.  Computes exactly what ddtree_vocab_reduce
+ * (temperature) followed by ddtree_verify_sample computes (bit-identical
+ * accept_len, path_nodes, out_tokens, bonus), but reads and weighs only the
+ * accept_len + 1 rows the walk visits instead of all N rows of every request:
+ * one 1024-thread workgroup per request, row after row.  Worth it when accept
+ * lengths are short next to the tree size; needs no maxv, R or workspace.
+ *   logits, uniforms, outputs, temperature: as for ddtree_verify_sample.
+ * Errors: DDTREE_EINVAL (null pointers, tree sizes, temperature <= 0, dtype),
+ *         DDTREE_EUNSUPPORTED (V > 64 * DDTREE_R_BLOCK).
+ */
+ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, const void* logits,
+                                        ddtree_dtype dtype, int32_t V, float temperature,
+                                        const uint64_t* uniforms, int32_t* accept_len,
+                                        int32_t* path_nodes, int32_t* out_tokens, int32_t* bonus,
+                                        hipStream_t stream);
 
 /* Host-only helper: the constants the sampling weights use for temperature T
  * (c = fp32(log2(e)/T) and a[0..6] = fp32((ln 2)^n / n!)).  No GPU needed. */

@@ -108,6 +108,12 @@ def test_host_validation_rejects_bad_arguments():
                                     fake, fake, fake, fake, None) == 1      # R_blocks missing
     assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 64 * 32768 + 1, fake, fake, fake,
                                     0.7, fake, fake, fake, fake, fake, None) == 2
+    assert lib.ddtree_verify_sample_lazy(ctypes.byref(t), fake, 1, 100, 0.0, fake, fake, fake,
+                                         fake, fake, None) == 1               # T <= 0
+    assert lib.ddtree_verify_sample_lazy(ctypes.byref(t), None, 1, 100, 0.7, fake, fake, fake,
+                                         fake, fake, None) == 1               # null logits
+    assert lib.ddtree_verify_sample_lazy(ctypes.byref(t), fake, 1, 64 * 32768 + 1, 0.7, fake,
+                                         fake, fake, fake, fake, None) == 2
     # attention
     offs = (ctypes.c_int32 * 2)(0, 64)
     args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]

@@ -117,6 +117,26 @@ def test_verify_sample(name):
         assert np.array_equal(o[k].cpu().numpy(), ref[k]), k
 
 
+@pytest.mark.parametrize("name", ALL)
+def test_verify_sample_lazy(name):
+    """The lazy walk reduces only the rows it visits; its outputs are the
+    oracle's (vocab pass + walk) bit for bit, at two temperatures, also when a
+    tiny temperature makes it follow the greedy path far into the tree."""
+    import tree_verification_build_amd as lib
+    c = case(name)
+    temps = sorted({c.cfg.temperature if c.cfg.temperature > 0 else 0.8, 0.05})
+    t = c.gpu_tree()
+    for T in temps:
+        say("verify_sample_lazy", name, "T", T)
+        o = lib.ddtree_verify_sample_lazy(t, c.d("logits"), T, c.d("uniforms"))
+        torch.cuda.synchronize()
+        ref_v = oracle.vocab_reduce(c.logits, c.tree["num_nodes"], T, dtype=c.cfg.dtype)
+        ref = oracle.verify_sample(c.tree, c.logits, ref_v["maxv"], ref_v["R"], T,
+                                   c.inp["uniforms"], c.cfg.D, dtype=c.cfg.dtype)
+        for k in ref:
+            assert np.array_equal(o[k].cpu().numpy(), ref[k]), (T, k)
+
+
 def _attn_sample(c):
     """(requests, heads) for the oracle: everything when small, a sample at full size."""
     cfg = c.cfg

@@ -49,9 +49,12 @@ lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f
 lib.ddtree_verify_greedy.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                      _vp, _vp, _vp]
+lib.ddtree_verify_sample_lazy.argtypes = [_tp, _vp, ctypes.c_int, _i32, _f32, _vp, _vp, _vp, _vp,
+                                          _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
-for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce", "ddtree_verify_greedy",
-           "ddtree_verify_sample", "ddtree_sampling_constants"):
+for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce",
+           "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
+           "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.ddtree_last_error.restype = ctypes.c_char_p
 lib.ddtree_version.restype = ctypes.c_char_p
@@ -270,6 +273,20 @@ def ddtree_verify_sample(tree, logits, maxv, R, R_blocks, temperature, uniforms,
                                     _ptr(uniforms),
                                     _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
                                     _ptr(o["out_tokens"]), _ptr(o["bonus"]), _stream(stream)))
+    return o
+
+
+def ddtree_verify_sample_lazy(tree, logits, temperature, uniforms, outputs=None, stream=None):
+    """The sampled walk reducing only the visited target rows (no vocab pass needed)."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(uniforms, "uniforms", torch.int64, (B, N, 2))
+    o = outputs or _walk_outputs(tree)
+    _check(lib.ddtree_verify_sample_lazy(tree.cstruct, _ptr(logits), _dtype_code(logits), V,
+                                         float(temperature), _ptr(uniforms),
+                                         _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
+                                         _ptr(o["out_tokens"]), _ptr(o["bonus"]),
+                                         _stream(stream)))
     return o
 
 

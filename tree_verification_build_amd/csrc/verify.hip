@@ -261,6 +261,233 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------ lazy sampled walk
+// The same walk as sample_kernel, but the target rows are reduced only when
+// the walk reaches them ("Implementing Temperature-Aware Tree Sampling for
+// DDTree", "Path B": the softmax only for the visited nodes): for
+// the row of the current node the workgroup computes the maximum, then the
+// integer weights summed per DDTREE_R_BLOCK block (hence R), with the same
+// arithmetic as ddtree_vocab_reduce, so the result is bit-identical to the
+// vocab pass followed by sample_kernel.  A row costs one read for the
+// maximum and one (mostly from cache) for the weights.
+constexpr int kLazyMaxBlocks = 64;
+
+// 16 bytes of logits as floats: E = 8 (bf16) or 4 (fp32); past V reads -inf
+template <typename T>
+__device__ __forceinline__ void lazy_load16(const T* row, long i, int V, bool vec, float* v) {
+  constexpr int E = Elem<T>::kPer16;
+  if (vec && i + E <= V) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + i);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (E == 8) v[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+      else v[e] = __uint_as_float(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = i + e < V ? Elem<T>::get(row, i + e) : -__builtin_huge_valf();
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
+    ddtree_tree t, const T* __restrict__ logits, int V, WeightConsts wc,
+    const uint64_t* __restrict__ uniforms, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path_nodes, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ bonus) {
+  constexpr int E = Elem<T>::kPer16;
+  constexpr int kPass = kSampleThreads * E;                  // tokens per pass
+  constexpr int kPassPerBlock = DDTREE_R_BLOCK / kPass;
+  static_assert(DDTREE_R_BLOCK % kPass == 0, "passes tile the weight blocks");
+  __shared__ uint64_t s_u0[kMaxN], s_u1[kMaxN];
+  __shared__ int32_t s_tok[kMaxN], s_fc[kMaxN], s_ns[kMaxN];
+  __shared__ int32_t s_rej[DDTREE_MAX_TOPK];
+  __shared__ uint64_t s_blkw[kLazyMaxBlocks][kSampleWaves];
+  __shared__ uint64_t s_Rb[kLazyMaxBlocks];
+  __shared__ uint64_t s_wave[kSampleWaves];
+  __shared__ float s_f[kSampleWaves];
+  __shared__ int s_nrej, s_cur, s_a, s_go, s_blk;
+  __shared__ uint64_t s_rres, s_trem;
+
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int N = t.N, D = t.D;
+  const long base = static_cast<long>(b) * N;
+  const int nn = t.num_nodes[b];
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  const int npass = (V + kPass - 1) / kPass;
+
+  for (int j = tid; j < N; j += kSampleThreads) {
+    int tk = -1, fc = -1, ns = -1;
+    if (j < nn) {
+      tk = t.token[base + j];
+      fc = t.first_child[base + j];
+      ns = t.next_sibling[base + j];
+    }
+    s_tok[j] = tk;
+    s_fc[j] = fc;
+    s_ns[j] = ns;
+    s_u0[j] = uniforms[(base + j) * 2 + 0];
+    s_u1[j] = uniforms[(base + j) * 2 + 1];
+  }
+  if (tid == 0) {
+    s_cur = 0;
+    s_a = 0;
+  }
+  __syncthreads();
+  int32_t* path = path_nodes + static_cast<long>(b) * (D + 1);
+  int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
+
+  float m = 0.f;
+  while (true) {
+    const int cur = s_cur;
+    const T* row = logits + (base + cur) * static_cast<long>(V);
+    const bool vec = aligned16(row) && (V % E == 0);
+    // the row maximum (float maximum; -0 read as +0, as in the vocab pass)
+    float vmax = -__builtin_huge_valf();
+#pragma unroll 8
+    for (int p = 0; p < npass; ++p) {   // unrolled: eight 16-byte loads in flight per thread
+      float v[E];
+      lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) vmax = max(vmax, v[e]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) vmax = max(vmax, shfl_xor_f32(vmax, o));
+    if (lane == 0) s_f[wave] = vmax;
+    __syncthreads();
+    m = s_f[0];
+#pragma unroll
+    for (int w = 1; w < kSampleWaves; ++w) m = max(m, s_f[w]);
+    m = m + 0.0f;
+    // the weights, summed per block of DDTREE_R_BLOCK tokens
+    uint64_t bsum = 0;
+#pragma unroll 4
+    for (int p = 0; p < npass; ++p) {
+      float v[E];
+      lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        bsum += weight(v[e], m, wc);
+        if (e & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      if ((p + 1) % kPassPerBlock == 0 || p == npass - 1) {
+        const uint64_t ws = wave_sum_u64(bsum);
+        if (lane == 0) s_blkw[p / kPassPerBlock][wave] = ws;
+        bsum = 0;
+      }
+    }
+    __syncthreads();
+    if (tid < nb) {
+      uint64_t bt = 0;
+      for (int w = 0; w < kSampleWaves; ++w) bt += s_blkw[tid][w];
+      s_Rb[tid] = bt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t rres = 0;
+      for (int k = 0; k < nb; ++k) rres += s_Rb[k];
+      // the children in rank order: accept iff mulhi(u, R_res) < w(token)
+      int nrej = 0, c = s_fc[cur];
+      bool moved = false;
+      while (c >= 0 && c < N && nrej < t.K) {
+        const int tk = s_tok[c];
+        const uint64_t wcur =
+            (tk >= 0 && tk < V) ? weight(Elem<T>::get(row, tk), m, wc) : 0ull;
+        if (__umul64hi(s_u0[c], rres) < wcur) {
+          moved = true;
+          break;
+        }
+        rres -= wcur;
+        s_rej[nrej] = tk;
+        ++nrej;
+        c = s_ns[c];
+      }
+      const int a = s_a;
+      if (moved && a < D) {
+        outt[a] = s_tok[c];
+        path[a + 1] = c;
+        s_cur = c;
+        s_a = a + 1;
+        s_go = 1;
+      } else {
+        s_go = 0;
+        s_nrej = nrej;
+        s_rres = rres;
+      }
+    }
+    __syncthreads();
+    if (!s_go) break;
+  }
+
+  // residual draw over the stopping node's row: which weight block holds it
+  // (the rejected tokens' weights come off their blocks), then 32 tokens per
+  // thread within the block
+  const int cur = s_cur, a = s_a, nrej = s_nrej;
+  const T* row = logits + (base + cur) * static_cast<long>(V);
+  if (wave == 0) {
+    const uint64_t tdraw = __umul64hi(s_u1[cur], s_rres);
+    uint64_t bs = 0;
+    if (lane < nb) {
+      bs = s_Rb[lane];
+      for (int r = 0; r < nrej; ++r) {
+        const int tk = s_rej[r];
+        if (tk >= 0 && tk / DDTREE_R_BLOCK == lane) bs -= weight(Elem<T>::get(row, tk), m, wc);
+      }
+    }
+    const uint64_t incl = wave_incl_scan_u64(bs, lane);
+    const uint64_t hit = __ballot(lane < nb && incl > tdraw);
+    const int blk = hit ? __builtin_ctzll(hit) : nb - 1;
+    const uint64_t ex = incl - bs;
+    const uint32_t exl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex), blk));
+    const uint32_t exh = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex >> 32), blk));
+    if (lane == 0) {
+      path[0] = 0;
+      s_blk = blk;
+      s_trem = tdraw - ((static_cast<uint64_t>(exh) << 32) | exl);
+      accept_len[b] = a;
+    }
+    for (int k = a + 1 + lane; k <= D; k += kWave) {
+      path[k] = -1;
+      outt[k] = -1;
+    }
+  }
+  __syncthreads();
+  const uint64_t trem = s_trem;
+  const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
+  float v[32];
+  load32<T>(row, x0, V, v);
+  uint64_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);
+  for (int r = 0; r < nrej; ++r) {
+    const long x = s_rej[r];
+    if (x >= x0 && x < x0 + 32) sum -= weight(v[x - x0], m, wc);
+  }
+  const uint64_t incl = wave_incl_scan_u64(sum, lane);
+  if (lane == kWave - 1) s_wave[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0;
+  for (int k = 0; k < wave; ++k) before += s_wave[k];
+  const uint64_t excl = before + incl - sum;
+  if (excl <= trem && trem < excl + sum) {
+    uint64_t acc = excl;
+    int pick = -1;
+    for (int e = 0; e < 32 && pick < 0; ++e) {
+      bool rej = false;
+      for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x0 + e);
+      if (rej) continue;
+      acc += weight(Elem<T>::get(row, x0 + e), m, wc);
+      if (acc > trem) pick = static_cast<int>(x0) + e;
+    }
+    outt[a] = pick;
+    bonus[b] = pick;
+  }
+}
+
 }  // namespace
 }  // namespace ddt
 
@@ -310,4 +537,37 @@ extern "C" ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const voi
     return fail(DDTREE_EINVAL, "ddtree_verify_sample: unknown dtype %d", static_cast<int>(dtype));
   }
   return check_launch("ddtree_verify_sample");
+}
+
+extern "C" ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, const void* logits,
+                                                   ddtree_dtype dtype, int32_t V,
+                                                   float temperature, const uint64_t* uniforms,
+                                                   int32_t* accept_len, int32_t* path_nodes,
+                                                   int32_t* out_tokens, int32_t* bonus,
+                                                   hipStream_t stream) {
+  using namespace ddt;
+  ddtree_status st = check_tree(tree, "ddtree_verify_sample_lazy");
+  if (st != DDTREE_OK) return st;
+  if (!logits || !uniforms || !accept_len || !path_nodes || !out_tokens || !bonus)
+    return fail(DDTREE_EINVAL, "ddtree_verify_sample_lazy: null pointer");
+  if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf()))
+    return fail(DDTREE_EINVAL, "ddtree_verify_sample_lazy: temperature must be > 0 and finite");
+  if (V < 1) return fail(DDTREE_EINVAL, "ddtree_verify_sample_lazy: V must be >= 1");
+  if (V > kLazyMaxBlocks * DDTREE_R_BLOCK)
+    return fail(DDTREE_EUNSUPPORTED, "ddtree_verify_sample_lazy: V = %d exceeds %d", V,
+                kLazyMaxBlocks * DDTREE_R_BLOCK);
+  const WeightConsts wc = weight_consts(temperature);
+  if (dtype == DDTREE_BF16) {
+    hipLaunchKernelGGL(sample_lazy_kernel<uint16_t>, dim3(tree->B), dim3(kSampleThreads), 0,
+                       stream, *tree, static_cast<const uint16_t*>(logits), V, wc, uniforms,
+                       accept_len, path_nodes, out_tokens, bonus);
+  } else if (dtype == DDTREE_F32) {
+    hipLaunchKernelGGL(sample_lazy_kernel<float>, dim3(tree->B), dim3(kSampleThreads), 0, stream,
+                       *tree, static_cast<const float*>(logits), V, wc, uniforms, accept_len,
+                       path_nodes, out_tokens, bonus);
+  } else {
+    return fail(DDTREE_EINVAL, "ddtree_verify_sample_lazy: unknown dtype %d",
+                static_cast<int>(dtype));
+  }
+  return check_launch("ddtree_verify_sample_lazy");
 }
