@@ -18,6 +18,9 @@ Sources (blog pages on DDTree speculative decoding):
                "The Design Constraint: Load Contexts Once".
   * vocab   -- Section 1 step 4 (per-node argmax); Section 3 (softmax over the
                verify logits at temperature T).
+  * linear  -- Section 3 (linear DFlash at temperature T: accept with
+               min(1, p_target / p_draft), else the residual) and "Mistakes and
+               Incorrect Assumptions" (the draft's full probabilities are needed).
   * verify  -- Section 1 step 5 (greedy walk, bonus token); Section 3 and
                "Implementing Temperature-Aware Tree Sampling for DDTree",
                "Path B: CPU-Side Tree Rejection Sampling" (tree rejection
@@ -32,6 +35,8 @@ from .build import build_tree, N_WORDS
 from .attention import tree_attention, to_f64
 from .vocab import vocab_reduce, weight_constants, weights
 from .verify import verify_greedy, verify_sample
+from .linear import verify_linear_sample
 
 __all__ = ["attach_draft_topk", "draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
-           "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample"]
+           "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample",
+           "verify_linear_sample"]
