@@ -239,6 +239,7 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     attn_ms = timed_calls(attention, reps)
     vocab_ms = timed_calls(vocab, reps)
     del sets, graphs
+    lin = run_linear(cfg, inp, tok_all, stream) if T > 0 else None
     # the draft top-K over the D draft rows of each request (outside the step),
     # over enough copies that the last-level cache does not hold them
     rows_d = dl[:, :cfg.D].contiguous()
@@ -262,10 +263,64 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     e1.record(stream)
     torch.cuda.synchronize()
     topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
-    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "attn_ms": attn_ms,
-            "vocab_ms": vocab_ms,
+    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "linear": lin,
+            "attn_ms": attn_ms, "vocab_ms": vocab_ms,
             "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
             "total_ctx": tot_ctx, "accept_len_mean": float(host_result[0].float().mean())}
+
+
+def run_linear(cfg, inp, tok_all, stream, reps=50):
+    """Linear speculative sampling on the workload's draft rows: a chain of D
+    drafted tokens per request (the draft's top-1 at each depth), target rows =
+    the draft rows plus the workload's target noise, both in the workload's dtype.
+    Times the vocabulary pass over the D+1 target and D draft rows plus the walk
+    (graph of back-to-back calls between two HIP events)."""
+    import torch
+    import tree_verification_build_amd as lib
+    import workloads
+    dev = "cuda:0"
+    B, D, T = cfg.B, cfg.D, cfg.temperature
+    chain = workloads.config(cfg.name, budget=D)
+    depth = np.tile(np.arange(D + 1, dtype=np.int32), (B, 1))
+    tl, _ = workloads.make_target_logits(chain, inp, depth, np.full(B, D + 1, np.int32))
+    dl = np.ascontiguousarray(inp["draft_logits"][:, :D])
+    if cfg.dtype == "bf16":
+        dl = workloads.f32_to_bf16_bits(dl)
+        tg = torch.from_numpy(tl.view(np.int16)).view(torch.bfloat16).to(dev)
+        dg = torch.from_numpy(dl.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        tg, dg = torch.from_numpy(tl).to(dev), torch.from_numpy(dl).to(dev)
+    x = tok_all[:, :D, 0].contiguous()
+    u = torch.from_numpy(np.ascontiguousarray(inp["uniforms"][:, :D + 1]).view(np.int64)).to(dev)
+    nq = torch.full((B,), D + 1, dtype=torch.int32, device=dev)
+    npd = torch.full((B,), D, dtype=torch.int32, device=dev)
+    out = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+           "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+           "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+
+    def call():
+        ts = lib.ddtree_vocab_reduce(tg, nq, T)
+        ds = lib.ddtree_vocab_reduce(dg, npd, T)
+        lib.ddtree_verify_linear_sample(tg, dg, x, T, u, target_stats=ts, draft_stats=ds,
+                                        outputs=out)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"ms_per_call": round(ms, 4), "accept_len_mean": float(out["accept_len"].float().mean()),
+            "calls": "ddtree_vocab_reduce (target D+1 rows, draft D rows) + "
+                     "ddtree_verify_linear_sample",
+            "chain": f"{B} requests x {D} drafted tokens (draft top-1), V {cfg.V}, T {T}"}
 
 
 def run_copy_calibration(mib, reps=20):
@@ -427,6 +482,8 @@ def main():
                        "in_step": False},
         "accept_len_mean": r["accept_len_mean"],
     }
+    if r["linear"] is not None:
+        line["linear_speculative_sampling"] = r["linear"]
     if r["t_lazy"] is not None:
         line["lazy_sampling_walk"] = {
             "steps_per_s": round(args.steps / r["t_lazy"], 2),

@@ -19,6 +19,7 @@
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
  *   ddtree_verify_sample_lazy  the same walk, reducing only the rows it visits
+ *   ddtree_verify_linear_sample  linear speculative sampling with draft probabilities
  *
  * Conventions shared by every call
  *   - Every data pointer is device-accessible memory owned by the caller
@@ -276,6 +277,45 @@ ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, const void* log
                                         const uint64_t* uniforms, int32_t* accept_len,
                                         int32_t* path_nodes, int32_t* out_tokens, int32_t* bonus,
                                         hipStream_t stream);
+
+/*
+ * ddtree_verify_linear_sample -- linear speculative sampling with the draft's
+ * own probabilities (a chain of D drafted tokens, no tree).
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 3
+ * (linear DFlash at temperature T: accept the drafted token with probability
+ * min(1, p_target / p_draft), else draw from the residual and stop) and
+ * "Mistakes and Incorrect Assumptions" (the draft's full probability of the
+ * sampled token is needed, not only its top-k log-prob).
+ * Readings: the drafted tokens were drawn from the draft's softmax at the same
+ * T; the residual is max(0, q - p) renormalised; q and p are the exact integer
+ * laws w / R (see ddtree_vocab_reduce), so position k accepts its token x iff
+ * floor(u0 * wp(x) * Rq / 2^64) < wq(x) * Rp, a rejection draws
+ * t = floor(u1 * Rr / 2^64) over r(y) = max(0, wq(y) Rp - wp(y) Rq) (from q if
+ * Rr = 0), and after D acceptances the bonus is drawn from target row D.
+ *   target_logits [B, D+1, V]  row k: the target's distribution for position k+1
+ *   draft_logits  [B, D, V]    row k: the draft distribution token k was drawn from
+ *   draft_tokens  [B, D] int32
+ *   maxq, Rq, Rq_blocks  ddtree_vocab_reduce(target_logits as [B, D+1, V],
+ *                  num_nodes = D+1, temperature): [B, D+1], [B, D+1], [B, D+1, nb]
+ *   maxp, Rp       ddtree_vocab_reduce(draft_logits as [B, D, V], num_nodes = D,
+ *                  temperature): [B, D], [B, D]
+ *   uniforms       [B, D+1, 2] raw 64-bit: slot 0 = accept test of position k,
+ *                  slot 1 = residual draw at k (or the bonus draw at k = D)
+ *   accept_len [B], out_tokens [B, D+1] (accepted tokens, then the residual or
+ *   bonus token, then -1), bonus [B]
+ * One 1024-thread workgroup per request; a residual is summed over the whole
+ * row pair (ALU work of the order of a vocabulary pass over two rows).
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature <= 0, dtype),
+ *         DDTREE_EUNSUPPORTED (V > 64 * DDTREE_R_BLOCK).
+ */
+ddtree_status ddtree_verify_linear_sample(const void* target_logits, const void* draft_logits,
+                                          ddtree_dtype dtype, int32_t B, int32_t D, int32_t V,
+                                          const int32_t* draft_tokens, const float* maxq,
+                                          const uint64_t* Rq, const uint64_t* Rq_blocks,
+                                          const float* maxp, const uint64_t* Rp,
+                                          float temperature, const uint64_t* uniforms,
+                                          int32_t* accept_len, int32_t* out_tokens,
+                                          int32_t* bonus, hipStream_t stream);
 
 /* Host-only helper: the constants the sampling weights use for temperature T
  * (c = fp32(log2(e)/T) and a[0..6] = fp32((ln 2)^n / n!)).  No GPU needed. */

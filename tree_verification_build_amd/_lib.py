@@ -51,10 +51,12 @@ lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp
                                      _vp, _vp, _vp]
 lib.ddtree_verify_sample_lazy.argtypes = [_tp, _vp, ctypes.c_int, _i32, _f32, _vp, _vp, _vp, _vp,
                                           _vp, _vp]
+lib.ddtree_verify_linear_sample.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
+                                            _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
-           "ddtree_sampling_constants"):
+           "ddtree_verify_linear_sample", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.ddtree_last_error.restype = ctypes.c_char_p
 lib.ddtree_version.restype = ctypes.c_char_p
@@ -287,6 +289,38 @@ def ddtree_verify_sample_lazy(tree, logits, temperature, uniforms, outputs=None,
                                          _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
                                          _ptr(o["out_tokens"]), _ptr(o["bonus"]),
                                          _stream(stream)))
+    return o
+
+
+def ddtree_verify_linear_sample(target_logits, draft_logits, draft_tokens, temperature, uniforms,
+                                target_stats=None, draft_stats=None, outputs=None, stream=None):
+    """Linear speculative sampling over a chain of D drafted tokens.  target_logits
+    [B, D+1, V], draft_logits [B, D, V], draft_tokens [B, D] int32, uniforms [B, D+1, 2]
+    int64 bits.  target_stats / draft_stats: ddtree_vocab_reduce results of the two
+    tensors at this temperature (computed here when omitted).  Returns dict(accept_len
+    [B], out_tokens [B, D+1], bonus [B])."""
+    B, D1, V = target_logits.shape
+    D = D1 - 1
+    _dev(target_logits, "target_logits", (torch.bfloat16, torch.float32))
+    _dev(draft_logits, "draft_logits", target_logits.dtype, (B, D, V))
+    _dev(draft_tokens, "draft_tokens", torch.int32, (B, D))
+    _dev(uniforms, "uniforms", torch.int64, (B, D + 1, 2))
+    dev = target_logits.device
+    if target_stats is None:
+        target_stats = ddtree_vocab_reduce(
+            target_logits, torch.full((B,), D + 1, dtype=torch.int32, device=dev), temperature)
+    if draft_stats is None:
+        draft_stats = ddtree_vocab_reduce(
+            draft_logits, torch.full((B,), D, dtype=torch.int32, device=dev), temperature)
+    o = outputs or {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+                    "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+                    "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+    _check(lib.ddtree_verify_linear_sample(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), B, D, V,
+        _ptr(draft_tokens), _ptr(target_stats["maxv"]), _ptr(target_stats["R"]),
+        _ptr(target_stats["R_blocks"]), _ptr(draft_stats["maxv"]), _ptr(draft_stats["R"]),
+        float(temperature), _ptr(uniforms), _ptr(o["accept_len"]), _ptr(o["out_tokens"]),
+        _ptr(o["bonus"]), _stream(stream)))
     return o
 
 

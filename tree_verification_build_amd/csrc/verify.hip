@@ -488,6 +488,235 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
   }
 }
 
+
+// ------------------------------------------------------------------ linear speculative sampling
+// A chain of D drafted tokens, each drawn by the draft from its own softmax
+// ("Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 3, linear
+// DFlash at temperature T): position k accepts its token x with probability
+// min(1, q(x) / p(x)), else draws from the residual max(0, q - p) and stops;
+// after D acceptances the bonus comes from the target row D.  q and p are the
+// exact integer laws w / R of the vocabulary pass (each row with its own
+// maximum), so the accept test and the residual are integer arithmetic:
+//   accept  iff  floor(u0 * wp(x) * Rq / 2^64) < wq(x) * Rp        (<= 147-bit)
+//   r(y) = max(0, wq(y) Rp - wp(y) Rq) (< 2^83), Rr = sum r (< 2^101),
+//   t = floor(u1 * Rr / 2^64), token = smallest y with running sum > t;
+// if Rr = 0 the draw is from q.  One 1024-thread workgroup per request:
+// thread 0 runs the accept tests; a residual is summed by the workgroup in
+// passes of 8192 tokens (8 consecutive per thread), the pass holding t is
+// found from the pass sums, and that pass is rescanned.
+typedef unsigned __int128 u128;
+
+__device__ __forceinline__ u128 mulhi_64x128(uint64_t u, u128 a) {
+  const uint64_t lo = static_cast<uint64_t>(a), hi = static_cast<uint64_t>(a >> 64);
+  return static_cast<u128>(__umul64hi(u, lo)) + static_cast<u128>(u) * hi;
+}
+
+__device__ __forceinline__ u128 shfl_xor_u128(u128 v, int m) {
+  const uint64_t lo = __shfl_xor(static_cast<uint64_t>(v), m, kWave);
+  const uint64_t hi = __shfl_xor(static_cast<uint64_t>(v >> 64), m, kWave);
+  return (static_cast<u128>(hi) << 64) | lo;
+}
+
+__device__ __forceinline__ u128 shfl_up_u128(u128 v, int d) {
+  const uint64_t lo = __shfl_up(static_cast<uint64_t>(v), d, kWave);
+  const uint64_t hi = __shfl_up(static_cast<uint64_t>(v >> 64), d, kWave);
+  return (static_cast<u128>(hi) << 64) | lo;
+}
+
+constexpr int kLinPass = kSampleThreads * 8;      // tokens per residual pass
+constexpr int kLinMaxPass = 64 * DDTREE_R_BLOCK / kLinPass;
+
+// residual weight of token y (0 past the row)
+template <typename T>
+__device__ __forceinline__ u128 residual_w(const T* qrow, const T* prow, long y, int V, float mq,
+                                           float mp, uint64_t Rq, uint64_t Rp,
+                                           const WeightConsts& wc) {
+  if (y >= V) return 0;
+  const uint64_t wq = weight(Elem<T>::get(qrow, y), mq, wc);
+  const uint64_t wp = weight(Elem<T>::get(prow, y), mp, wc);
+  const u128 a = static_cast<u128>(wq) * Rp, b = static_cast<u128>(wp) * Rq;
+  return a > b ? a - b : 0;
+}
+
+// inclusive scan of a u128 over the workgroup in token (= thread) order;
+// returns the exclusive prefix of this thread and writes the total
+__device__ __forceinline__ u128 block_excl_scan_u128(u128 v, int lane, int wave, u128* s_w,
+                                                     u128* total) {
+  u128 incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const u128 o = shfl_up_u128(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) s_w[wave] = incl;
+  __syncthreads();
+  u128 before = 0, tot = 0;
+  for (int k = 0; k < kSampleWaves; ++k) {
+    if (k < wave) before += s_w[k];
+    tot += s_w[k];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
+    const T* __restrict__ tlog, const T* __restrict__ dlog, int D, int V,
+    const int32_t* __restrict__ dtok, const float* __restrict__ maxq,
+    const uint64_t* __restrict__ Rq, const uint64_t* __restrict__ Rqb,
+    const float* __restrict__ maxp, const uint64_t* __restrict__ Rp, WeightConsts wc,
+    const uint64_t* __restrict__ uniforms, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ bonus) {
+  __shared__ u128 s_w[kSampleWaves];
+  __shared__ u128 s_pass[kLinMaxPass];
+  __shared__ uint64_t s_wave[kSampleWaves];
+  __shared__ int s_k, s_mode, s_pick, s_blk;
+  __shared__ u128 s_t;
+  __shared__ uint64_t s_trem;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
+
+  if (tid == 0) {
+    // accept tests, position by position
+    int k = 0;
+    for (; k < D; ++k) {
+      const long rq = static_cast<long>(b) * (D + 1) + k, rp = static_cast<long>(b) * D + k;
+      const int x = dtok[rp];
+      uint64_t wq = 0, wp = 0;
+      if (x >= 0 && x < V) {
+        wq = weight(Elem<T>::get(tlog + rq * V, x), maxq[rq], wc);
+        wp = weight(Elem<T>::get(dlog + rp * V, x), maxp[rp], wc);
+      }
+      const u128 A = static_cast<u128>(wp) * Rq[rq], B = static_cast<u128>(wq) * Rp[rp];
+      if (!(mulhi_64x128(uniforms[rq * 2 + 0], A) < B)) break;
+      outt[k] = x;
+    }
+    s_k = k;
+    // mode 0: draw from q of row k (the bonus, or a vanished residual); 1: residual
+    s_mode = k < D ? 1 : 0;
+    s_pick = -1;
+  }
+  __syncthreads();
+  const int k = s_k;
+  const long rq = static_cast<long>(b) * (D + 1) + k;
+  const T* qrow = tlog + rq * V;
+  const uint64_t u1 = uniforms[rq * 2 + 1];
+  if (s_mode == 1) {
+    const long rp = static_cast<long>(b) * D + k;
+    const T* prow = dlog + rp * V;
+    const float mq = maxq[rq], mp = maxp[rp];
+    const uint64_t Rqk = Rq[rq], Rpk = Rp[rp];
+    const int npass = (V + kLinPass - 1) / kLinPass;
+    // pass sums of the residual
+    for (int p = 0; p < npass; ++p) {
+      const long y0 = static_cast<long>(p) * kLinPass + static_cast<long>(tid) * 8;
+      u128 s = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += residual_w<T>(qrow, prow, y0 + e, V, mq, mp, Rqk, Rpk, wc);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) s += shfl_xor_u128(s, m);
+      if (lane == 0) s_w[wave] = s;
+      __syncthreads();
+      if (tid == 0) {
+        u128 t = 0;
+        for (int w = 0; w < kSampleWaves; ++w) t += s_w[w];
+        s_pass[p] = t;
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      u128 Rr = 0;
+      for (int p = 0; p < npass; ++p) Rr += s_pass[p];
+      if (Rr == 0) {
+        s_mode = 0;   // q and p proportional: draw from q
+      } else {
+        const u128 t = mulhi_64x128(u1, Rr);
+        u128 acc = 0;
+        int p = 0;
+        while (p < npass - 1 && acc + s_pass[p] <= t) acc += s_pass[p++];
+        s_blk = p;
+        s_t = t - acc;
+      }
+    }
+    __syncthreads();
+    if (s_mode == 1) {
+      // rescan the pass holding the draw, in token order
+      const u128 t = s_t;
+      const long y0 = static_cast<long>(s_blk) * kLinPass + static_cast<long>(tid) * 8;
+      u128 r[8], s = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        r[e] = residual_w<T>(qrow, prow, y0 + e, V, mq, mp, Rqk, Rpk, wc);
+        s += r[e];
+      }
+      u128 tot;
+      const u128 excl = block_excl_scan_u128(s, lane, wave, s_w, &tot);
+      if (s > 0 && excl <= t && t < excl + s) {
+        u128 acc = excl;
+        int pick = -1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          acc += r[e];
+          if (pick < 0 && acc > t) pick = static_cast<int>(y0) + e;
+        }
+        s_pick = pick;
+      }
+      __syncthreads();
+    }
+  }
+  if (s_mode == 0) {
+    // draw from q of row k with the block sums of the vocabulary pass
+    if (wave == 0) {
+      const uint64_t tdraw = __umul64hi(u1, Rq[rq]);
+      const uint64_t bs = lane < nb ? Rqb[rq * nb + lane] : 0ull;
+      const uint64_t incl = wave_incl_scan_u64(bs, lane);
+      const uint64_t hit = __ballot(lane < nb && incl > tdraw);
+      const int blk = hit ? __builtin_ctzll(hit) : nb - 1;
+      const uint64_t ex = incl - bs;
+      const uint32_t exl = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex), blk));
+      const uint32_t exh = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<uint32_t>(ex >> 32), blk));
+      if (lane == 0) {
+        s_blk = blk;
+        s_trem = tdraw - ((static_cast<uint64_t>(exh) << 32) | exl);
+      }
+    }
+    __syncthreads();
+    const uint64_t trem = s_trem;
+    const float m = maxq[rq];
+    const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
+    float v[32];
+    load32<T>(qrow, x0, V, v);
+    uint64_t sum = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);
+    const uint64_t incl = wave_incl_scan_u64(sum, lane);
+    if (lane == kWave - 1) s_wave[wave] = incl;
+    __syncthreads();
+    uint64_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    const uint64_t excl = before + incl - sum;
+    if (excl <= trem && trem < excl + sum) {
+      uint64_t acc = excl;
+      int pick = -1;
+      for (int e = 0; e < 32 && pick < 0; ++e) {
+        acc += weight(v[e], m, wc);
+        if (acc > trem) pick = static_cast<int>(x0) + e;
+      }
+      s_pick = pick;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    accept_len[b] = k;
+    outt[k] = s_pick;
+    bonus[b] = s_pick;
+    for (int j = k + 1; j <= D; ++j) outt[j] = -1;
+  }
+}
+
 }  // namespace
 }  // namespace ddt
 
@@ -570,4 +799,40 @@ extern "C" ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, cons
                 static_cast<int>(dtype));
   }
   return check_launch("ddtree_verify_sample_lazy");
+}
+
+extern "C" ddtree_status ddtree_verify_linear_sample(
+    const void* target_logits, const void* draft_logits, ddtree_dtype dtype, int32_t B, int32_t D,
+    int32_t V, const int32_t* draft_tokens, const float* maxq, const uint64_t* Rq,
+    const uint64_t* Rq_blocks, const float* maxp, const uint64_t* Rp, float temperature,
+    const uint64_t* uniforms, int32_t* accept_len, int32_t* out_tokens, int32_t* bonus,
+    hipStream_t stream) {
+  using namespace ddt;
+  if (!target_logits || !draft_logits || !draft_tokens || !maxq || !Rq || !Rq_blocks || !maxp ||
+      !Rp || !uniforms || !accept_len || !out_tokens || !bonus)
+    return fail(DDTREE_EINVAL, "ddtree_verify_linear_sample: null pointer");
+  if (B < 1 || D < 1 || D > DDTREE_MAX_DEPTH || V < 1)
+    return fail(DDTREE_EINVAL, "ddtree_verify_linear_sample: sizes out of range (B=%d D=%d V=%d)",
+                B, D, V);
+  if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf()))
+    return fail(DDTREE_EINVAL, "ddtree_verify_linear_sample: temperature must be > 0 and finite");
+  if (V > kWave * DDTREE_R_BLOCK)
+    return fail(DDTREE_EUNSUPPORTED, "ddtree_verify_linear_sample: V = %d exceeds %d", V,
+                kWave * DDTREE_R_BLOCK);
+  const WeightConsts wc = weight_consts(temperature);
+  if (dtype == DDTREE_BF16) {
+    hipLaunchKernelGGL(linear_sample_kernel<uint16_t>, dim3(B), dim3(kSampleThreads), 0, stream,
+                       static_cast<const uint16_t*>(target_logits),
+                       static_cast<const uint16_t*>(draft_logits), D, V, draft_tokens, maxq, Rq,
+                       Rq_blocks, maxp, Rp, wc, uniforms, accept_len, out_tokens, bonus);
+  } else if (dtype == DDTREE_F32) {
+    hipLaunchKernelGGL(linear_sample_kernel<float>, dim3(B), dim3(kSampleThreads), 0, stream,
+                       static_cast<const float*>(target_logits),
+                       static_cast<const float*>(draft_logits), D, V, draft_tokens, maxq, Rq,
+                       Rq_blocks, maxp, Rp, wc, uniforms, accept_len, out_tokens, bonus);
+  } else {
+    return fail(DDTREE_EINVAL, "ddtree_verify_linear_sample: unknown dtype %d",
+                static_cast<int>(dtype));
+  }
+  return check_launch("ddtree_verify_linear_sample");
 }
