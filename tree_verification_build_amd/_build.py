@@ -21,6 +21,12 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-source extras.  attention.hip: keep MFMA accumulators in ordinary VGPRs;
+# with the AGPR forms the compiler copies the attention accumulators between the
+# two register files on every key tile.
+FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -36,7 +42,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *HIP_FLAGS, "-c", src, "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -472,13 +472,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// NaN-propagating maximum: gfx950 has a three-operand instruction for it that,
+// unlike fmaxf's, needs no quieting of its operands first
+__device__ __forceinline__ float nmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum over the four 16-lane rows (lanes l, l^16, l^32, l^48): the gfx950
 // lane swaps return {x, x of the partner lane} in some order
 __device__ __forceinline__ float rows_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float rows_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -637,10 +641,10 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
           if (!((mg >> (kb * 16 + e)) & 1ull)) sv[kb][e] = -__builtin_huge_valf();
     }
     // online softmax in base 2 with a lagging maximum
-    float t0 = max(max(sv[0][0], sv[0][1]), max(sv[0][2], sv[0][3]));
+    float t0 = nmax(nmax(sv[0][0], sv[0][1]), nmax(sv[0][2], sv[0][3]));
 #pragma unroll
     for (int kb = 1; kb < KB; ++kb)
-      t0 = max(t0, max(max(sv[kb][0], sv[kb][1]), max(sv[kb][2], sv[kb][3])));
+      t0 = nmax(t0, nmax(nmax(sv[kb][0], sv[kb][1]), nmax(sv[kb][2], sv[kb][3])));
     const float mc = rows_max(t0) * c;
     const bool up = mc > m_run + kLagLog2;
     if (__builtin_amdgcn_ballot_w64(up)) {
