@@ -21,6 +21,9 @@ Sources (blog pages on DDTree speculative decoding):
   * linear  -- Section 3 (linear DFlash at temperature T: accept with
                min(1, p_target / p_draft), else the residual) and "Mistakes and
                Incorrect Assumptions" (the draft's full probabilities are needed).
+  * commit  -- Section 1 step 5 and its summary (the longest verified path is
+               committed) and Section 2 (the context cache grows by the
+               committed tokens and is read once by later steps).
   * verify  -- Section 1 step 5 (greedy walk, bonus token); Section 3 and
                "Implementing Temperature-Aware Tree Sampling for DDTree",
                "Path B: CPU-Side Tree Rejection Sampling" (tree rejection
@@ -36,7 +39,8 @@ from .attention import tree_attention, to_f64
 from .vocab import vocab_reduce, weight_constants, weights
 from .verify import verify_greedy, verify_sample
 from .linear import verify_linear_sample
+from .commit import commit_path
 
 __all__ = ["attach_draft_topk", "draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
            "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample",
-           "verify_linear_sample"]
+           "verify_linear_sample", "commit_path"]
