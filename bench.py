@@ -238,6 +238,22 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     reps = max(1, steps // rotate)
     attn_ms = timed_calls(attention, reps)
     vocab_ms = timed_calls(vocab, reps)
+    # the commit that follows a step (not part of it): the last step's walk, its
+    # path rows into a compact cache (request b's position p at row
+    # b * (D + 1) + p - prefix_len[b])
+    walk = {k: v.to(dev) for k, v in outputs.items()}
+    cb = (torch.arange(cfg.B, dtype=torch.int64, device=dev) * (cfg.D + 1)
+          - small["prefix_len"].to(torch.int64))
+    kcache = torch.empty((cfg.B * (cfg.D + 1), cfg.Hkv, cfg.Dh), dtype=base["k_tree"].dtype,
+                         device=dev)
+    vcache = torch.empty_like(kcache)
+    nxt = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
+    nroot = torch.empty_like(nxt)
+    commit_ms = timed_calls(lambda s: lib.ddtree_commit(
+        tree, walk, s["k_tree"], s["v_tree"], kcache, vcache, cb, 1 << 30,
+        next_prefix_len=nxt, next_root=nroot), reps)
+    commit_rows = int(walk["accept_len"].sum().item()) + cfg.B
+    commit_bytes = commit_rows * 2 * 2 * cfg.Hkv * cfg.Dh * base["k_tree"].element_size()
     del sets, graphs
     lin = run_linear(cfg, inp, tok_all, stream) if T > 0 else None
     # the draft top-K over the D draft rows of each request (outside the step),
@@ -264,7 +280,8 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     torch.cuda.synchronize()
     topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
     return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "linear": lin,
-            "attn_ms": attn_ms, "vocab_ms": vocab_ms,
+            "attn_ms": attn_ms, "vocab_ms": vocab_ms, "commit_ms": commit_ms,
+            "commit_rows": commit_rows, "commit_bytes": commit_bytes,
             "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
             "total_ctx": tot_ctx, "accept_len_mean": float(host_result[0].float().mean())}
 
@@ -480,6 +497,8 @@ def main():
         "draft_topk": {"achieved_GBs": round(r["topk_bytes"] / (r["topk_ms"] * 1e-3) / 1e9, 1),
                        "avg_ms": round(r["topk_ms"], 5), "bytes_per_launch": r["topk_bytes"],
                        "in_step": False},
+        "commit": {"avg_ms": round(r["commit_ms"], 5), "rows": r["commit_rows"],
+                   "bytes_per_launch": r["commit_bytes"], "in_step": False},
         "accept_len_mean": r["accept_len_mean"],
     }
     if r["linear"] is not None:

@@ -20,6 +20,8 @@
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
  *   ddtree_verify_sample_lazy  the same walk, reducing only the rows it visits
  *   ddtree_verify_linear_sample  linear speculative sampling with draft probabilities
+ *   ddtree_commit          the accepted path's K/V rows into the context cache;
+ *                          the next step's prefix length and root token
  *
  * Conventions shared by every call
  *   - Every data pointer is device-accessible memory owned by the caller
@@ -316,6 +318,44 @@ ddtree_status ddtree_verify_linear_sample(const void* target_logits, const void*
                                           float temperature, const uint64_t* uniforms,
                                           int32_t* accept_len, int32_t* out_tokens,
                                           int32_t* bonus, hipStream_t stream);
+
+/*
+ * ddtree_commit -- commit the accepted path into the context KV cache.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 1
+ * step 5 and its summary (the single longest verified path is committed) and
+ * Section 2 (the context cache grows by the committed tokens and is read once
+ * by later steps).
+ * Readings: the rows committed are the verify pass's K/V of the root and of the
+ * accepted nodes (path_nodes[b][0 .. accept_len[b]]); node n goes to its tree
+ * position (tree->position, = prefix_len + depth); the bonus token has no K/V
+ * yet and becomes the next root.
+ *   tree        the build's outputs (position is read)
+ *   accept_len, path_nodes [B, D+1], bonus   from a verify walk
+ *   k_tree, v_tree [B, N, Hkv, Dh] (dtype): the tree's keys and values, as
+ *               passed to ddtree_tree_attention
+ *   k_cache, v_cache [cache_rows, Hkv, Dh] (dtype): the cache; request b's
+ *               position p is row cache_base[b] + p (for one request, the
+ *               packed context of ddtree_tree_attention with ctx_offsets
+ *               {0, prefix_len}; for several, per-request slabs)
+ *   cache_base  [B] int64 device array
+ *   capacity    positions per request: a row whose position is >= capacity,
+ *               or whose row index falls outside [0, cache_rows), is not
+ *               written (no error; compare next_prefix_len with capacity)
+ *   next_prefix_len [B]  position[b][0] + accept_len[b] + 1, or -1 when
+ *               accept_len[b] is outside [0, D] (nothing is written then)
+ *   next_root   [B]      the bonus token
+ * next_prefix_len / next_root may alias the build's prefix_len / root_tok
+ * inputs (not accept_len or path_nodes); the cache must not overlap k_tree /
+ * v_tree.
+ * Errors: DDTREE_EINVAL (null pointers, sizes, dtype, alignment),
+ *         DDTREE_EUNSUPPORTED (Hkv * Dh * element size not a multiple of 16).
+ */
+ddtree_status ddtree_commit(const ddtree_tree* tree, const int32_t* accept_len,
+                            const int32_t* path_nodes, const int32_t* bonus, const void* k_tree,
+                            const void* v_tree, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
+                            void* k_cache, void* v_cache, const int64_t* cache_base,
+                            int64_t cache_rows, int32_t capacity, int32_t* next_prefix_len,
+                            int32_t* next_root, hipStream_t stream);
 
 /* Host-only helper: the constants the sampling weights use for temperature T
  * (c = fp32(log2(e)/T) and a[0..6] = fp32((ln 2)^n / n!)).  No GPU needed. */

@@ -114,6 +114,19 @@ def test_host_validation_rejects_bad_arguments():
                                          fake, fake, None) == 1               # null logits
     assert lib.ddtree_verify_sample_lazy(ctypes.byref(t), fake, 1, 64 * 32768 + 1, 0.7, fake,
                                          fake, fake, fake, fake, None) == 2
+    # commit (tree, accept_len, path_nodes, bonus, k/v tree, Hkv, Dh, dtype, k/v cache,
+    # cache_base, cache_rows, capacity, next_prefix_len, next_root, stream)
+    cm = [ctypes.byref(t), fake, fake, fake, fake, fake]
+    tail = [fake, fake, fake, 100, 50, fake, fake, None]
+    assert lib.ddtree_commit(ctypes.byref(t), None, *cm[2:], 8, 128, 1, *tail) == 1
+    assert lib.ddtree_commit(*cm, 0, 128, 1, *tail) == 1                 # Hkv < 1
+    assert lib.ddtree_commit(*cm, 8, 128, 4, *tail) == 1                 # dtype
+    assert lib.ddtree_commit(*cm, 1, 4, 1, *tail) == 2                   # 8-byte rows
+    assert lib.ddtree_commit(*cm, 8, 128, 1, fake, fake, fake, -1, 50, fake, fake, None) == 1
+    assert lib.ddtree_commit(*cm, 8, 128, 1, fake, fake, fake, 100, -1, fake, fake, None) == 1
+    assert lib.ddtree_commit(*cm, 8, 128, 1, fake, fake, fake, 100, 50, None, fake, None) == 1
+    assert lib.ddtree_commit(*cm, 8, 128, 1, ctypes.c_void_p(24), fake, fake, 100, 50, fake,
+                             fake, None) == 1                            # misaligned cache
     # attention
     offs = (ctypes.c_int32 * 2)(0, 64)
     args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]

@@ -53,10 +53,12 @@ lib.ddtree_verify_sample_lazy.argtypes = [_tp, _vp, ctypes.c_int, _i32, _f32, _v
                                           _vp, _vp]
 lib.ddtree_verify_linear_sample.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
                                             _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
+lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_int, _vp, _vp, _vp,
+                              ctypes.c_int64, _i32, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
-           "ddtree_verify_linear_sample", "ddtree_sampling_constants"):
+           "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.ddtree_last_error.restype = ctypes.c_char_p
 lib.ddtree_version.restype = ctypes.c_char_p
@@ -322,6 +324,41 @@ def ddtree_verify_linear_sample(target_logits, draft_logits, draft_tokens, tempe
         float(temperature), _ptr(uniforms), _ptr(o["accept_len"]), _ptr(o["out_tokens"]),
         _ptr(o["bonus"]), _stream(stream)))
     return o
+
+
+def ddtree_commit(tree, walk, k_tree, v_tree, k_cache, v_cache, cache_base, capacity,
+                  next_prefix_len=None, next_root=None, stream=None):
+    """Write the accepted path's K/V rows into the cache (in place).
+
+    walk: a verify walk's outputs (accept_len, path_nodes, bonus); k_tree, v_tree
+    [B, N, Hkv, Dh]; k_cache, v_cache [rows, Hkv, Dh] of the same dtype;
+    cache_base int64 [B] (row of position 0 of each request).  Returns
+    (next_prefix_len, next_root), int32 [B]."""
+    B, N = tree.B, tree.N
+    _dev(k_tree, "k_tree", (torch.bfloat16, torch.float32))
+    if k_tree.dim() != 4 or tuple(k_tree.shape[:2]) != (B, N):
+        raise ValueError(f"k_tree has shape {tuple(k_tree.shape)}, expected ({B}, {N}, Hkv, Dh)")
+    Hkv, Dh = int(k_tree.shape[2]), int(k_tree.shape[3])
+    _dev(v_tree, "v_tree", k_tree.dtype, tuple(k_tree.shape))
+    _dev(k_cache, "k_cache", k_tree.dtype)
+    if k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (Hkv, Dh):
+        raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected (rows, {Hkv}, {Dh})")
+    _dev(v_cache, "v_cache", k_tree.dtype, tuple(k_cache.shape))
+    _dev(cache_base, "cache_base", torch.int64, (B,))
+    _dev(walk["accept_len"], "accept_len", torch.int32, (B,))
+    _dev(walk["path_nodes"], "path_nodes", torch.int32, (B, tree.D + 1))
+    _dev(walk["bonus"], "bonus", torch.int32, (B,))
+    dev = k_tree.device
+    if next_prefix_len is None:
+        next_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev)
+    if next_root is None:
+        next_root = torch.empty((B,), dtype=torch.int32, device=dev)
+    _check(lib.ddtree_commit(tree.cstruct, _ptr(walk["accept_len"]), _ptr(walk["path_nodes"]),
+                             _ptr(walk["bonus"]), _ptr(k_tree), _ptr(v_tree), Hkv, Dh,
+                             _dtype_code(k_tree), _ptr(k_cache), _ptr(v_cache), _ptr(cache_base),
+                             int(k_cache.shape[0]), int(capacity), _ptr(next_prefix_len),
+                             _ptr(next_root), _stream(stream)))
+    return next_prefix_len, next_root
 
 
 def ddtree_sampling_constants(temperature):
