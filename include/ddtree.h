@@ -13,7 +13,8 @@
  *   ddtree_build           per-depth draft top-k  ->  best-first token tree
  *   ddtree_tree_attention  every tree node attends to its request's context
  *                          (streamed from HBM once, shared by all nodes) and
- *                          to its own ancestors
+ *                          to its own ancestors (ddtree_tree_attention_ranges:
+ *                          the same with per-request context row ranges)
  *   ddtree_vocab_reduce    per-node argmax / max / log-sum-exp and, for
  *                          sampling, the exact integer softmax total R
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
@@ -173,6 +174,39 @@ ddtree_status ddtree_tree_attention(const void* q, const void* k_ctx, const void
                                     const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh,
                                     ddtree_dtype dtype, float scale, void* out, float* lse,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ddtree_tree_attention_ranges -- the same tree attention with each request's
+ * context given as a (start, length) range of rows instead of packed offsets,
+ * so that a batch can keep its caches in per-request slabs that grow in place
+ * (ddtree_commit appends the accepted path at row cache_base[b] + position;
+ * the next step then passes ctx_start = cache_base, ctx_len = next_prefix_len).
+ * Source: as ddtree_tree_attention; "Dissecting DDTree's Tree-Parallel
+ * Evaluation Strategy", Section 2 (the cache that later steps read once grows
+ * by the committed tokens).
+ *   ctx_start, ctx_len  [B] int32 device: request b's context is rows
+ *                [ctx_start[b], ctx_start[b] + ctx_len[b]) of k_ctx / v_ctx
+ *                (ranges may leave gaps; rows outside every range are not read)
+ *   ctx_start_host, ctx_len_host  the same values in host memory (the split
+ *                plan is made on the host)
+ *   workspace    ddtree_tree_attention_ranges_workspace_size(...) bytes
+ * Every other argument, the outputs and the numerics are those of
+ * ddtree_tree_attention.
+ * Errors: as ddtree_tree_attention; DDTREE_EINVAL also for a negative start or
+ *         length, or start + length beyond INT32_MAX.
+ */
+size_t ddtree_tree_attention_ranges_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                                   int32_t Dh, const int32_t* ctx_len_host);
+
+ddtree_status ddtree_tree_attention_ranges(const void* q, const void* k_ctx, const void* v_ctx,
+                                           const int32_t* ctx_start, const int32_t* ctx_len,
+                                           const int32_t* ctx_start_host,
+                                           const int32_t* ctx_len_host, const void* k_tree,
+                                           const void* v_tree, const ddtree_tree* tree,
+                                           int32_t Hq, int32_t Hkv, int32_t Dh,
+                                           ddtree_dtype dtype, float scale, void* out,
+                                           float* lse, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
 
 /*
  * ddtree_vocab_reduce -- one pass over the target logits of every tree node.

@@ -127,6 +127,15 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.ddtree_commit(*cm, 8, 128, 1, fake, fake, fake, 100, 50, None, fake, None) == 1
     assert lib.ddtree_commit(*cm, 8, 128, 1, ctypes.c_void_p(24), fake, fake, 100, 50, fake,
                              fake, None) == 1                            # misaligned cache
+    # attention, range form
+    st1, ln1, lnbad = (ctypes.c_int32 * 1)(0), (ctypes.c_int32 * 1)(64), (ctypes.c_int32 * 1)(-1)
+    rg = [fake, fake, fake, fake, fake]
+    assert lib.ddtree_tree_attention_ranges(*rg, st1, lnbad, fake, fake, ctypes.byref(t), 4, 4, 64,
+                                            1, 0.125, fake, None, None, 0, None) == 1
+    assert lib.ddtree_tree_attention_ranges(*rg, None, ln1, fake, fake, ctypes.byref(t), 4, 4, 64,
+                                            1, 0.125, fake, None, None, 0, None) == 1
+    assert lib.ddtree_tree_attention_ranges(*rg, st1, ln1, fake, fake, ctypes.byref(t), 4, 4, 96,
+                                            1, 0.125, fake, None, None, 0, None) == 2
     # attention
     offs = (ctypes.c_int32 * 2)(0, 64)
     args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]
@@ -148,6 +157,11 @@ def test_workspace_sizes_are_host_only_and_sane():
     ws = t.ddtree_tree_attention_workspace_size(1, 33, 8, 8, 128, offs)
     assert ws > 0 and ws % 4 == 0
     assert t.ddtree_tree_attention_workspace_size(1, 9, 4, 4, 96, offs) == 0
+    # the range form sizes its workspace from the lengths alone
+    lens = np.array([300, 0, 5000, 64], np.int32)
+    packed = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    assert t.ddtree_tree_attention_ranges_workspace_size(4, 33, 8, 2, 128, lens) == \
+        t.ddtree_tree_attention_workspace_size(4, 33, 8, 2, 128, packed) > 0
     assert t.ddtree_vocab_reduce_workspace_size(1, 33, 163840) > 0
     assert t.ddtree_vocab_reduce_workspace_size(64, 33, 163840) == 0
     # draft top-k: slices of 1024..8192 elements, K keys and one (max, sum) pair each

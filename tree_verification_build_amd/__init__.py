@@ -1,7 +1,7 @@
 """libddtree: the DDTree tree-verify step on AMD MI355X (gfx950).
 
 Thin ctypes binding over the C-ABI in include/ddtree.h.  The functions carry
-the C names (ddtree_draft_topk, ddtree_build, ddtree_tree_attention,
+the C names (ddtree_draft_topk, ddtree_build, ddtree_tree_attention[_ranges],
 ddtree_vocab_reduce, ddtree_verify_greedy, ddtree_verify_sample,
 ddtree_verify_sample_lazy, ddtree_verify_linear_sample, ddtree_commit); they only check and marshal
 arguments -- torch tensors on the GPU in, device pointers and the current
@@ -13,7 +13,8 @@ from ._lib import (  # noqa: F401
     DDTREE_BF16, DDTREE_F32, DdtreeError, Tree, alloc_tree, ddtree_build, ddtree_commit,
     ddtree_draft_topk,
     ddtree_draft_topk_workspace_size, ddtree_last_error,
-    ddtree_sampling_constants, ddtree_tree_attention, ddtree_tree_attention_workspace_size,
+    ddtree_sampling_constants, ddtree_tree_attention, ddtree_tree_attention_ranges,
+    ddtree_tree_attention_ranges_workspace_size, ddtree_tree_attention_workspace_size,
     ddtree_verify_greedy, ddtree_verify_linear_sample, ddtree_verify_sample,
     ddtree_verify_sample_lazy, ddtree_version,
     ddtree_vocab_reduce,

@@ -42,6 +42,11 @@ lib.ddtree_tree_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i3
 lib.ddtree_tree_attention_workspace_size.restype = _sz
 lib.ddtree_tree_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32, _i32,
                                       ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp]
+lib.ddtree_tree_attention_ranges_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp]
+lib.ddtree_tree_attention_ranges_workspace_size.restype = _sz
+lib.ddtree_tree_attention_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32,
+                                             _i32, _i32, ctypes.c_int, _f32, _vp, _vp, _vp, _sz,
+                                             _vp]
 lib.ddtree_vocab_reduce_workspace_size.argtypes = [_i32, _i32, _i32]
 lib.ddtree_vocab_reduce_workspace_size.restype = _sz
 lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp,
@@ -56,7 +61,8 @@ lib.ddtree_verify_linear_sample.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, 
 lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_int, _vp, _vp, _vp,
                               ctypes.c_int64, _i32, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
-for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention", "ddtree_vocab_reduce",
+for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
+           "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
            "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
@@ -215,6 +221,48 @@ def ddtree_tree_attention(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), hptr, _ptr(k_tree), _ptr(v_tree),
         tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), float(scale), _ptr(out), _ptr(lse),
         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def ddtree_tree_attention_ranges_workspace_size(B, N, Hq, Hkv, Dh, ctx_len_host) -> int:
+    a, p = _host_offsets(ctx_len_host)
+    return int(lib.ddtree_tree_attention_ranges_workspace_size(B, N, Hq, Hkv, Dh, p))
+
+
+def ddtree_tree_attention_ranges(q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_host,
+                                 ctx_len_host, k_tree, v_tree, tree, scale=None, out=None,
+                                 want_lse=False, workspace=None, stream=None):
+    """Tree attention with request b's context = rows [ctx_start[b], ctx_start[b] +
+    ctx_len[b]) of k_ctx / v_ctx.  Returns (out [B, N, Hq, Dh], lse or None)."""
+    B, N, Hq, Dh = q.shape
+    Hkv = k_tree.shape[2]
+    _dev(q, "q", (torch.bfloat16, torch.float32))
+    _dev(k_tree, "k_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(v_tree, "v_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(k_ctx, "k_ctx", q.dtype)
+    _dev(v_ctx, "v_ctx", q.dtype, tuple(k_ctx.shape))
+    _dev(ctx_start, "ctx_start", torch.int32, (B,))
+    _dev(ctx_len, "ctx_len", torch.int32, (B,))
+    hs, hsp = _host_offsets(ctx_start_host)
+    hl, hlp = _host_offsets(ctx_len_host)
+    if hs.shape != (B,) or hl.shape != (B,):
+        raise ValueError("ctx_start_host / ctx_len_host must hold B values")
+    end = int((hs.astype(np.int64) + hl).max()) if B else 0
+    if k_ctx.shape[0] < end or tuple(k_ctx.shape[1:]) != (Hkv, Dh):
+        raise ValueError(f"k_ctx must be [>= {end}, {Hkv}, {Dh}]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype, tuple(q.shape))
+    lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device) if want_lse else None
+    need = int(lib.ddtree_tree_attention_ranges_workspace_size(B, N, Hq, Hkv, Dh, hlp))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    if scale is None:
+        scale = 1.0 / float(Dh) ** 0.5
+    _check(lib.ddtree_tree_attention_ranges(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len), hsp, hlp,
+        _ptr(k_tree), _ptr(v_tree), tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), float(scale),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 

@@ -28,6 +28,7 @@
 // fp32 uses v_mfma_f32_16x16x4_f32.
 #include <algorithm>
 #include <cstdlib>
+#include <vector>
 
 #include "common.hpp"
 
@@ -51,7 +52,9 @@ struct AttnArgs {
   const void* q;
   const void* k_ctx;
   const void* v_ctx;
-  const int32_t* ctx_offsets;
+  const int32_t* ctx_offsets;   // [B+1] packed context ranges, or null when ctx_start is set
+  const int32_t* ctx_start;     // [B] first context row of each request (range form), or null
+  const int32_t* ctx_len;       // [B] context length of each request (range form)
   const void* k_tree;
   const void* v_tree;
   const uint64_t* vis;
@@ -65,10 +68,11 @@ struct AttnArgs {
                       // (bf16 from the DMA kernel, fp32 from the register kernel)
   float2* ws_ml;      // [total_splits * Hkv, M] (running max in log2 units, sum)
   // split plan for B <= kTabMax (tab_n = B, else 0): request b owns splits
-  // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b+1])
+  // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b] + tab_len[b])
   int tab_n;
   int tab_split0[kTabMax + 1];
-  int tab_off[kTabMax + 1];
+  int tab_off[kTabMax];
+  int tab_len[kTabMax];
 };
 
 // ------------------------------------------------------------------ dtype policies
@@ -214,10 +218,22 @@ struct SplitItem {
   int b, split, nsplit, ctx0, len;
 };
 
+// Context rows of request bb: [*off, *off + *L), from the packed offsets or
+// from the per-request (start, length) ranges.
+__device__ __forceinline__ void ctx_range(const AttnArgs& a, int bb, int* off, int* L) {
+  if (a.ctx_start) {
+    *off = a.ctx_start[bb];
+    *L = a.ctx_len[bb];
+  } else {
+    *off = a.ctx_offsets[bb];
+    *L = a.ctx_offsets[bb + 1] - *off;
+  }
+}
+
 // Which request owns split `sid` (splits are numbered request by request,
 // ceil(L_b / SK) of them, at least one).  For up to kTabMax requests the host
-// passes the split and context offsets in the kernel arguments; otherwise
-// wave 0 searches ctx_offsets and publishes the result in LDS.
+// passes the split plan and context ranges in the kernel arguments; otherwise
+// wave 0 searches the context ranges and publishes the result in LDS.
 __device__ __forceinline__ void find_split(const AttnArgs& a, int sid, int SK, int lane,
                                            SplitItem* out);
 
@@ -228,7 +244,7 @@ __device__ __forceinline__ SplitItem lookup_split(const AttnArgs& a, int sid, in
     while (b + 1 < a.tab_n && sid >= a.tab_split0[b + 1]) ++b;
     if (sid >= a.tab_split0[a.tab_n]) return SplitItem{-1, 0, 0, 0, 0};
     return SplitItem{b, sid - a.tab_split0[b], a.tab_split0[b + 1] - a.tab_split0[b], a.tab_off[b],
-                     a.tab_off[b + 1] - a.tab_off[b]};
+                     a.tab_len[b]};
   }
   if (wave == 0) find_split(a, sid, a.split_keys, lane, shared_item);
   __syncthreads();
@@ -242,8 +258,7 @@ __device__ __forceinline__ void find_split(const AttnArgs& a, int sid, int SK, i
     const int bb = b0 + lane;
     int nb = 0, off = 0, L = 0;
     if (bb < a.B) {
-      off = a.ctx_offsets[bb];
-      L = a.ctx_offsets[bb + 1] - off;
+      ctx_range(a, bb, &off, &L);
       nb = L > 0 ? (L + SK - 1) / SK : 1;
     }
     int incl = nb;
@@ -753,7 +768,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   } else {
     const int SK = a.split_keys;
     auto nsplits = [&](int bb) {
-      const int L = a.ctx_offsets[bb + 1] - a.ctx_offsets[bb];
+      int off, L;
+      ctx_range(a, bb, &off, &L);
       return L > 0 ? (L + SK - 1) / SK : 1;
     };
     ns = nsplits(b);
@@ -849,8 +865,9 @@ int keys_per_tile(ddtree_dtype dt, int Dh, int /*qb*/) {
 // Keys per split: about `target` workgroups over the whole context (two per CU),
 // at least 256 keys (a few tiles, so each workgroup keeps loads in flight) and
 // at most 2048 (bounds the imbalance of ragged batches); whole tiles.
-int plan_split_keys(const int32_t* offs_host, int B, int Hkv, int kt) {
-  long total = static_cast<long>(offs_host[B]) - offs_host[0];
+int plan_split_keys(const int32_t* lens, int B, int Hkv, int kt) {
+  long total = 0;
+  for (int b = 0; b < B; ++b) total += lens[b];
   int target = 512;
   if (const char* env = std::getenv("DDTREE_ATTN_TARGET_WGS")) target = std::max(1, atoi(env));
   long sk = (total * Hkv + target - 1) / target;
@@ -864,11 +881,11 @@ int plan_split_keys(const int32_t* offs_host, int B, int Hkv, int kt) {
   return static_cast<int>(std::min<long>(sk, 1L << 30));
 }
 
-int count_splits(const int32_t* offs_host, int B, int sk, bool* any_multi) {
+int count_splits(const int32_t* lens, int B, int sk, bool* any_multi) {
   int tot = 0;
   *any_multi = false;
   for (int b = 0; b < B; ++b) {
-    const int L = offs_host[b + 1] - offs_host[b];
+    const int L = lens[b];
     const int nb = L > 0 ? (L + sk - 1) / sk : 1;
     *any_multi |= nb > 1;
     tot += nb;
@@ -924,22 +941,14 @@ void launch_dma(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
   }
 }
 
-}  // namespace
-}  // namespace ddt
-
-extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
-                                                       int32_t Hkv, int32_t Dh,
-                                                       const int32_t* ctx_offsets_host) {
-  using namespace ddt;
-  if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_offsets_host || (Dh != 64 && Dh != 128))
-    return 0;
+size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const int32_t* lens) {
   const int M = N * (Hq / Hkv);
   const int qb = (M + 15) / 16;
   size_t best = 0;
   for (ddtree_dtype dt : {DDTREE_BF16, DDTREE_F32}) {
-    const int sk = plan_split_keys(ctx_offsets_host, B, Hkv, keys_per_tile(dt, Dh, qb));
+    const int sk = plan_split_keys(lens, B, Hkv, keys_per_tile(dt, Dh, qb));
     bool multi;
-    const int tot = count_splits(ctx_offsets_host, B, sk, &multi);
+    const int tot = count_splits(lens, B, sk, &multi);
     if (!multi) continue;
     const size_t need = static_cast<size_t>(tot) * Hkv * M * (Dh * sizeof(float) + sizeof(float2));
     best = std::max(best, need);
@@ -947,50 +956,43 @@ extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int
   return best;
 }
 
-extern "C" ddtree_status ddtree_tree_attention(
-    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_offsets,
-    const int32_t* ctx_offsets_host, const void* k_tree, const void* v_tree,
-    const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
-    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-    hipStream_t stream) {
-  using namespace ddt;
-  ddtree_status st = check_tree(tree, "ddtree_tree_attention");
-  if (st != DDTREE_OK) return st;
-  if (!q || !k_tree || !v_tree || !ctx_offsets || !ctx_offsets_host || !out)
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: null pointer");
+// Shared body of the packed-offset and range forms.  starts/lens: host copies
+// of the context ranges (validated by the caller); a.ctx_offsets or
+// a.ctx_start/ctx_len already set to the device arrays.
+ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const void* k_ctx,
+                             const void* v_ctx, const int32_t* starts, const int32_t* lens,
+                             const void* k_tree, const void* v_tree, const ddtree_tree* tree,
+                             int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale,
+                             void* out, float* lse, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!q || !k_tree || !v_tree || !out) return fail(DDTREE_EINVAL, "%s: null pointer", who);
   if (dtype != DDTREE_BF16 && dtype != DDTREE_F32)
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: unknown dtype %d", static_cast<int>(dtype));
+    return fail(DDTREE_EINVAL, "%s: unknown dtype %d", who, static_cast<int>(dtype));
   if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: Hq=%d must be a multiple of Hkv=%d", Hq, Hkv);
+    return fail(DDTREE_EINVAL, "%s: Hq=%d must be a multiple of Hkv=%d", who, Hq, Hkv);
   if (Dh != 64 && Dh != 128)
-    return fail(DDTREE_EUNSUPPORTED, "ddtree_tree_attention: head_dim %d (supported: 64, 128)", Dh);
+    return fail(DDTREE_EUNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", who, Dh);
   if (!(scale > 0.0f) || !(scale < __builtin_huge_valf()))
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: scale must be > 0 and finite");
+    return fail(DDTREE_EINVAL, "%s: scale must be > 0 and finite", who);
   const int B = tree->B, N = tree->N;
   const int M = N * (Hq / Hkv);
   if (M > 1024)
-    return fail(DDTREE_EUNSUPPORTED,
-                "ddtree_tree_attention: %d query rows per KV head (N * Hq / Hkv) exceed 1024", M);
-  if (ctx_offsets_host[0] != 0)
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: ctx_offsets[0] must be 0");
-  for (int b = 0; b < B; ++b)
-    if (ctx_offsets_host[b + 1] < ctx_offsets_host[b])
-      return fail(DDTREE_EINVAL, "ddtree_tree_attention: ctx_offsets must be non-decreasing");
-  if (ctx_offsets_host[B] > 0 && (!k_ctx || !v_ctx))
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: null context K/V");
+    return fail(DDTREE_EUNSUPPORTED, "%s: %d query rows per KV head (N * Hq / Hkv) exceed 1024",
+                who, M);
+  long total = 0;
+  for (int b = 0; b < B; ++b) total += lens[b];
+  if (total > 0 && (!k_ctx || !v_ctx)) return fail(DDTREE_EINVAL, "%s: null context K/V", who);
   if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
       (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)))
-    return fail(DDTREE_EINVAL, "ddtree_tree_attention: tensors must be 16-byte aligned");
+    return fail(DDTREE_EINVAL, "%s: tensors must be 16-byte aligned", who);
   const int qb = (std::min(M, 128) + 15) / 16;   // 16-row query blocks per slice
   const int kt = keys_per_tile(dtype, Dh, qb);
-  const int sk = plan_split_keys(ctx_offsets_host, B, Hkv, kt);
+  const int sk = plan_split_keys(lens, B, Hkv, kt);
   bool multi;
-  const int total = count_splits(ctx_offsets_host, B, sk, &multi);
-  AttnArgs a;
+  const int splits = count_splits(lens, B, sk, &multi);
   a.q = q;
   a.k_ctx = k_ctx;
   a.v_ctx = v_ctx;
-  a.ctx_offsets = ctx_offsets;
   a.k_tree = k_tree;
   a.v_tree = v_tree;
   a.vis = tree->vis;
@@ -1009,33 +1011,32 @@ extern "C" ddtree_status ddtree_tree_attention(
     a.tab_n = B;
     int acc = 0;
     for (int b = 0; b < B; ++b) {
-      const int L = ctx_offsets_host[b + 1] - ctx_offsets_host[b];
       a.tab_split0[b] = acc;
-      a.tab_off[b] = ctx_offsets_host[b];
-      acc += L > 0 ? (L + sk - 1) / sk : 1;
+      a.tab_off[b] = starts[b];
+      a.tab_len[b] = lens[b];
+      acc += lens[b] > 0 ? (lens[b] + sk - 1) / sk : 1;
     }
     a.tab_split0[B] = acc;
-    a.tab_off[B] = ctx_offsets_host[B];
   }
   a.out = out;
   a.lse = lse;
   a.ws_o = nullptr;
   a.ws_ml = nullptr;
   if (multi) {
-    const size_t need = static_cast<size_t>(total) * Hkv * M * Dh * sizeof(float);
-    const size_t need_ml = static_cast<size_t>(total) * Hkv * M * sizeof(float2);
+    const size_t need = static_cast<size_t>(splits) * Hkv * M * Dh * sizeof(float);
+    const size_t need_ml = static_cast<size_t>(splits) * Hkv * M * sizeof(float2);
     if (!workspace || workspace_bytes < need + need_ml || !aligned16(workspace))
-      return fail(DDTREE_EINVAL, "ddtree_tree_attention: workspace of %zu bytes needed, got %zu",
+      return fail(DDTREE_EINVAL, "%s: workspace of %zu bytes needed, got %zu", who,
                   need + need_ml, workspace_bytes);
     a.ws_o = workspace;
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + need);
   }
   if (dtype == DDTREE_BF16) {
-    if (Dh == 128) launch_dma(qb, a, total, stream);
-    else launch_qb<PolicyBF16<64>>(qb, a, total, stream);
+    if (Dh == 128) launch_dma(qb, a, splits, stream);
+    else launch_qb<PolicyBF16<64>>(qb, a, splits, stream);
   } else {
-    if (Dh == 128) launch_qb<PolicyF32<128>>(qb, a, total, stream);
-    else launch_qb<PolicyF32<64>>(qb, a, total, stream);
+    if (Dh == 128) launch_qb<PolicyF32<128>>(qb, a, splits, stream);
+    else launch_qb<PolicyF32<64>>(qb, a, splits, stream);
   }
   if (multi) {
     const dim3 g(B * Hkv, M);
@@ -1048,5 +1049,83 @@ extern "C" ddtree_status ddtree_tree_attention(
       else hipLaunchKernelGGL((combine_kernel<float, float, 64>), g, dim3(256), 0, stream, a);
     }
   }
-  return check_launch("ddtree_tree_attention");
+  return check_launch(who);
+}
+
+}  // namespace
+}  // namespace ddt
+
+extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
+                                                       int32_t Hkv, int32_t Dh,
+                                                       const int32_t* ctx_offsets_host) {
+  using namespace ddt;
+  if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_offsets_host || (Dh != 64 && Dh != 128))
+    return 0;
+  std::vector<int32_t> lens(B);
+  for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_offsets_host[b + 1] - ctx_offsets_host[b]);
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data());
+}
+
+extern "C" size_t ddtree_tree_attention_ranges_workspace_size(int32_t B, int32_t N, int32_t Hq,
+                                                              int32_t Hkv, int32_t Dh,
+                                                              const int32_t* ctx_len_host) {
+  using namespace ddt;
+  if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_len_host || (Dh != 64 && Dh != 128))
+    return 0;
+  std::vector<int32_t> lens(B);
+  for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_len_host[b]);
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data());
+}
+
+extern "C" ddtree_status ddtree_tree_attention(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_offsets,
+    const int32_t* ctx_offsets_host, const void* k_tree, const void* v_tree,
+    const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
+    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  using namespace ddt;
+  const char* who = "ddtree_tree_attention";
+  ddtree_status st = check_tree(tree, who);
+  if (st != DDTREE_OK) return st;
+  if (!ctx_offsets || !ctx_offsets_host) return fail(DDTREE_EINVAL, "%s: null pointer", who);
+  const int B = tree->B;
+  if (ctx_offsets_host[0] != 0) return fail(DDTREE_EINVAL, "%s: ctx_offsets[0] must be 0", who);
+  for (int b = 0; b < B; ++b)
+    if (ctx_offsets_host[b + 1] < ctx_offsets_host[b])
+      return fail(DDTREE_EINVAL, "%s: ctx_offsets must be non-decreasing", who);
+  std::vector<int32_t> lens(B);
+  for (int b = 0; b < B; ++b) lens[b] = ctx_offsets_host[b + 1] - ctx_offsets_host[b];
+  AttnArgs a;
+  a.ctx_offsets = ctx_offsets;
+  a.ctx_start = nullptr;
+  a.ctx_len = nullptr;
+  return attention_impl(a, who, q, k_ctx, v_ctx, ctx_offsets_host, lens.data(), k_tree, v_tree,
+                        tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
+                        stream);
+}
+
+extern "C" ddtree_status ddtree_tree_attention_ranges(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_start,
+    const int32_t* ctx_len, const int32_t* ctx_start_host, const int32_t* ctx_len_host,
+    const void* k_tree, const void* v_tree, const ddtree_tree* tree, int32_t Hq, int32_t Hkv,
+    int32_t Dh, ddtree_dtype dtype, float scale, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  using namespace ddt;
+  const char* who = "ddtree_tree_attention_ranges";
+  ddtree_status st = check_tree(tree, who);
+  if (st != DDTREE_OK) return st;
+  if (!ctx_start || !ctx_len || !ctx_start_host || !ctx_len_host)
+    return fail(DDTREE_EINVAL, "%s: null pointer", who);
+  for (int b = 0; b < tree->B; ++b)
+    if (ctx_start_host[b] < 0 || ctx_len_host[b] < 0 ||
+        static_cast<long>(ctx_start_host[b]) + ctx_len_host[b] > INT32_MAX)
+      return fail(DDTREE_EINVAL, "%s: request %d: context start %d, length %d", who, b,
+                  ctx_start_host[b], ctx_len_host[b]);
+  AttnArgs a;
+  a.ctx_offsets = nullptr;
+  a.ctx_start = ctx_start;
+  a.ctx_len = ctx_len;
+  return attention_impl(a, who, q, k_ctx, v_ctx, ctx_start_host, ctx_len_host, k_tree, v_tree,
+                        tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
+                        stream);
 }
