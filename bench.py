@@ -254,7 +254,9 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
         next_prefix_len=nxt, next_root=nroot), reps)
     commit_rows = int(walk["accept_len"].sum().item()) + cfg.B
     commit_bytes = commit_rows * 2 * 2 * cfg.Hkv * cfg.Dh * base["k_tree"].element_size()
-    del sets, graphs
+    del sets
+    if graph:
+        del graphs
     lin = run_linear(cfg, inp, tok_all, stream) if T > 0 else None
     # the draft top-K over the D draft rows of each request (outside the step),
     # over enough copies that the last-level cache does not hold them
