@@ -21,6 +21,8 @@ Sources (blog pages on DDTree speculative decoding):
   * linear  -- Section 3 (linear DFlash at temperature T: accept with
                min(1, p_target / p_draft), else the residual) and "Mistakes and
                Incorrect Assumptions" (the draft's full probabilities are needed).
+  * topp    -- Section 3 (top_p threaded through to the verify walk): the
+               nucleus of the integer target law.
   * commit  -- Section 1 step 5 and its summary (the longest verified path is
                committed) and Section 2 (the context cache grows by the
                committed tokens and is read once by later steps).
@@ -40,7 +42,9 @@ from .vocab import vocab_reduce, weight_constants, weights
 from .verify import verify_greedy, verify_sample
 from .linear import verify_linear_sample
 from .commit import commit_path
+from .topp import keep_mask, nucleus_row, top_p_fixed, vocab_top_p
 
 __all__ = ["attach_draft_topk", "draft_topk", "log_sum_exp", "build_tree", "N_WORDS", "tree_attention", "to_f64",
            "vocab_reduce", "weight_constants", "weights", "verify_greedy", "verify_sample",
-           "verify_linear_sample", "commit_path"]
+           "verify_linear_sample", "commit_path", "keep_mask", "nucleus_row", "top_p_fixed",
+           "vocab_top_p"]

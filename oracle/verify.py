@@ -79,12 +79,26 @@ def _row_f32(logits, b, n, dtype):
 
 
 def verify_sample(tree: dict, logits, maxv, R, temperature: float, uniforms, D: int,
-                  dtype: str = "f32") -> dict:
+                  dtype: str = "f32", nucleus=None) -> dict:
     """Tree rejection sampling.  logits [B, N, V]; maxv, R from the vocabulary step;
-    uniforms u64 [B, N, 2].  Same outputs as verify_greedy."""
+    uniforms u64 [B, N, 2].  Same outputs as verify_greedy.
+
+    nucleus: optional (thr_w, thr_id) [B, N] from the top-p oracle; a token then
+    weighs w inside its row's kept set and 0 outside, and R must be the kept
+    totals R_p ("Dissecting DDTree's Tree-Parallel Evaluation Strategy",
+    Section 3: top_p threaded through to the verify walk)."""
     if not temperature > 0:
         raise ValueError("verify_sample needs temperature > 0")
     c, a = weight_constants(temperature)
+
+    def wsel(row, ids, b, n):
+        w = weights(row[ids], maxv[b, n], c, a)
+        if nucleus is None:
+            return w
+        tw, ti = np.uint64(nucleus[0][b, n]), int(nucleus[1][b, n])
+        keep = (w > tw) | ((w == tw) & (np.asarray(ids) <= ti))
+        return np.where(keep, w, np.uint64(0))
+
     B = tree["token"].shape[0]
     res = _outputs(B, D)
     for b in range(B):
@@ -97,7 +111,7 @@ def verify_sample(tree: dict, logits, maxv, R, temperature: float, uniforms, D: 
             moved = False
             for ch in _children(tree, b, cur):
                 tok = int(tree["token"][b, ch])
-                wc = int(weights(row[tok:tok + 1], maxv[b, cur], c, a)[0])
+                wc = int(wsel(row, np.array([tok]), b, cur)[0])
                 t = (int(uniforms[b, ch, 0]) * r_res) >> 64
                 if t < wc:
                     cur = ch
@@ -110,7 +124,7 @@ def verify_sample(tree: dict, logits, maxv, R, temperature: float, uniforms, D: 
                 rejected.append(tok)
             if moved:
                 continue
-            w = weights(row, maxv[b, cur], c, a)
+            w = wsel(row, np.arange(row.shape[0]), b, cur)
             w[rejected] = 0
             assert int(w.sum(dtype=np.uint64)) == r_res
             t = (int(uniforms[b, cur, 1]) * r_res) >> 64
