@@ -75,6 +75,9 @@ def set_host_wait(mode):
         return "auto"
 
 
+TOP_P = 0.9   # nucleus mass of the top-p figure (sampling workloads)
+
+
 def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     import torch
     import tree_verification_build_amd as lib
@@ -219,6 +222,44 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
             stream.synchronize()
         t_lazy = time.perf_counter() - t_start
 
+    # sampling workloads: the step with top-p (p = 0.9) nuclei: vocabulary pass, the
+    # per-node nucleus, then the walk on it; same synchronised loop
+    t_topp = None
+    if T > 0:
+        nuc = None
+
+        def step_topp(i):
+            nonlocal nuc
+            s = sets[i % rotate]
+            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                             small["prefix_len"], cfg.budget, tree=tree)
+            attention(s)
+            v = vocab(s)
+            nuc = lib.ddtree_vocab_top_p(s["logits"], tree.num_nodes, v["maxv"], v["R"], T,
+                                         TOP_P, outputs=nuc)
+            lib.ddtree_verify_sample_top_p(tree, s["logits"], v["maxv"], nuc, T,
+                                           small["uniforms"], outputs=outputs)
+        step_topp(0)                 # eager once: allocates the nucleus outputs
+        torch.cuda.synchronize()
+        run_topp = step_topp
+        if graph:
+            topp_graphs = []
+            for i in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step_topp(i)
+                topp_graphs.append(g)
+            run_topp = lambda i: topp_graphs[i % rotate].replay()  # noqa: E731
+        for i in range(warmup):
+            run_topp(i)
+            stream.synchronize()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            run_topp(i)
+            stream.synchronize()
+        t_topp = time.perf_counter() - t_start
+
     # kernel durations: a HIP graph of back-to-back calls over the rotated input sets,
     # replayed between two HIP events on this stream (no host gaps fall inside)
     def timed_calls(fn, reps):
@@ -281,7 +322,7 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     e1.record(stream)
     torch.cuda.synchronize()
     topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
-    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "linear": lin,
+    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "t_topp": t_topp, "linear": lin,
             "attn_ms": attn_ms, "vocab_ms": vocab_ms, "commit_ms": commit_ms,
             "commit_rows": commit_rows, "commit_bytes": commit_bytes,
             "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
@@ -511,6 +552,13 @@ def main():
             "ms_per_step": round(r["t_lazy"] / args.steps * 1e3, 4),
             "step": "build, attention, ddtree_verify_sample_lazy (target rows reduced only "
                     "where the walk goes; same outputs)"}
+    if r["t_topp"] is not None:
+        line["top_p_sampling_walk"] = {
+            "top_p": TOP_P,
+            "steps_per_s": round(args.steps / r["t_topp"], 2),
+            "ms_per_step": round(r["t_topp"] / args.steps * 1e3, 4),
+            "step": "build, attention, ddtree_vocab_reduce, ddtree_vocab_top_p, "
+                    "ddtree_verify_sample_top_p"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = run_cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -20,6 +20,8 @@
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
  *   ddtree_verify_sample_lazy  the same walk, reducing only the rows it visits
+ *   ddtree_vocab_top_p     per-node top-p nucleus of the integer target law
+ *   ddtree_verify_sample_top_p  the sampled walk on the top-p nuclei
  *   ddtree_verify_linear_sample  linear speculative sampling with draft probabilities
  *   ddtree_commit          the accepted path's K/V rows into the context cache;
  *                          the next step's prefix length and root token
@@ -313,6 +315,54 @@ ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, const void* log
                                         const uint64_t* uniforms, int32_t* accept_len,
                                         int32_t* path_nodes, int32_t* out_tokens, int32_t* bonus,
                                         hipStream_t stream);
+
+/*
+ * ddtree_vocab_top_p -- the top-p (nucleus) truncation of every node's target
+ * law, for ddtree_verify_sample_top_p.
+ * Source: "Dissecting DDTree's Tree-Parallel Evaluation Strategy", Section 3
+ * (temperature and top_p threaded through to the verify walk).
+ * Readings: tokens are ordered by their integer weight w (see
+ * ddtree_vocab_reduce) descending, equal weights by id ascending; the nucleus
+ * is the shortest prefix whose weight sum S satisfies 2^32 * S >= P * R with
+ * P = rint(top_p * 2^32) clamped to [1, 2^32].  It is described by its last
+ * token (weight thr_w, id thr_id): a token is kept iff w > thr_w, or
+ * w == thr_w and id <= thr_id.
+ *   logits [B, N, V] dtype; num_nodes [B]; maxv, R [B, N] from
+ *   ddtree_vocab_reduce at the same temperature (temperature > 0)
+ *   top_p in (0, 1]
+ *   thr_w [B, N] uint64, thr_id [B, N] int32, Rp [B, N] uint64 (the kept
+ *   total), Rp_blocks [B, N, ceil(V / DDTREE_R_BLOCK)] uint64 (kept weight per
+ *   token block).  Padding rows: 0, -1, 0, 0.
+ * One 1024-thread workgroup per row; a few passes over the row and then an
+ * LDS-resident search while the candidates fit (8192 tokens), row passes
+ * otherwise.
+ * Errors: DDTREE_EINVAL (null pointers, sizes, temperature, top_p, dtype),
+ *         DDTREE_EUNSUPPORTED (V > 64 * DDTREE_R_BLOCK).
+ */
+ddtree_status ddtree_vocab_top_p(const void* logits, ddtree_dtype dtype, int32_t B, int32_t N,
+                                 int32_t V, const int32_t* num_nodes, const float* maxv,
+                                 const uint64_t* R, float temperature, float top_p,
+                                 uint64_t* thr_w, int32_t* thr_id, uint64_t* Rp,
+                                 uint64_t* Rp_blocks, hipStream_t stream);
+
+/*
+ * ddtree_verify_sample_top_p -- the sampled walk of ddtree_verify_sample on
+ * the rows' top-p nuclei: every weight outside its row's nucleus counts as 0
+ * (accept tests, residual totals and the residual draw alike).
+ * Source: as ddtree_verify_sample; "Dissecting DDTree's Tree-Parallel
+ * Evaluation Strategy", Section 3 (top_p threaded through to the walk).
+ *   maxv from ddtree_vocab_reduce; Rp, Rp_blocks, thr_w, thr_id from
+ *   ddtree_vocab_top_p; every other argument and output as ddtree_verify_sample.
+ * Errors: as ddtree_verify_sample.
+ */
+ddtree_status ddtree_verify_sample_top_p(const ddtree_tree* tree, const void* logits,
+                                         ddtree_dtype dtype, int32_t V, const float* maxv,
+                                         const uint64_t* Rp, const uint64_t* Rp_blocks,
+                                         const uint64_t* thr_w, const int32_t* thr_id,
+                                         float temperature, const uint64_t* uniforms,
+                                         int32_t* accept_len, int32_t* path_nodes,
+                                         int32_t* out_tokens, int32_t* bonus,
+                                         hipStream_t stream);
 
 /*
  * ddtree_verify_linear_sample -- linear speculative sampling with the draft's

@@ -127,6 +127,19 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.ddtree_commit(*cm, 8, 128, 1, fake, fake, fake, 100, 50, None, fake, None) == 1
     assert lib.ddtree_commit(*cm, 8, 128, 1, ctypes.c_void_p(24), fake, fake, 100, 50, fake,
                              fake, None) == 1                            # misaligned cache
+    # top-p
+    tp = [fake, 1, 1, 9, 100, fake, fake, fake]
+    outs = [fake, fake, fake, fake, None]
+    assert lib.ddtree_vocab_top_p(*tp, 0.8, 0.0, *outs) == 1            # top_p <= 0
+    assert lib.ddtree_vocab_top_p(*tp, 0.8, 1.5, *outs) == 1            # top_p > 1
+    assert lib.ddtree_vocab_top_p(*tp, 0.0, 0.9, *outs) == 1            # T <= 0
+    assert lib.ddtree_vocab_top_p(fake, 1, 1, 9, 64 * 32768 + 1, fake, fake, fake, 0.8, 0.9,
+                                  *outs) == 2
+    assert lib.ddtree_vocab_top_p(None, *tp[1:], 0.8, 0.9, *outs) == 1
+    sv = [ctypes.byref(t), fake, 1, 100, fake, fake, fake, fake, fake]
+    wo = [fake, fake, fake, fake, fake, None]
+    assert lib.ddtree_verify_sample_top_p(*sv, 0.0, *wo) == 1            # T <= 0
+    assert lib.ddtree_verify_sample_top_p(*sv[:7], None, fake, 0.8, *wo) == 1   # thr_w missing
     # attention, range form
     st1, ln1, lnbad = (ctypes.c_int32 * 1)(0), (ctypes.c_int32 * 1)(64), (ctypes.c_int32 * 1)(-1)
     rg = [fake, fake, fake, fake, fake]

@@ -58,13 +58,18 @@ lib.ddtree_verify_sample_lazy.argtypes = [_tp, _vp, ctypes.c_int, _i32, _f32, _v
                                           _vp, _vp]
 lib.ddtree_verify_linear_sample.argtypes = [_vp, _vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp,
                                             _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp]
+lib.ddtree_vocab_top_p.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _f32, _f32,
+                                   _vp, _vp, _vp, _vp, _vp]
+lib.ddtree_verify_sample_top_p.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _vp, _vp,
+                                           _f32, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_int, _vp, _vp, _vp,
                               ctypes.c_int64, _i32, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
            "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
-           "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_sampling_constants"):
+           "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_vocab_top_p",
+           "ddtree_verify_sample_top_p", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.ddtree_last_error.restype = ctypes.c_char_p
 lib.ddtree_version.restype = ctypes.c_char_p
@@ -371,6 +376,47 @@ def ddtree_verify_linear_sample(target_logits, draft_logits, draft_tokens, tempe
         _ptr(target_stats["R_blocks"]), _ptr(draft_stats["maxv"]), _ptr(draft_stats["R"]),
         float(temperature), _ptr(uniforms), _ptr(o["accept_len"]), _ptr(o["out_tokens"]),
         _ptr(o["bonus"]), _stream(stream)))
+    return o
+
+
+def ddtree_vocab_top_p(logits, num_nodes, maxv, R, temperature, top_p, outputs=None,
+                       stream=None):
+    """Per node row: the top-p nucleus (thr_w, thr_id) and its totals (Rp, Rp_blocks)."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(num_nodes, "num_nodes", torch.int32, (B,))
+    _dev(maxv, "maxv", torch.float32, (B, N))
+    _dev(R, "R", torch.int64, (B, N))
+    dev = logits.device
+    nb = (V + R_BLOCK - 1) // R_BLOCK
+    o = outputs or {"thr_w": torch.empty((B, N), dtype=torch.int64, device=dev),
+                    "thr_id": torch.empty((B, N), dtype=torch.int32, device=dev),
+                    "Rp": torch.empty((B, N), dtype=torch.int64, device=dev),
+                    "Rp_blocks": torch.empty((B, N, nb), dtype=torch.int64, device=dev)}
+    _check(lib.ddtree_vocab_top_p(_ptr(logits), _dtype_code(logits), B, N, V, _ptr(num_nodes),
+                                  _ptr(maxv), _ptr(R), float(temperature), float(top_p),
+                                  _ptr(o["thr_w"]), _ptr(o["thr_id"]), _ptr(o["Rp"]),
+                                  _ptr(o["Rp_blocks"]), _stream(stream)))
+    return o
+
+
+def ddtree_verify_sample_top_p(tree, logits, maxv, nucleus, temperature, uniforms, outputs=None,
+                               stream=None):
+    """The sampled walk on the nuclei of ddtree_vocab_top_p (`nucleus`: its outputs)."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    _dev(maxv, "maxv", torch.float32, (B, N))
+    _dev(nucleus["Rp"], "Rp", torch.int64, (B, N))
+    _dev(nucleus["Rp_blocks"], "Rp_blocks", torch.int64, (B, N, (V + R_BLOCK - 1) // R_BLOCK))
+    _dev(nucleus["thr_w"], "thr_w", torch.int64, (B, N))
+    _dev(nucleus["thr_id"], "thr_id", torch.int32, (B, N))
+    _dev(uniforms, "uniforms", torch.int64, (B, N, 2))
+    o = outputs or _walk_outputs(tree)
+    _check(lib.ddtree_verify_sample_top_p(
+        tree.cstruct, _ptr(logits), _dtype_code(logits), V, _ptr(maxv), _ptr(nucleus["Rp"]),
+        _ptr(nucleus["Rp_blocks"]), _ptr(nucleus["thr_w"]), _ptr(nucleus["thr_id"]),
+        float(temperature), _ptr(uniforms), _ptr(o["accept_len"]), _ptr(o["path_nodes"]),
+        _ptr(o["out_tokens"]), _ptr(o["bonus"]), _stream(stream)))
     return o
 
 

@@ -110,13 +110,22 @@ __device__ __forceinline__ void load32(const T* row, long x0, int V, float (&v)[
 constexpr int kTokPerThread = DDTREE_R_BLOCK / kSampleThreads;
 static_assert(kTokPerThread == 32, "one weight block = 32 tokens per thread");
 
-template <typename T>
+// Top-p: a token is in its row's nucleus iff its weight exceeds the row's
+// threshold weight, or equals it and its id is at most the threshold id.
+__device__ __forceinline__ bool in_nucleus(uint64_t w, long x, uint64_t tw, int ti) {
+  return w > tw || (w == tw && x <= ti);
+}
+
+// NUC: the walk runs on the rows' top-p nuclei (R and Rb are then the kept
+// totals and block sums, thr_w / thr_id the rows' thresholds).
+template <typename T, bool NUC>
 __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     ddtree_tree t, const T* __restrict__ logits, int V, const float* __restrict__ maxv,
     const uint64_t* __restrict__ R, const uint64_t* __restrict__ Rb, WeightConsts wc,
     const uint64_t* __restrict__ uniforms, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ path_nodes, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ bonus) {
+    int32_t* __restrict__ bonus, const uint64_t* __restrict__ thr_w,
+    const int32_t* __restrict__ thr_id) {
   __shared__ uint64_t s_w[kMaxN], s_R[kMaxN], s_u0[kMaxN], s_u1[kMaxN];
   __shared__ int32_t s_tok[kMaxN], s_fc[kMaxN], s_ns[kMaxN];
   __shared__ int32_t s_rej[DDTREE_MAX_TOPK];
@@ -146,6 +155,9 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
         const int p = t.parent[base + j];
         const float l = Elem<T>::get(logits, (base + p) * static_cast<long>(V) + tk);
         w = weight(l, maxv[base + p], wc);
+        if constexpr (NUC) {
+          if (!in_nucleus(w, tk, thr_w[base + p], thr_id[base + p])) w = 0;
+        }
       }
     }
     s_w[j] = w;
@@ -228,16 +240,23 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const int cur = s_cur, nrej = s_nrej;
   const uint64_t trem = s_trem;
   const float m = maxv[base + cur];
+  const uint64_t tw = NUC ? thr_w[base + cur] : 0;
+  const int ti = NUC ? thr_id[base + cur] : 0;
+  auto wt = [&](float l, long x) -> uint64_t {
+    const uint64_t w = weight(l, m, wc);
+    if constexpr (NUC) return in_nucleus(w, x, tw, ti) ? w : 0;
+    return w;
+  };
   const T* row = logits + (base + cur) * static_cast<long>(V);
   const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
   float v[32];
   load32<T>(row, x0, V, v);
   uint64_t sum = 0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);   // -inf past V weighs 0
+  for (int e = 0; e < 32; ++e) sum += wt(v[e], x0 + e);   // -inf past V weighs 0
   for (int r = 0; r < nrej; ++r) {
     const long x = s_rej[r];
-    if (x >= x0 && x < x0 + 32) sum -= weight(v[x - x0], m, wc);   // rejected: excluded
+    if (x >= x0 && x < x0 + 32) sum -= wt(v[x - x0], x);   // rejected: excluded
   }
   const uint64_t incl = wave_incl_scan_u64(sum, lane);
   if (lane == kWave - 1) s_wave[wave] = incl;
@@ -252,7 +271,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
       bool rej = false;
       for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x0 + e);
       if (rej) continue;
-      acc += weight(Elem<T>::get(row, x0 + e), m, wc);
+      acc += wt(Elem<T>::get(row, x0 + e), x0 + e);
       if (acc > trem) pick = static_cast<int>(x0) + e;
     }
     int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
@@ -755,17 +774,50 @@ extern "C" ddtree_status ddtree_verify_sample(const ddtree_tree* tree, const voi
                 kWave * DDTREE_R_BLOCK);
   const WeightConsts wc = weight_consts(temperature);
   if (dtype == DDTREE_BF16) {
-    hipLaunchKernelGGL(sample_kernel<uint16_t>, dim3(tree->B), dim3(kSampleThreads), 0, stream,
-                       *tree, static_cast<const uint16_t*>(logits), V, maxv, R, R_blocks, wc, uniforms,
-                       accept_len, path_nodes, out_tokens, bonus);
+    hipLaunchKernelGGL((sample_kernel<uint16_t, false>), dim3(tree->B), dim3(kSampleThreads), 0,
+                       stream, *tree, static_cast<const uint16_t*>(logits), V, maxv, R, R_blocks,
+                       wc, uniforms, accept_len, path_nodes, out_tokens, bonus, nullptr, nullptr);
   } else if (dtype == DDTREE_F32) {
-    hipLaunchKernelGGL(sample_kernel<float>, dim3(tree->B), dim3(kSampleThreads), 0, stream,
-                       *tree, static_cast<const float*>(logits), V, maxv, R, R_blocks, wc, uniforms,
-                       accept_len, path_nodes, out_tokens, bonus);
+    hipLaunchKernelGGL((sample_kernel<float, false>), dim3(tree->B), dim3(kSampleThreads), 0,
+                       stream, *tree, static_cast<const float*>(logits), V, maxv, R, R_blocks, wc,
+                       uniforms, accept_len, path_nodes, out_tokens, bonus, nullptr, nullptr);
   } else {
     return fail(DDTREE_EINVAL, "ddtree_verify_sample: unknown dtype %d", static_cast<int>(dtype));
   }
   return check_launch("ddtree_verify_sample");
+}
+
+extern "C" ddtree_status ddtree_verify_sample_top_p(
+    const ddtree_tree* tree, const void* logits, ddtree_dtype dtype, int32_t V, const float* maxv,
+    const uint64_t* Rp, const uint64_t* Rp_blocks, const uint64_t* thr_w, const int32_t* thr_id,
+    float temperature, const uint64_t* uniforms, int32_t* accept_len, int32_t* path_nodes,
+    int32_t* out_tokens, int32_t* bonus, hipStream_t stream) {
+  using namespace ddt;
+  const char* who = "ddtree_verify_sample_top_p";
+  ddtree_status st = check_tree(tree, who);
+  if (st != DDTREE_OK) return st;
+  if (!logits || !maxv || !Rp || !Rp_blocks || !thr_w || !thr_id || !uniforms || !accept_len ||
+      !path_nodes || !out_tokens || !bonus)
+    return fail(DDTREE_EINVAL, "%s: null pointer", who);
+  if (!(temperature > 0.0f) || !(temperature < __builtin_huge_valf()))
+    return fail(DDTREE_EINVAL, "%s: temperature must be > 0 and finite", who);
+  if (V < 1) return fail(DDTREE_EINVAL, "%s: V must be >= 1", who);
+  if (V > kWave * DDTREE_R_BLOCK)
+    return fail(DDTREE_EUNSUPPORTED, "%s: V = %d exceeds %d", who, V, kWave * DDTREE_R_BLOCK);
+  const WeightConsts wc = weight_consts(temperature);
+  if (dtype == DDTREE_BF16) {
+    hipLaunchKernelGGL((sample_kernel<uint16_t, true>), dim3(tree->B), dim3(kSampleThreads), 0,
+                       stream, *tree, static_cast<const uint16_t*>(logits), V, maxv, Rp,
+                       Rp_blocks, wc, uniforms, accept_len, path_nodes, out_tokens, bonus, thr_w,
+                       thr_id);
+  } else if (dtype == DDTREE_F32) {
+    hipLaunchKernelGGL((sample_kernel<float, true>), dim3(tree->B), dim3(kSampleThreads), 0,
+                       stream, *tree, static_cast<const float*>(logits), V, maxv, Rp, Rp_blocks,
+                       wc, uniforms, accept_len, path_nodes, out_tokens, bonus, thr_w, thr_id);
+  } else {
+    return fail(DDTREE_EINVAL, "%s: unknown dtype %d", who, static_cast<int>(dtype));
+  }
+  return check_launch(who);
 }
 
 extern "C" ddtree_status ddtree_verify_sample_lazy(const ddtree_tree* tree, const void* logits,
