@@ -458,8 +458,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 // land at M0 + 16 * lane) into a ring of NS tile buffers, so that NS - 1 tiles
 // are in flight while one is computed and no registers are spent on staging.
 // Rows are stored whole (256 bytes) with their sixteen 16-byte chunks XOR-
-// swizzled by (row & 7), which keeps both the DMA writes and the MFMA operand
-// reads free of bank conflicts.  V stays row-major: the V^T operand of the
+// swizzled by the row index (kSwK / kSwV below), which spreads the DMA writes
+// and the MFMA operand reads over the LDS banks.  V stays row-major: the V^T operand of the
 // PV product comes from ds_read_b64_tr_b16, whose 16-lane transpose yields, for
 // lane (g, i), V[4g + k][d0 + i] (k = 0..3) when lane j of the 16 points at
 // row 4g + j/4, column d0 + 4 (j % 4) -- exactly the key order of the S^T
@@ -511,6 +511,13 @@ __device__ __forceinline__ float rows_sum(float x) {
 // more, so p = 2^(s - m) stays <= 2^8 and the rescale is rare.
 constexpr float kLagLog2 = 8.0f;
 
+// XOR swizzle masks of the LDS rows: a 64-lane ds_read_b128 is served 16 lanes
+// (256 bytes, all 64 banks) at a time, and the K reads' 16 lanes are 16
+// consecutive rows, so K rows swizzle by (row & 15) (with (row & 7), rows r and
+// r + 8 collided: measured 2.7 conflict cycles per LDS instruction, 1.3 now).
+// The V reads' lane groups span 8 rows; (row & 15) measured no different there.
+constexpr int kSwK = 15, kSwV = 7;
+
 template <int QB, int NW, int NS>
 __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   using elem = uint16_t;
@@ -550,7 +557,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
   for (int j = 0; j < DPW; ++j) {
     const int r = 4 * ((wave * DPW + j) & 15) + lrow;
-    loff[j] = r * rstride + ((lchunk ^ (r & 7)) * 8);
+    loff[j] = r * rstride + ((lchunk ^ (r & ((wave * DPW + j) >> 4 ? kSwV : kSwK))) * 8);
   }
 #define DDT_DMA_TILE(T_)                                                                        \
   do {                                                                                          \
@@ -573,7 +580,8 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
         const int r_ = 4 * rq_ + lrow;                                                          \
         const int key_ = min(base_ + r_, lim_);                                                 \
         const elem* src_ = (vp_ ? (ctx_ ? vc0 : vt0) : (ctx_ ? kc0 : kt0)) +                    \
-                           static_cast<long>(key_) * rstride + ((lchunk ^ (r_ & 7)) * 8);       \
+                           static_cast<long>(key_) * rstride +                                  \
+                           ((lchunk ^ (r_ & (vp_ ? kSwV : kSwK))) * 8);                         \
         dma16(src_, slot_ + static_cast<uint32_t>(vp_ * HALF + rq_ * 1024));                    \
       }                                                                                         \
     }                                                                                           \
@@ -634,7 +642,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 #pragma unroll
       for (int s = 0; s < QF; ++s) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & 7)) * 16));
+            kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & kSwK)) * 16));
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
       }
       sv[kb] = acc;
@@ -695,7 +703,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
         for (int hh = 0; hh < 2; ++hh) {
           const int row = 32 * j + 16 * hh + 4 * g + (l16 >> 2);
           const int chunk = 2 * db + ((l16 & 3) >> 1);
-          const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & 7)) * 16) + (l16 & 1) * 8;
+          const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & kSwV)) * 16) + (l16 & 1) * 8;
           h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
         }
         // whole-vector casts: element-wise bf16 inserts from the 16-bit lanes
