@@ -525,6 +525,7 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
   constexpr int HALF = KT * DH * 2;               // 16 KB: the K (or V) rows of a tile
   constexpr int TILE = 2 * HALF;
   constexpr int DPW = 32 / NW;                    // 1 KB DMA instructions per wave per tile
+  constexpr bool kHoist = NW == 4;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ SplitItem s_item;
   const uint32_t smem_base = static_cast<uint32_t>(reinterpret_cast<size_t>(
@@ -635,17 +636,67 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
     const unsigned char* kbuf = smem + (t % NS) * TILE;
     const unsigned char* vbuf = kbuf + HALF;
     f32x4_t sv[KB];
+    bf16x8_t vf[kHoist ? KT / 32 : 1][kHoist ? DB : 1];
+    if constexpr (kHoist) {
+      // With 4 waves (at most two per SIMD), every LDS read of the tile is
+      // issued ahead of its use, so that a wave keeps many reads in flight
+      // instead of waiting on each: all K fragments, then the QK^T products,
+      // then all V^T fragments, whose latency the softmax below covers.  The
+      // scheduling barriers keep the compiler from interleaving each read with
+      // its consumer again.  (This needs ~210 VGPRs; the 8-wave form must stay
+      // at <= 128 so that two of its workgroups share a CU, and keeps the
+      // compiler's own schedule.)  K fragments and products go k-step by
+      // k-step, so the KB independent accumulator chains interleave.
+      bf16x8_t kf[QF][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int row = kb * 16 + l16;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < QF; ++s)
 #pragma unroll
-      for (int s = 0; s < QF; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-            kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & kSwK)) * 16));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+        for (int kb = 0; kb < KB; ++kb) {
+          const int row = kb * 16 + l16;
+          kf[s][kb] = *reinterpret_cast<const bf16x8_t*>(
+              kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & kSwK)) * 16));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sv[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < QF; ++s)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          sv[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kb], qf[s], sv[kb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < KT / 32; ++j)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          i16x4_t h[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * j + 16 * hh + 4 * g + (l16 >> 2);
+            const int chunk = 2 * db + ((l16 & 3) >> 1);
+            const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & kSwV)) * 16) + (l16 & 1) * 8;
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+          }
+          // whole-vector casts: element-wise bf16 inserts from the 16-bit lanes
+          // are lowered wrongly (the upper half of each read is dropped)
+          const u32x2_t w0 = __builtin_bit_cast(u32x2_t, h[0]);
+          const u32x2_t w1 = __builtin_bit_cast(u32x2_t, h[1]);
+          vf[j][db] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = kb * 16 + l16;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < QF; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              kbuf + row * (DH * 2) + (((4 * s + g) ^ (row & kSwK)) * 16));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+        }
+        sv[kb] = acc;
       }
-      sv[kb] = acc;
     }
     // masks: only the last context tile of a split and the tree tiles have any
     if (!(t < nctx_tiles && k0 + (t + 1) * KT <= k1)) {
@@ -698,20 +749,23 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        i16x4_t h[2];
+        bf16x8_t v8;
+        if constexpr (kHoist) {
+          v8 = vf[j][db];
+        } else {
+          i16x4_t h[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * j + 16 * hh + 4 * g + (l16 >> 2);
-          const int chunk = 2 * db + ((l16 & 3) >> 1);
-          const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & kSwV)) * 16) + (l16 & 1) * 8;
-          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 32 * j + 16 * hh + 4 * g + (l16 >> 2);
+            const int chunk = 2 * db + ((l16 & 3) >> 1);
+            const unsigned char* p = vbuf + row * (DH * 2) + ((chunk ^ (row & kSwV)) * 16) + (l16 & 1) * 8;
+            h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+          }
+          const u32x2_t w0 = __builtin_bit_cast(u32x2_t, h[0]);
+          const u32x2_t w1 = __builtin_bit_cast(u32x2_t, h[1]);
+          v8 = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
         }
-        // whole-vector casts: element-wise bf16 inserts from the 16-bit lanes
-        // are lowered wrongly (the upper half of each read is dropped)
-        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, h[0]);
-        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, h[1]);
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v8, pf, o[db], 0, 0, 0);
       }
     }
   }
@@ -926,16 +980,36 @@ void launch_qb(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
   }
 }
 
-// Two LDS stages (64 KB): two workgroups per CU, each with one tile in flight
-// while it computes the other; deeper rings measured no faster.
-constexpr int kDmaStages = 2;
+// LDS ring depth.  Two stages (64 KB) let two workgroups share a CU, each
+// with one tile in flight while it computes the other.  Three and four
+// stages (4-wave form only) measured no faster, also for grids of at most one
+// workgroup per CU, where they would not cost occupancy; DDTREE_ATTN_STAGES
+// selects them.
+int dma_stages(int qb) {
+  int ns = 2;
+  if (const char* env = std::getenv("DDTREE_ATTN_STAGES")) ns = atoi(env);
+  if (qb > 4 || ns < 2 || ns > 4) ns = 2;
+  return ns;
+}
+
+template <int QB, int NS>
+void launch_dma_qbs(const AttnArgs& a, int total_splits, hipStream_t st) {
+  constexpr int NW = QB <= 4 ? 4 : 8;
+  const size_t lds = static_cast<size_t>(NS) * 2 * 64 * 128 * 2;
+  const dim3 grid(total_splits, a.Hkv, (a.M + 127) / 128);
+  hipLaunchKernelGGL((attn_dma_kernel<QB, NW, NS>), grid, dim3(NW * 64), lds, st, a);
+}
 
 template <int QB>
 void launch_dma_qb(const AttnArgs& a, int total_splits, hipStream_t st) {
-  constexpr int NW = QB <= 4 ? 4 : 8;
-  const size_t lds = static_cast<size_t>(kDmaStages) * 2 * 64 * 128 * 2;
-  const dim3 grid(total_splits, a.Hkv, (a.M + 127) / 128);
-  hipLaunchKernelGGL((attn_dma_kernel<QB, NW, kDmaStages>), grid, dim3(NW * 64), lds, st, a);
+  if constexpr (QB <= 4) {
+    switch (dma_stages(QB)) {
+      case 3: launch_dma_qbs<QB, 3>(a, total_splits, st); return;
+      case 4: launch_dma_qbs<QB, 4>(a, total_splits, st); return;
+      default: break;
+    }
+  }
+  launch_dma_qbs<QB, 2>(a, total_splits, st);
 }
 
 void launch_dma(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
