@@ -79,6 +79,59 @@ def test_vocab_reduce(name):
         if T > 0:
             assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
             assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
+            # without the log-sum-exp, bf16 rows take their weights from a table
+            r2 = lib.ddtree_vocab_reduce(c.d("logits"), torch.from_numpy(nn).to("cuda:0"), T)
+            torch.cuda.synchronize()
+            assert np.array_equal(r2["argmax"].cpu().numpy(), ref["argmax"])
+            assert np.array_equal(r2["maxv"].cpu().numpy().view(np.uint32),
+                                  ref["maxv"].view(np.uint32))
+            assert np.array_equal(r2["R"].cpu().numpy().view(np.uint64), ref["R"])
+            assert np.array_equal(r2["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
+
+
+def _awkward_bf16_rows(V, seed):
+    """bf16 logit rows whose weights fall outside a per-row table of the
+    larger magnitudes: tiny, zero, negative-zero and subnormal values, values
+    spread over many binades, a row max of 0, a large row max, a negative
+    row max, equal values, and the most negative finite bf16 value."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    mag = np.exp2(rng.uniform(-140, 6, size=V)).astype(np.float32)   # 2^-140 .. 2^6
+    rows.append(mag * rng.choice([-1.0, 1.0], size=V).astype(np.float32))
+    r = rng.normal(0, 3, size=V).astype(np.float32)
+    r[rng.integers(0, V, size=V // 8)] = 0.0
+    r[rng.integers(0, V, size=V // 8)] = -0.0
+    r[rng.integers(0, V, size=V // 16)] = np.float32(1e-40)          # subnormal
+    rows.append(r)
+    r = -np.abs(rng.normal(0, 1e-3, size=V)).astype(np.float32)
+    r[rng.integers(0, V)] = 0.0                                       # max 0
+    rows.append(r)
+    rows.append((rng.normal(0, 3, size=V) + 3.0e4).astype(np.float32))  # large max
+    rows.append((rng.normal(0, 50, size=V) - 400.0).astype(np.float32))  # negative max, wide
+    rows.append(np.full(V, 1.5, dtype=np.float32))                   # all equal
+    r = rng.normal(0, 3, size=V).astype(np.float32)
+    r[rng.integers(0, V, size=V // 4)] = np.float32(-3.3895314e38)  # bf16 0xFF7F
+    rows.append(r)
+    x = np.stack(rows)[None]                                          # [1, 7, V]
+    return workloads.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 25.0])
+def test_vocab_sampling_awkward_rows(T):
+    """R and its block sums on rows built to miss the weight table (bit-exact)."""
+    import tree_verification_build_amd as lib
+    V = 40960 + 8 * 7
+    bits = _awkward_bf16_rows(V, 51)
+    nn = np.array([bits.shape[1]], dtype=np.int32)
+    say("vocab awkward rows", "T", T, "V", V)
+    logits = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    r = lib.ddtree_vocab_reduce(logits, torch.from_numpy(nn).to("cuda:0"), T)
+    torch.cuda.synchronize()
+    ref = oracle.vocab_reduce(bits, nn, T, dtype="bf16")
+    assert np.array_equal(r["argmax"].cpu().numpy(), ref["argmax"])
+    assert np.array_equal(r["maxv"].cpu().numpy().view(np.uint32), ref["maxv"].view(np.uint32))
+    assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
+    assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -168,6 +221,37 @@ def test_tree_attention(name):
     sel = ~np.isnan(lse_ref) & np.isfinite(lse_ref)
     assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
     assert np.all(np.isneginf(l[np.isneginf(lse_ref)]))
+
+
+# bf16 head dim 128 runs the DMA kernel in one variant per count of 16-row query
+# blocks (1-4: four waves, reads issued ahead of use; 5-8: eight waves); the
+# workloads above reach 1, 3, 5 and 8 blocks.  Contexts of 300-1500 tokens give
+# both single-split and multi-split requests.
+QUERY_BLOCKS = {
+    2: dict(budget=19, Hq=2, Hkv=2, D=8, K=4),     # M = 20
+    4: dict(budget=27, Hq=4, Hkv=2, D=8, K=4),     # M = 56
+    6: dict(budget=47, Hq=4, Hkv=2, D=8, K=4),     # M = 96
+    7: dict(budget=111, Hq=2, Hkv=2, D=16, K=8),   # M = 112
+}
+
+
+@pytest.mark.parametrize("qb", sorted(QUERY_BLOCKS))
+def test_attention_query_blocks(qb):
+    cfg = workloads.config("ragged", B=3, ctx=(300, 1500), Dh=128, V=1024, temperature=0.0,
+                           seed_index=40 + qb, **QUERY_BLOCKS[qb])
+    c = Case(cfg)
+    M = (cfg.budget + 1) * cfg.Hq // cfg.Hkv
+    assert (M + 15) // 16 == qb
+    say("attention query blocks", qb, cfg)
+    t = c.gpu_tree()
+    out, lse = c.gpu_attention(t)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = c.oracle_attention()
+    err, scale = assert_attention_close(attn_to_f64(out), o_ref, "bf16")
+    say("attention query blocks", qb, "max abs err", err, "max |o|", scale)
+    l = lse.cpu().numpy().astype(np.float64)
+    sel = np.isfinite(lse_ref)
+    assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
 
 
 @pytest.mark.parametrize("name", ["bf16_gqa", "single", "ragged"])

@@ -31,6 +31,10 @@ constexpr int kSplitThreads = 256;
 // blocks of DDTREE_R_BLOCK tokens a sampling row may have (V <= 64 blocks)
 constexpr int kMaxRowBlocks = 64;
 constexpr int kRowThreads = 1024;
+// binades of bf16 magnitudes tabulated per sampling row (both signs:
+// 2 * kTabE * 128 weights, 40 KB of LDS)
+constexpr int kTabE = 20;
+constexpr int kTabSpan = kTabE * 128;
 
 // 16 bytes of logits (E = 8 bf16 or 4 fp32 values): raw bits and their floats.
 template <typename T> struct Vec;
@@ -250,7 +254,9 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kRowThreads / kWave;
   constexpr int kPassPerBlock = DDTREE_R_BLOCK / (kRowThreads * E);   // passes per weight block
+  constexpr bool kTab = sizeof(T) == 2 && !kLse;   // bf16 weights from an LDS table
   const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  __shared__ uint64_t s_tab[kTab ? 2 * kTabSpan + 1 : 1];
   __shared__ uint64_t s_u[kMaxRowBlocks];
   __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
   __shared__ float s_f[kWaves];
@@ -320,6 +326,49 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
 
+  // bf16 rows: the weight depends only on a logit's 16-bit pattern (and on
+  // m and c, fixed for the row), so the row's workgroup first tabulates it in
+  // LDS for every pattern of the kTabE binades at and below the larger of |m|
+  // and |m - 32/c| (the magnitudes that can carry weight), both signs, with
+  // weight() itself; the weight pass then indexes the table by the pattern's
+  // sign, exponent and mantissa.  A pattern outside the window (smaller
+  // magnitudes, subnormals, zeros, non-finite values; rare in a row whose
+  // logits spread over several units) takes weight() directly, so every
+  // weight is the one weight() gives, bit for bit, whatever the window.
+  // Entry layout: sign * kTabSpan + (hi - a) for the 15-bit magnitude
+  // pattern a (exponent and mantissa) in [lo, hi]; entry 2 * kTabSpan is 0
+  // and stands for every pattern outside the window.
+  uint32_t hi = 0, span = 0;
+  if constexpr (kTab) {
+    const float big = max(fabsf(m), fabsf(m - 32.0f / wc.c));
+    const int e_top = static_cast<int>((__float_as_uint(big) >> 23) & 0xFFu);
+    const int e_hi = min(e_top, 254), e_lo = max(e_top - kTabE + 1, 1);
+    hi = (static_cast<uint32_t>(e_hi) << 7) | 127u;
+    span = e_hi >= e_lo ? hi - (static_cast<uint32_t>(e_lo) << 7) + 1u : 0u;
+    for (int t = tid; t <= 2 * kTabSpan; t += kRowThreads) {
+      const uint32_t off = static_cast<uint32_t>(t % kTabSpan);
+      uint64_t wv = 0;
+      if (t < 2 * kTabSpan && off < span) {
+        const uint32_t u = (static_cast<uint32_t>(t / kTabSpan) << 15) | (hi - off);
+        const float l = __uint_as_float(u << 16);
+        // patterns above m occur in no row with this maximum; their entries
+        // are never read
+        if (l <= m) wv = weight(l, m, wc);
+      }
+      s_tab[t] = wv;
+    }
+    __syncthreads();
+  }
+  // weight of one bf16 pattern u from the table, or 0 with its bit set in
+  // `miss` when u lies outside the window
+  uint32_t miss = 0;
+  auto tab_weight = [&](uint32_t u, int bit) -> uint64_t {
+    const uint32_t off = hi - (u & 0x7FFFu);   // wraps above the window
+    const bool in = off < span;
+    miss |= in ? 0u : 1u << bit;
+    return s_tab[in ? (u >> 15) * kTabSpan + off : 2u * kTabSpan];
+  };
+
   // weights, summed per block of DDTREE_R_BLOCK tokens (kPassPerBlock passes):
   // each wave's share of a block goes to LDS, the row total is the sum of
   // the blocks
@@ -330,17 +379,45 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
     // opaque to the optimiser: stops it from keeping the first pass's
     // unpacked floats alive (160 of them) instead of the packed raw bits
     __asm__ volatile("" : "+v"(raw[p]));
-    float v[E];
-    Vec<T>::unpack(raw[p], v);
+    if constexpr (kTab) {
+      const u32x4_t w4 = raw[p];
+      const int bit0 = (p % kPassPerBlock) * E;
 #pragma unroll
-    for (int k = 0; k < E; ++k) {
-      bsum += weight(v[k], m, wc);
-      if (kLse) esum += __expf(v[k] - m);
-      // two elements in flight at most: more interleaving runs the 1024-thread
-      // workgroup's 128 registers per lane out and spills weights to scratch
-      if (k & 1) __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < 4; ++k) {
+        bsum += tab_weight(w4[k] & 0xFFFFu, bit0 + 2 * k);
+        bsum += tab_weight(w4[k] >> 16, bit0 + 2 * k + 1);
+        // four lookups in flight at most (registers: see below)
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      float v[E];
+      Vec<T>::unpack(raw[p], v);
+#pragma unroll
+      for (int k = 0; k < E; ++k) {
+        bsum += weight(v[k], m, wc);
+        if (kLse) esum += __expf(v[k] - m);
+        // two elements in flight at most: more interleaving runs the 1024-thread
+        // workgroup's 128 registers per lane out and spills weights to scratch
+        if (k & 1) __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if ((p + 1) % kPassPerBlock == 0 || p == MAXP - 1) {
+      if constexpr (kTab) {
+        // the block's logits outside the table, weighed directly (re-read
+        // from memory: rare, and it keeps weight() out of the unrolled loop)
+        if (__builtin_amdgcn_ballot_w64(miss != 0)) {
+          const int p0 = p - p % kPassPerBlock;
+#pragma unroll 1
+          while (miss) {
+            const int j = __builtin_ctz(miss);
+            miss &= miss - 1u;
+            const long i = static_cast<long>(p0 + j / E) * kRowThreads * E + tid * E + j % E;
+            // past the row end: the -inf padding, weight 0
+            if (i < V) bsum += weight(__uint_as_float(static_cast<uint32_t>(rp[i]) << 16), m, wc);
+          }
+        }
+        miss = 0;
+      }
       const uint64_t ws = wave_sum_u64(bsum);
       if (lane == 0) s_blk[p / kPassPerBlock][wave] = ws;
       bsum = 0;
