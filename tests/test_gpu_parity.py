@@ -134,6 +134,43 @@ def test_vocab_sampling_awkward_rows(T):
     assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
 
 
+@pytest.mark.parametrize("name", ["bf16_gqa", "batched"])
+def test_vocab_sampling_without_workspace(name):
+    """Called without the greedy workspace, a bf16 sampling reduce runs the
+    single-kernel row pass (the row held in registers) instead of the greedy
+    pass plus the streaming weight pass: same outputs, bit for bit."""
+    from tree_verification_build_amd import _lib as L
+    c = case(name)
+    T = c.cfg.temperature if c.cfg.temperature > 0 else 0.8
+    nn = c.tree["num_nodes"]
+    logits = c.d("logits")
+    B, N, V = logits.shape
+    dev = logits.device
+    am = torch.empty((B, N), dtype=torch.int32, device=dev)
+    mx = torch.empty((B, N), dtype=torch.float32, device=dev)
+    R = torch.empty((B, N), dtype=torch.int64, device=dev)
+    nb = (V + L.R_BLOCK - 1) // L.R_BLOCK
+    Rb = torch.empty((B, N, nb), dtype=torch.int64, device=dev)
+    nn_d = torch.from_numpy(nn).to(dev)
+    say("vocab without workspace", name, "T", T)
+    L._check(L.lib.ddtree_vocab_reduce(L._ptr(logits), L._dtype_code(logits), B, N, V,
+                                       L._ptr(nn_d), float(T), L._ptr(am), L._ptr(mx), L._ptr(R),
+                                       L._ptr(Rb), None, None, 0, L._stream(None)))
+    torch.cuda.synchronize()
+    # every valid row at small size; a sample (with padding rows) at full size
+    rng = np.random.default_rng(11)
+    todo = [(b, n) for b in range(B) for n in range(N)]
+    if len(todo) > 64:
+        todo = [todo[i] for i in sorted(rng.choice(len(todo), size=48, replace=False))]
+    ref = oracle.vocab_reduce(c.logits, nn, T, dtype=c.cfg.dtype,
+                              rows=[(b, n) for b, n in todo if n < nn[b]])
+    bi = np.array([b for b, _ in todo]), np.array([n for _, n in todo])
+    assert np.array_equal(am.cpu().numpy()[bi], ref["argmax"][bi])
+    assert np.array_equal(mx.cpu().numpy().view(np.uint32)[bi], ref["maxv"].view(np.uint32)[bi])
+    assert np.array_equal(R.cpu().numpy().view(np.uint64)[bi], ref["R"][bi])
+    assert np.array_equal(Rb.cpu().numpy().view(np.uint64)[bi], ref["R_blocks"][bi])
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_verify_greedy(name):
     import tree_verification_build_amd as lib

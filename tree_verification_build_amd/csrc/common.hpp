@@ -130,6 +130,58 @@ __device__ __forceinline__ uint64_t weight(float l, float m, const WeightConsts&
   return P24 >> sh;
 }
 
+// ---------------------------------------------------------------- weight table
+// Once a row's m (and the temperature's c) are fixed, weight() of a bf16
+// logit depends only on its 16-bit pattern.  A workgroup that weighs many
+// logits of one row tabulates weight() in LDS for the patterns of the kTabE
+// binades at and below max(|m|, |m - 32/c|) (the magnitudes that can carry
+// weight), both signs: entry sign * kTabSpan + (hi - a) for the 15-bit
+// magnitude pattern a in [hi - span + 1, hi], and entry 2 * kTabSpan = 0 for
+// every pattern outside that window.  Callers weigh a miss with weight()
+// itself, so every weight is weight()'s own value whatever the window.
+constexpr int kTabE = 20;
+constexpr int kTabSpan = kTabE * 128;
+constexpr int kTabEntries = 2 * kTabSpan + 1;   // 40 KB of uint64
+
+struct WeightTable {
+  uint32_t hi, span;
+};
+
+// Every thread of the workgroup calls this (tid in [0, nthreads)); the caller
+// synchronises the workgroup before the first lookup.
+__device__ __forceinline__ WeightTable fill_weight_table(uint64_t* s_tab, float m,
+                                                         const WeightConsts& wc, int tid,
+                                                         int nthreads) {
+  const float big = max(fabsf(m), fabsf(m - 32.0f / wc.c));
+  const int e_top = static_cast<int>((__float_as_uint(big) >> 23) & 0xFFu);
+  const int e_hi = min(e_top, 254), e_lo = max(e_top - kTabE + 1, 1);
+  WeightTable tb;
+  tb.hi = (static_cast<uint32_t>(e_hi) << 7) | 127u;
+  tb.span = e_hi >= e_lo ? tb.hi - (static_cast<uint32_t>(e_lo) << 7) + 1u : 0u;
+  for (int t = tid; t < kTabEntries; t += nthreads) {
+    const uint32_t off = static_cast<uint32_t>(t % kTabSpan);
+    uint64_t wv = 0;
+    if (t < 2 * kTabSpan && off < tb.span) {
+      const uint32_t u = (static_cast<uint32_t>(t / kTabSpan) << 15) | (tb.hi - off);
+      const float l = __uint_as_float(u << 16);
+      // patterns above m occur in no row with this maximum; their entries
+      // are never read
+      if (l <= m) wv = weight(l, m, wc);
+    }
+    s_tab[t] = wv;
+  }
+  return tb;
+}
+
+// Table weight of bf16 pattern u; `in` is false (and the result 0) outside
+// the window.  Branch-free: a miss reads the zero entry.
+__device__ __forceinline__ uint64_t table_weight(const uint64_t* s_tab, const WeightTable& tb,
+                                                 uint32_t u, bool& in) {
+  const uint32_t off = tb.hi - (u & 0x7FFFu);   // wraps above the window
+  in = off < tb.span;
+  return s_tab[in ? (u >> 15) * kTabSpan + off : 2u * kTabSpan];
+}
+
 // ---------------------------------------------------------------- element access
 template <typename T> struct Elem;
 template <> struct Elem<float> {

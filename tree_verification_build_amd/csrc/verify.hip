@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   __shared__ uint64_t s_wave[kSampleWaves];
   __shared__ int s_nrej, s_cur, s_a, s_blk, s_found_thread;
   __shared__ uint64_t s_trem, s_found_excl;
+  __shared__ uint64_t s_tab[sizeof(T) == 2 ? kTabEntries : 1];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -242,15 +243,30 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   const float m = maxv[base + cur];
   const uint64_t tw = NUC ? thr_w[base + cur] : 0;
   const int ti = NUC ? thr_id[base + cur] : 0;
-  auto wt = [&](float l, long x) -> uint64_t {
-    const uint64_t w = weight(l, m, wc);
-    if constexpr (NUC) return in_nucleus(w, x, tw, ti) ? w : 0;
-    return w;
-  };
   const T* row = logits + (base + cur) * static_cast<long>(V);
   const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
   float v[32];
   load32<T>(row, x0, V, v);
+  // bf16: the row's weights from a table of weight() (common.hpp), filled
+  // while the block's logits are in flight; a logit outside the table's
+  // window is weighed with weight() itself
+  WeightTable tb{0u, 0u};
+  if constexpr (sizeof(T) == 2) {
+    tb = fill_weight_table(s_tab, m, wc, tid, kSampleThreads);
+    __syncthreads();
+  }
+  auto wt = [&](float l, long x) -> uint64_t {
+    uint64_t w;
+    if constexpr (sizeof(T) == 2) {
+      bool in;
+      w = table_weight(s_tab, tb, __float_as_uint(l) >> 16, in);
+      if (!in) w = weight(l, m, wc);
+    } else {
+      w = weight(l, m, wc);
+    }
+    if constexpr (NUC) return in_nucleus(w, x, tw, ti) ? w : 0;
+    return w;
+  };
   uint64_t sum = 0;
 #pragma unroll
   for (int e = 0; e < 32; ++e) sum += wt(v[e], x0 + e);   // -inf past V weighs 0
@@ -264,22 +280,35 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   uint64_t before = 0;
   for (int k = 0; k < wave; ++k) before += s_wave[k];
   const uint64_t excl = before + incl - sum;
-  if (excl <= trem && trem < excl + sum) {
-    uint64_t acc = excl;
-    int pick = -1;
-    for (int e = 0; e < 32 && pick < 0; ++e) {
-      bool rej = false;
-      for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x0 + e);
-      if (rej) continue;
-      acc += wt(Elem<T>::get(row, x0 + e), x0 + e);
-      if (acc > trem) pick = static_cast<int>(x0) + e;
+  // The wave holding the draw finds it: lane e takes token e of the thread
+  // whose range contains the draw (shuffled from that thread's registers),
+  // weighs it (0 when rejected), and an inclusive scan of the 32 weights
+  // gives the first token whose running sum passes the draw.
+  const uint64_t holder = __ballot(excl <= trem && trem < excl + sum);
+  if (holder) {
+    const int src = __builtin_ctzll(holder);
+    const uint64_t excl_s = __shfl(excl, src, kWave);
+    float x = -__builtin_huge_valf();
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float t = __shfl(v[e], src, kWave);
+      x = lane == e ? t : x;
     }
-    int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
-    outt[s_a] = pick;
-    bonus[b] = pick;
+    const long xs = static_cast<long>(s_blk) * DDTREE_R_BLOCK +
+                    static_cast<long>(wave * kWave + src) * kTokPerThread + lane;
+    bool rej = false;
+    for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == xs);
+    const uint64_t w = lane < 32 && !rej ? wt(x, xs) : 0ull;
+    const uint64_t incl_s = wave_incl_scan_u64(w, lane);
+    const uint64_t hit = __ballot(lane < 32 && excl_s + incl_s > trem);
+    if (lane == 0) {
+      const int pick = hit ? static_cast<int>(xs) + __builtin_ctzll(hit) : -1;
+      int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
+      outt[s_a] = pick;
+      bonus[b] = pick;
+    }
   }
 }
-
 
 // ------------------------------------------------------------------ lazy sampled walk
 // The same walk as sample_kernel, but the target rows are reduced only when

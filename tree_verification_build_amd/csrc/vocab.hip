@@ -31,10 +31,6 @@ constexpr int kSplitThreads = 256;
 // blocks of DDTREE_R_BLOCK tokens a sampling row may have (V <= 64 blocks)
 constexpr int kMaxRowBlocks = 64;
 constexpr int kRowThreads = 1024;
-// binades of bf16 magnitudes tabulated per sampling row (both signs:
-// 2 * kTabE * 128 weights, 40 KB of LDS)
-constexpr int kTabE = 20;
-constexpr int kTabSpan = kTabE * 128;
 
 // 16 bytes of logits (E = 8 bf16 or 4 fp32 values): raw bits and their floats.
 template <typename T> struct Vec;
@@ -256,7 +252,7 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
   constexpr int kPassPerBlock = DDTREE_R_BLOCK / (kRowThreads * E);   // passes per weight block
   constexpr bool kTab = sizeof(T) == 2 && !kLse;   // bf16 weights from an LDS table
   const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
-  __shared__ uint64_t s_tab[kTab ? 2 * kTabSpan + 1 : 1];
+  __shared__ uint64_t s_tab[kTab ? kTabEntries : 1];
   __shared__ uint64_t s_u[kMaxRowBlocks];
   __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
   __shared__ float s_f[kWaves];
@@ -326,47 +322,20 @@ __global__ __launch_bounds__(kRowThreads) void row_kernel(
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
 
-  // bf16 rows: the weight depends only on a logit's 16-bit pattern (and on
-  // m and c, fixed for the row), so the row's workgroup first tabulates it in
-  // LDS for every pattern of the kTabE binades at and below the larger of |m|
-  // and |m - 32/c| (the magnitudes that can carry weight), both signs, with
-  // weight() itself; the weight pass then indexes the table by the pattern's
-  // sign, exponent and mantissa.  A pattern outside the window (smaller
-  // magnitudes, subnormals, zeros, non-finite values; rare in a row whose
-  // logits spread over several units) takes weight() directly, so every
-  // weight is the one weight() gives, bit for bit, whatever the window.
-  // Entry layout: sign * kTabSpan + (hi - a) for the 15-bit magnitude
-  // pattern a (exponent and mantissa) in [lo, hi]; entry 2 * kTabSpan is 0
-  // and stands for every pattern outside the window.
-  uint32_t hi = 0, span = 0;
+  // bf16 rows take their weights from a table of weight() in LDS (common.hpp:
+  // fill_weight_table); a logit outside its window reads 0 and sets its bit
+  // in `miss`, and is weighed with weight() itself at the end of its block.
+  WeightTable tb{0u, 0u};
   if constexpr (kTab) {
-    const float big = max(fabsf(m), fabsf(m - 32.0f / wc.c));
-    const int e_top = static_cast<int>((__float_as_uint(big) >> 23) & 0xFFu);
-    const int e_hi = min(e_top, 254), e_lo = max(e_top - kTabE + 1, 1);
-    hi = (static_cast<uint32_t>(e_hi) << 7) | 127u;
-    span = e_hi >= e_lo ? hi - (static_cast<uint32_t>(e_lo) << 7) + 1u : 0u;
-    for (int t = tid; t <= 2 * kTabSpan; t += kRowThreads) {
-      const uint32_t off = static_cast<uint32_t>(t % kTabSpan);
-      uint64_t wv = 0;
-      if (t < 2 * kTabSpan && off < span) {
-        const uint32_t u = (static_cast<uint32_t>(t / kTabSpan) << 15) | (hi - off);
-        const float l = __uint_as_float(u << 16);
-        // patterns above m occur in no row with this maximum; their entries
-        // are never read
-        if (l <= m) wv = weight(l, m, wc);
-      }
-      s_tab[t] = wv;
-    }
+    tb = fill_weight_table(s_tab, m, wc, tid, kRowThreads);
     __syncthreads();
   }
-  // weight of one bf16 pattern u from the table, or 0 with its bit set in
-  // `miss` when u lies outside the window
   uint32_t miss = 0;
   auto tab_weight = [&](uint32_t u, int bit) -> uint64_t {
-    const uint32_t off = hi - (u & 0x7FFFu);   // wraps above the window
-    const bool in = off < span;
+    bool in;
+    const uint64_t wv = table_weight(s_tab, tb, u, in);
     miss |= in ? 0u : 1u << bit;
-    return s_tab[in ? (u >> 15) * kTabSpan + off : 2u * kTabSpan];
+    return wv;
   };
 
   // weights, summed per block of DDTREE_R_BLOCK tokens (kPassPerBlock passes):
@@ -538,6 +507,91 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
   }
 }
 
+// Sampling weights of bf16 rows whose maximum is already known (maxv from the
+// greedy pass: the same maximum and lowest index the sampling row kernel
+// finds).  With m known the row need not stay in registers: one 1024-thread
+// workgroup per row streams it block by block (DDTREE_R_BLOCK tokens, four
+// 16-byte vectors per thread, the next block's loads in flight while the
+// current one is weighed), so two workgroups share a CU and the loads of one
+// overlap the arithmetic of the other.  Weights come from the LDS table of
+// weight() (common.hpp); a logit outside its window is re-read and weighed
+// with weight() itself.
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void wsum_kernel(
+    const uint16_t* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
+    WeightConsts wc, const float* __restrict__ maxv, uint64_t* __restrict__ R,
+    uint64_t* __restrict__ Rb) {
+  constexpr int E = 8;
+  constexpr int kWaves = kRowThreads / kWave;
+  constexpr int kQ = DDTREE_R_BLOCK / (kRowThreads * E);   // vectors per thread per block
+  static_assert(kQ * E <= 32, "miss bits of one block fit a word");
+  __shared__ uint64_t s_tab[kTabEntries];
+  __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
+  const int row = blockIdx.x;
+  const int b = row / N, n = row % N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+  if (n >= num_nodes[b]) {
+    if (tid == 0) R[row] = 0;
+    if (Rb)
+      for (int k = tid; k < nb; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
+    return;
+  }
+  const float m = maxv[row];
+  const uint16_t* rp = logits + static_cast<long>(row) * V;
+  auto load_block = [&](int blk, u32x4_t (&dst)[kQ]) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const long i = (static_cast<long>(blk) * kQ + q) * kRowThreads * E + tid * E;
+      const uint32_t z = Vec<uint16_t>::kNegInfWord;
+      dst[q] = i < V ? *reinterpret_cast<const u32x4_t*>(rp + i) : u32x4_t{z, z, z, z};
+    }
+  };
+  u32x4_t cur[kQ], nxt[kQ];
+  load_block(0, cur);
+  const WeightTable tb = fill_weight_table(s_tab, m, wc, tid, kRowThreads);
+  __syncthreads();
+  for (int blk = 0; blk < nb; ++blk) {
+    if (blk + 1 < nb) load_block(blk + 1, nxt);
+    uint64_t bsum = 0;
+    uint32_t miss = 0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        bool in0, in1;
+        bsum += table_weight(s_tab, tb, cur[q][k] & 0xFFFFu, in0);
+        bsum += table_weight(s_tab, tb, cur[q][k] >> 16, in1);
+        miss |= (in0 ? 0u : 1u << (q * E + 2 * k)) | (in1 ? 0u : 1u << (q * E + 2 * k + 1));
+      }
+    if (__builtin_amdgcn_ballot_w64(miss != 0)) {
+#pragma unroll 1
+      while (miss) {
+        const int j = __builtin_ctz(miss);
+        miss &= miss - 1u;
+        const long i = (static_cast<long>(blk) * kQ + j / E) * kRowThreads * E + tid * E + j % E;
+        // past the row end: the -inf padding, weight 0
+        if (i < V) bsum += weight(__uint_as_float(static_cast<uint32_t>(rp[i]) << 16), m, wc);
+      }
+    }
+    const uint64_t ws = wave_sum_u64(bsum);
+    if (lane == 0) s_blk[blk][wave] = ws;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) cur[q] = nxt[q];
+  }
+  __syncthreads();
+  // block sums, then the row total as the sum of the blocks (one wave)
+  if (wave == 0) {
+    uint64_t bt = 0;
+    if (lane < nb) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) bt += s_blk[lane][w];
+      if (Rb) Rb[static_cast<long>(row) * nb + lane] = bt;
+    }
+    const uint64_t tot = wave_sum_u64(bt);
+    if (lane == 0) R[row] = tot;
+  }
+}
+
 // Split count for the greedy pass: enough workgroups to cover the chip
 // (about 1024 resident), each slice a whole number of 16-byte vectors per thread.
 void split_plan(int rows, int V, int elem_bytes, int* S_out, int* chunk_out) {
@@ -657,7 +711,20 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
       return fail(DDTREE_EUNSUPPORTED, "ddtree_vocab_reduce: V = %d exceeds %d for sampling", V,
                   kMaxRowBlocks * DDTREE_R_BLOCK);
     const WeightConsts wc = weight_consts(temperature);
-    if (dtype == DDTREE_BF16)
+    // bf16 rows without the log-sum-exp: the greedy pass (argmax, max) and a
+    // streaming weight pass, when the caller gave the greedy workspace
+    int S, chunk;
+    split_plan(rows, V, 2, &S, &chunk);
+    const bool streamed = dtype == DDTREE_BF16 && !lse && V % 8 == 0 && aligned16(logits) &&
+                          (S <= 1 || (workspace && workspace_bytes >= greedy_ws_bytes(rows, S) &&
+                                      aligned16(workspace)));
+    if (streamed) {
+      launch_greedy<uint16_t>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
+                              maxv, nullptr);
+      hipLaunchKernelGGL(wsum_kernel, dim3(rows), dim3(kRowThreads), 0, stream,
+                         static_cast<const uint16_t*>(logits), N, V, num_nodes, wc, maxv, R,
+                         R_blocks);
+    } else if (dtype == DDTREE_BF16)
       launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R,
                                 R_blocks, lse);
     else
