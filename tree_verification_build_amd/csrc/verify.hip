@@ -357,6 +357,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
   __shared__ float s_f[kSampleWaves];
   __shared__ int s_nrej, s_cur, s_a, s_go, s_blk;
   __shared__ uint64_t s_rres, s_trem;
+  __shared__ uint64_t s_tab[sizeof(T) == 2 ? kTabEntries : 1];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -390,6 +391,18 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
   int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
 
   float m = 0.f;
+  WeightTable tb{0u, 0u};
+  // bf16: the weight of a logit of the current row from the row's table of
+  // weight() (common.hpp); outside the table's window, weight() itself
+  auto wt = [&](float l) -> uint64_t {
+    if constexpr (sizeof(T) == 2) {
+      bool in;
+      const uint64_t w = table_weight(s_tab, tb, __float_as_uint(l) >> 16, in);
+      return in ? w : weight(l, m, wc);
+    } else {
+      return weight(l, m, wc);
+    }
+  };
   while (true) {
     const int cur = s_cur;
     const T* row = logits + (base + cur) * static_cast<long>(V);
@@ -411,6 +424,11 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
 #pragma unroll
     for (int w = 1; w < kSampleWaves; ++w) m = max(m, s_f[w]);
     m = m + 0.0f;
+    if constexpr (sizeof(T) == 2) {
+      __syncthreads();   // the previous row's table is no longer read
+      tb = fill_weight_table(s_tab, m, wc, tid, kSampleThreads);
+      __syncthreads();
+    }
     // the weights, summed per block of DDTREE_R_BLOCK tokens
     uint64_t bsum = 0;
 #pragma unroll 4
@@ -419,7 +437,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
       lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        bsum += weight(v[e], m, wc);
+        bsum += wt(v[e]);
         if (e & 1) __builtin_amdgcn_sched_barrier(0);
       }
       if ((p + 1) % kPassPerBlock == 0 || p == npass - 1) {
@@ -443,8 +461,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
       bool moved = false;
       while (c >= 0 && c < N && nrej < t.K) {
         const int tk = s_tok[c];
-        const uint64_t wcur =
-            (tk >= 0 && tk < V) ? weight(Elem<T>::get(row, tk), m, wc) : 0ull;
+        const uint64_t wcur = (tk >= 0 && tk < V) ? wt(Elem<T>::get(row, tk)) : 0ull;
         if (__umul64hi(s_u0[c], rres) < wcur) {
           moved = true;
           break;
@@ -483,7 +500,7 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
       bs = s_Rb[lane];
       for (int r = 0; r < nrej; ++r) {
         const int tk = s_rej[r];
-        if (tk >= 0 && tk / DDTREE_R_BLOCK == lane) bs -= weight(Elem<T>::get(row, tk), m, wc);
+        if (tk >= 0 && tk / DDTREE_R_BLOCK == lane) bs -= wt(Elem<T>::get(row, tk));
       }
     }
     const uint64_t incl = wave_incl_scan_u64(bs, lane);
@@ -510,10 +527,10 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
   load32<T>(row, x0, V, v);
   uint64_t sum = 0;
 #pragma unroll
-  for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);
+  for (int e = 0; e < 32; ++e) sum += wt(v[e]);
   for (int r = 0; r < nrej; ++r) {
     const long x = s_rej[r];
-    if (x >= x0 && x < x0 + 32) sum -= weight(v[x - x0], m, wc);
+    if (x >= x0 && x < x0 + 32) sum -= wt(Elem<T>::get(row, x));
   }
   const uint64_t incl = wave_incl_scan_u64(sum, lane);
   if (lane == kWave - 1) s_wave[wave] = incl;
@@ -521,18 +538,29 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
   uint64_t before = 0;
   for (int k = 0; k < wave; ++k) before += s_wave[k];
   const uint64_t excl = before + incl - sum;
-  if (excl <= trem && trem < excl + sum) {
-    uint64_t acc = excl;
-    int pick = -1;
-    for (int e = 0; e < 32 && pick < 0; ++e) {
-      bool rej = false;
-      for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == x0 + e);
-      if (rej) continue;
-      acc += weight(Elem<T>::get(row, x0 + e), m, wc);
-      if (acc > trem) pick = static_cast<int>(x0) + e;
+  // the pick, by the wave holding the draw (as in sample_kernel)
+  const uint64_t holder = __ballot(excl <= trem && trem < excl + sum);
+  if (holder) {
+    const int src = __builtin_ctzll(holder);
+    const uint64_t excl_s = __shfl(excl, src, kWave);
+    float x = -__builtin_huge_valf();
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const float tv = __shfl(v[e], src, kWave);
+      x = lane == e ? tv : x;
     }
-    outt[a] = pick;
-    bonus[b] = pick;
+    const long xs = static_cast<long>(s_blk) * DDTREE_R_BLOCK +
+                    static_cast<long>(wave * kWave + src) * kTokPerThread + lane;
+    bool rej = false;
+    for (int r = 0; r < nrej; ++r) rej |= (s_rej[r] == xs);
+    const uint64_t w = lane < 32 && !rej ? wt(x) : 0ull;
+    const uint64_t incl_s = wave_incl_scan_u64(w, lane);
+    const uint64_t hit = __ballot(lane < 32 && excl_s + incl_s > trem);
+    if (lane == 0) {
+      const int pick = hit ? static_cast<int>(xs) + __builtin_ctzll(hit) : -1;
+      outt[a] = pick;
+      bonus[b] = pick;
+    }
   }
 }
 
