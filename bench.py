@@ -222,6 +222,40 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
             stream.synchronize()
         t_lazy = time.perf_counter() - t_start
 
+    # greedy workloads: the same step with the vocabulary reduction and the walk in
+    # one call (ddtree_vocab_verify_greedy: the slice merge and the walk share a
+    # launch; same outputs); same synchronised loop
+    t_fused = None
+    if T == 0:
+        f_am = torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev)
+        f_mx = torch.empty((cfg.B, cfg.N), dtype=torch.float32, device=dev)
+
+        def step_fused(i):
+            s = sets[i % rotate]
+            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                             small["prefix_len"], cfg.budget, tree=tree)
+            attention(s)
+            lib.ddtree_vocab_verify_greedy(s["logits"], tree, workspace=ws_v, outputs=outputs,
+                                           argmax=f_am, maxv=f_mx)
+        run_fused = step_fused
+        if graph:
+            fused_graphs = []
+            for i in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step_fused(i)
+                fused_graphs.append(g)
+            run_fused = lambda i: fused_graphs[i % rotate].replay()  # noqa: E731
+        for i in range(warmup):
+            run_fused(i)
+            stream.synchronize()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            run_fused(i)
+            stream.synchronize()
+        t_fused = time.perf_counter() - t_start
+
     # sampling workloads: the step with top-p (p = 0.9) nuclei: vocabulary pass, the
     # per-node nucleus, then the walk on it; same synchronised loop
     t_topp = None
@@ -322,7 +356,8 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     e1.record(stream)
     torch.cuda.synchronize()
     topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
-    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "t_topp": t_topp, "linear": lin,
+    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "t_topp": t_topp,
+            "t_fused": t_fused, "linear": lin,
             "attn_ms": attn_ms, "vocab_ms": vocab_ms, "commit_ms": commit_ms,
             "commit_rows": commit_rows, "commit_bytes": commit_bytes,
             "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
@@ -546,6 +581,12 @@ def main():
     }
     if r["linear"] is not None:
         line["linear_speculative_sampling"] = r["linear"]
+    if r["t_fused"] is not None:
+        line["fused_greedy_step"] = {
+            "steps_per_s": round(args.steps / r["t_fused"], 2),
+            "ms_per_step": round(r["t_fused"] / args.steps * 1e3, 4),
+            "step": "build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
+                    "greedy walk in one call; same outputs)"}
     if r["t_lazy"] is not None:
         line["lazy_sampling_walk"] = {
             "steps_per_s": round(args.steps / r["t_lazy"], 2),

@@ -18,6 +18,8 @@
  *   ddtree_vocab_reduce    per-node argmax / max / log-sum-exp and, for
  *                          sampling, the exact integer softmax total R
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
+ *   ddtree_vocab_verify_greedy  ddtree_vocab_reduce (greedy) and
+ *                          ddtree_verify_greedy in one call (one launch fewer)
  *   ddtree_verify_sample   temperature-T tree rejection sampling walk
  *   ddtree_verify_sample_lazy  the same walk, reducing only the rows it visits
  *   ddtree_vocab_top_p     per-node top-p nucleus of the integer target law
@@ -265,6 +267,31 @@ ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dtype, int32_
 ddtree_status ddtree_verify_greedy(const ddtree_tree* tree, const int32_t* argmax,
                                    int32_t* accept_len, int32_t* path_nodes, int32_t* out_tokens,
                                    int32_t* bonus, hipStream_t stream);
+
+/*
+ * ddtree_vocab_verify_greedy -- the greedy vocabulary reduction and the
+ * greedy walk in one call: the same argmax, maxv, accept_len, path_nodes,
+ * out_tokens and bonus as ddtree_vocab_reduce (temperature 0, no lse)
+ * followed by ddtree_verify_greedy, bit for bit.  The per-row merge of the
+ * vocabulary slices and the walk share one launch (one workgroup per
+ * request), which saves a dependent kernel launch at small batch.
+ * Source: as ddtree_vocab_reduce ("Dissecting DDTree's Tree-Parallel
+ * Evaluation Strategy", Section 1 step 4: argmax at every node) and
+ * ddtree_verify_greedy (Section 1 step 5).
+ *   logits      [B, N, V] row-major, dtype bf16 or f32; B and N from `tree`
+ *   argmax, maxv  [B, N] outputs as ddtree_vocab_reduce's (padding rows:
+ *               -1 and -inf)
+ *   accept_len, path_nodes, out_tokens, bonus: as ddtree_verify_greedy
+ *   workspace   ddtree_vocab_reduce_workspace_size(B, N, V) bytes, 16-byte
+ *               aligned (may be null when that size is 0); caller-owned
+ * Errors: DDTREE_EINVAL (null pointers, tree sizes, V < 1, unknown dtype,
+ *         workspace missing or too small).
+ */
+ddtree_status ddtree_vocab_verify_greedy(const void* logits, ddtree_dtype dtype, int32_t V,
+                                         const ddtree_tree* tree, int32_t* argmax, float* maxv,
+                                         int32_t* accept_len, int32_t* path_nodes,
+                                         int32_t* out_tokens, int32_t* bonus, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ddtree_verify_sample -- temperature-T tree rejection sampling walk.

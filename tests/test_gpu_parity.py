@@ -190,6 +190,30 @@ def test_verify_greedy(name):
 
 
 @pytest.mark.parametrize("name", ALL)
+def test_vocab_verify_greedy(name):
+    """The fused call equals ddtree_vocab_reduce + ddtree_verify_greedy (and the
+    oracle) bit for bit, at every workload's vocabulary and tree shape."""
+    import tree_verification_build_amd as lib
+    c = case(name)
+    t = c.gpu_tree()
+    say("vocab_verify_greedy", name)
+    f = lib.ddtree_vocab_verify_greedy(c.d("logits"), t)
+    v = lib.ddtree_vocab_reduce(c.d("logits"), t.num_nodes, 0.0)
+    g = lib.ddtree_verify_greedy(t, v["argmax"])
+    torch.cuda.synchronize()
+    assert np.array_equal(f["argmax"].cpu().numpy(), v["argmax"].cpu().numpy())
+    assert np.array_equal(f["maxv"].cpu().numpy().view(np.uint32),
+                          v["maxv"].cpu().numpy().view(np.uint32))
+    for k in g:
+        assert np.array_equal(f[k].cpu().numpy(), g[k].cpu().numpy()), k
+    ref_v = oracle.vocab_reduce(c.logits, c.tree["num_nodes"], 0.0, dtype=c.cfg.dtype)
+    ref = oracle.verify_greedy(c.tree, ref_v["argmax"], c.cfg.D)
+    assert np.array_equal(f["argmax"].cpu().numpy(), ref_v["argmax"])
+    for k in ref:
+        assert np.array_equal(f[k].cpu().numpy(), ref[k]), k
+
+
+@pytest.mark.parametrize("name", ALL)
 def test_verify_sample(name):
     import tree_verification_build_amd as lib
     c = case(name)

@@ -2,7 +2,7 @@
 
 Thin ctypes binding over the C-ABI in include/ddtree.h.  The functions carry
 the C names (ddtree_draft_topk, ddtree_build, ddtree_tree_attention[_ranges],
-ddtree_vocab_reduce, ddtree_verify_greedy, ddtree_verify_sample,
+ddtree_vocab_reduce, ddtree_verify_greedy, ddtree_vocab_verify_greedy, ddtree_verify_sample,
 ddtree_verify_sample_lazy, ddtree_verify_linear_sample, ddtree_vocab_top_p,
 ddtree_verify_sample_top_p, ddtree_commit); they only check and marshal
 arguments -- torch tensors on the GPU in, device pointers and the current
@@ -18,6 +18,6 @@ from ._lib import (  # noqa: F401
     ddtree_tree_attention_ranges_workspace_size, ddtree_tree_attention_workspace_size,
     ddtree_verify_greedy, ddtree_verify_linear_sample, ddtree_verify_sample,
     ddtree_verify_sample_lazy, ddtree_verify_sample_top_p, ddtree_version, ddtree_vocab_top_p,
-    ddtree_vocab_reduce,
+    ddtree_vocab_reduce, ddtree_vocab_verify_greedy,
     ddtree_vocab_reduce_workspace_size, library_path, lib,
 )

@@ -52,6 +52,8 @@ lib.ddtree_vocab_reduce_workspace_size.restype = _sz
 lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _sz, _vp]
 lib.ddtree_verify_greedy.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.ddtree_vocab_verify_greedy.argtypes = [_vp, ctypes.c_int, _i32, _tp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _sz, _vp]
 lib.ddtree_verify_sample.argtypes = [_tp, _vp, ctypes.c_int, _i32, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
                                      _vp, _vp, _vp]
 lib.ddtree_verify_sample_lazy.argtypes = [_tp, _vp, ctypes.c_int, _i32, _f32, _vp, _vp, _vp, _vp,
@@ -67,7 +69,8 @@ lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
            "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
-           "ddtree_verify_greedy", "ddtree_verify_sample", "ddtree_verify_sample_lazy",
+           "ddtree_verify_greedy", "ddtree_vocab_verify_greedy", "ddtree_verify_sample",
+           "ddtree_verify_sample_lazy",
            "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_vocab_top_p",
            "ddtree_verify_sample_top_p", "ddtree_sampling_constants"):
     getattr(lib, _f).restype = ctypes.c_int
@@ -314,6 +317,32 @@ def ddtree_verify_greedy(tree, argmax, outputs=None, stream=None):
                                     _ptr(o["path_nodes"]), _ptr(o["out_tokens"]),
                                     _ptr(o["bonus"]), _stream(stream)))
     return o
+
+
+
+def ddtree_vocab_verify_greedy(logits, tree, workspace=None, outputs=None, argmax=None, maxv=None,
+                               stream=None):
+    """ddtree_vocab_reduce (greedy) + ddtree_verify_greedy in one call: returns the
+    walk's outputs plus "argmax" and "maxv"."""
+    B, N, V = logits.shape
+    _dev(logits, "logits", (torch.bfloat16, torch.float32))
+    if (B, N) != (tree.B, tree.N):
+        raise ValueError(f"logits rows {(B, N)} do not match the tree {(tree.B, tree.N)}")
+    dev = logits.device
+    argmax = argmax if argmax is not None else torch.empty((B, N), dtype=torch.int32, device=dev)
+    maxv = maxv if maxv is not None else torch.empty((B, N), dtype=torch.float32, device=dev)
+    _dev(argmax, "argmax", torch.int32, (B, N))
+    _dev(maxv, "maxv", torch.float32, (B, N))
+    need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    o = outputs or _walk_outputs(tree)
+    _check(lib.ddtree_vocab_verify_greedy(_ptr(logits), _dtype_code(logits), V, tree.cstruct,
+                                          _ptr(argmax), _ptr(maxv), _ptr(o["accept_len"]),
+                                          _ptr(o["path_nodes"]), _ptr(o["out_tokens"]),
+                                          _ptr(o["bonus"]), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
+    return dict(o, argmax=argmax, maxv=maxv)
 
 
 def ddtree_verify_sample(tree, logits, maxv, R, R_blocks, temperature, uniforms, outputs=None,

@@ -182,6 +182,69 @@ __device__ __forceinline__ uint64_t table_weight(const uint64_t* s_tab, const We
   return s_tab[in ? (u >> 15) * kTabSpan + off : 2u * kTabSpan];
 }
 
+// ---------------------------------------------------------------- greedy walk
+// The greedy walk of request b by one wave ("Dissecting DDTree's
+// Tree-Parallel Evaluation Strategy", Section 1 step 5): from the root, move
+// to the child whose token equals the target argmax at the current node
+// (children's tokens are distinct, so it is unique) until there is none or
+// the depth reaches D; accept_len = moves, bonus = argmax at the last node.
+// Lane l holds nodes l and l + 64 (N <= 128): their parent and token, -2 for
+// nodes that do not exist.
+struct WalkNodes {
+  int par[2], tok[2];
+};
+
+__device__ __forceinline__ WalkNodes walk_load(const ddtree_tree& t, int b, int lane) {
+  const int N = t.N;
+  const long base = static_cast<long>(b) * N;
+  WalkNodes w;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int j = lane + s * kWave;
+    w.par[s] = j < N ? t.parent[base + j] : -2;
+    w.tok[s] = j < N ? t.token[base + j] : -2;
+  }
+  return w;
+}
+
+// s_am: the argmax of every node of the request (-1 for padding nodes), in
+// LDS; w: walk_load() with the nodes >= num_nodes[b] already set to -2.
+__device__ __forceinline__ void walk_run(const ddtree_tree& t, int b, const int32_t* s_am,
+                                         const WalkNodes& w, int lane,
+                                         int32_t* __restrict__ accept_len,
+                                         int32_t* __restrict__ path_nodes,
+                                         int32_t* __restrict__ out_tokens,
+                                         int32_t* __restrict__ bonus) {
+  const int D = t.D;
+  int32_t* path = path_nodes + static_cast<long>(b) * (D + 1);
+  int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
+  int cur = 0, a = 0;
+  while (a < D) {
+    const int target = s_am[cur];
+    const uint64_t m0 = __ballot(w.par[0] == cur && w.tok[0] == target);
+    const uint64_t m1 = __ballot(w.par[1] == cur && w.tok[1] == target);
+    if (!m0 && !m1) break;
+    const int c = m0 ? __builtin_ctzll(m0) : kWave + __builtin_ctzll(m1);
+    if (lane == 0) outt[a] = target;
+    cur = c;
+    ++a;
+    if (lane == 0) path[a] = c;
+  }
+  const int bon = s_am[cur];
+  for (int k = lane; k <= D; k += kWave) {
+    if (k > a) {
+      path[k] = -1;
+      outt[k] = -1;
+    }
+  }
+  if (lane == 0) {
+    path[0] = 0;
+    outt[a] = bon;
+    accept_len[b] = a;
+    bonus[b] = bon;
+  }
+}
+
 // ---------------------------------------------------------------- element access
 template <typename T> struct Elem;
 template <> struct Elem<float> {

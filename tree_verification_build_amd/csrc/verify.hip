@@ -29,16 +29,15 @@ __global__ __launch_bounds__(64) void greedy_kernel(ddtree_tree t, const int32_t
   __shared__ int32_t s_am[kMaxN];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
-  const int N = t.N, D = t.D;
+  const int N = t.N;
   const long base = static_cast<long>(b) * N;
   // the tree and argmax rows are read before num_nodes is known (all N
   // entries exist), so that the loads do not wait for it
-  int par[2], tok[2], am[2];
+  WalkNodes w = walk_load(t, b, lane);
+  int am[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int j = lane + s * kWave;
-    par[s] = j < N ? t.parent[base + j] : -2;
-    tok[s] = j < N ? t.token[base + j] : -2;
     am[s] = j < N ? argmax[base + j] : -1;
   }
   const int nn = t.num_nodes[b];
@@ -46,38 +45,12 @@ __global__ __launch_bounds__(64) void greedy_kernel(ddtree_tree t, const int32_t
   for (int s = 0; s < 2; ++s) {
     const int j = lane + s * kWave;
     const bool ok = j < nn;
-    par[s] = ok ? par[s] : -2;
-    tok[s] = ok ? tok[s] : -2;
+    w.par[s] = ok ? w.par[s] : -2;
+    w.tok[s] = ok ? w.tok[s] : -2;
     if (j < N) s_am[j] = ok ? am[s] : -1;
   }
   __syncthreads();
-  int32_t* path = path_nodes + static_cast<long>(b) * (D + 1);
-  int32_t* outt = out_tokens + static_cast<long>(b) * (D + 1);
-  int cur = 0, a = 0;
-  while (a < D) {
-    const int target = s_am[cur];
-    const uint64_t m0 = __ballot(par[0] == cur && tok[0] == target);
-    const uint64_t m1 = __ballot(par[1] == cur && tok[1] == target);
-    if (!m0 && !m1) break;
-    const int c = m0 ? __builtin_ctzll(m0) : kWave + __builtin_ctzll(m1);
-    if (lane == 0) outt[a] = target;
-    cur = c;
-    ++a;
-    if (lane == 0) path[a] = c;
-  }
-  const int bon = s_am[cur];
-  for (int k = lane; k <= D; k += kWave) {
-    if (k > a) {
-      path[k] = -1;
-      outt[k] = -1;
-    }
-  }
-  if (lane == 0) {
-    path[0] = 0;
-    outt[a] = bon;
-    accept_len[b] = a;
-    bonus[b] = bon;
-  }
+  walk_run(t, b, s_am, w, lane, accept_len, path_nodes, out_tokens, bonus);
 }
 
 constexpr int kSampleThreads = 1024;

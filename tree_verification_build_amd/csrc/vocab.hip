@@ -23,6 +23,9 @@
 #include "common.hpp"
 
 namespace ddt {
+
+ddtree_status check_tree(const ddtree_tree* t, const char* who);
+
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -592,6 +595,66 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
   }
 }
 
+// Greedy merge and walk in one launch: one workgroup per request merges the
+// slice keys of all its rows (an LDS 64-bit maximum per row: the largest
+// packed key, as in finalize_kernel, hence the same argmax and max), writes
+// argmax and max, and its first wave then walks the tree from LDS
+// (common.hpp: walk_run).  The dependent launch this saves is most of the
+// cost of the merge and of the walk at small batch.
+constexpr int kMergeWalkThreads = 1024;
+
+__global__ __launch_bounds__(kMergeWalkThreads) void merge_walk_kernel(
+    ddtree_tree t, int S, const uint64_t* __restrict__ ws_key, int32_t* __restrict__ argmax,
+    float* __restrict__ maxv, int32_t* __restrict__ accept_len, int32_t* __restrict__ path_nodes,
+    int32_t* __restrict__ out_tokens, int32_t* __restrict__ bonus) {
+  __shared__ unsigned long long s_key[DDTREE_MAX_NODES];
+  __shared__ int32_t s_am[DDTREE_MAX_NODES];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int N = t.N;
+  const long base = static_cast<long>(b) * N;
+  WalkNodes w{};
+  if (wave == 0) w = walk_load(t, b, lane);
+  for (int n = tid; n < N; n += kMergeWalkThreads) s_key[n] = 0ull;
+  const int nn = t.num_nodes[b];
+  __syncthreads();
+  // this request's keys: S per row, rows base .. base + N - 1; four loads in
+  // flight per thread before their LDS maxima
+  const uint64_t* keys = ws_key + base * S;
+  const int total = N * S;
+  for (int i0 = tid; i0 < total; i0 += 4 * kMergeWalkThreads) {
+    uint64_t kk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kMergeWalkThreads;
+      kk[u] = i < total ? keys[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kMergeWalkThreads;
+      if (i < total) atomicMax(&s_key[i / S], static_cast<unsigned long long>(kk[u]));
+    }
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += kMergeWalkThreads) {
+    const bool valid = n < nn;
+    const uint64_t key = s_key[n];
+    const int am = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
+    argmax[base + n] = am;
+    maxv[base + n] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
+    s_am[n] = am;
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bool ok = lane + s2 * kWave < nn;
+      w.par[s2] = ok ? w.par[s2] : -2;
+      w.tok[s2] = ok ? w.tok[s2] : -2;
+    }
+    walk_run(t, b, s_am, w, lane, accept_len, path_nodes, out_tokens, bonus);
+  }
+}
+
 // Split count for the greedy pass: enough workgroups to cover the chip
 // (about 1024 resident), each slice a whole number of 16-byte vectors per thread.
 void split_plan(int rows, int V, int elem_bytes, int* S_out, int* chunk_out) {
@@ -747,4 +810,46 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
     launch_greedy<float>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
                          maxv, lse);
   return check_launch("ddtree_vocab_reduce");
+}
+
+extern "C" ddtree_status ddtree_vocab_verify_greedy(const void* logits, ddtree_dtype dtype,
+                                                    int32_t V, const ddtree_tree* tree,
+                                                    int32_t* argmax, float* maxv,
+                                                    int32_t* accept_len, int32_t* path_nodes,
+                                                    int32_t* out_tokens, int32_t* bonus,
+                                                    void* workspace, size_t workspace_bytes,
+                                                    hipStream_t stream) {
+  using namespace ddt;
+  const char* who = "ddtree_vocab_verify_greedy";
+  if (const ddtree_status st = check_tree(tree, who)) return st;
+  if (!logits || !argmax || !maxv || !accept_len || !path_nodes || !out_tokens || !bonus)
+    return fail(DDTREE_EINVAL, "%s: null pointer", who);
+  if (V < 1) return fail(DDTREE_EINVAL, "%s: V = %d", who, V);
+  if (dtype != DDTREE_BF16 && dtype != DDTREE_F32)
+    return fail(DDTREE_EINVAL, "%s: unknown dtype %d", who, static_cast<int>(dtype));
+  const int rows = tree->B * tree->N;
+  int S, chunk;
+  split_plan(rows, V, dtype == DDTREE_BF16 ? 2 : 4, &S, &chunk);
+  if (S > 1) {
+    const size_t need = greedy_ws_bytes(rows, S);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+      return fail(DDTREE_EINVAL, "%s: workspace of %zu bytes needed, got %zu", who, need,
+                  workspace_bytes);
+  }
+  uint64_t* ws_key = static_cast<uint64_t*>(workspace);
+  float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<size_t>(rows) * S);
+  const dim3 grid(S, rows);
+  if (dtype == DDTREE_BF16)
+    hipLaunchKernelGGL((split_kernel<uint16_t, false>), grid, dim3(kSplitThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), tree->N, V, tree->num_nodes, S, chunk,
+                       ws_key, ws_ms, argmax, maxv, nullptr);
+  else
+    hipLaunchKernelGGL((split_kernel<float, false>), grid, dim3(kSplitThreads), 0, stream,
+                       static_cast<const float*>(logits), tree->N, V, tree->num_nodes, S, chunk,
+                       ws_key, ws_ms, argmax, maxv, nullptr);
+  if (S == 1)   // the split pass wrote argmax and max itself: the plain walk follows
+    return ddtree_verify_greedy(tree, argmax, accept_len, path_nodes, out_tokens, bonus, stream);
+  hipLaunchKernelGGL(merge_walk_kernel, dim3(tree->B), dim3(kMergeWalkThreads), 0, stream, *tree,
+                     S, ws_key, argmax, maxv, accept_len, path_nodes, out_tokens, bonus);
+  return check_launch(who);
 }
