@@ -575,16 +575,31 @@ __device__ __forceinline__ u128 shfl_up_u128(u128 v, int d) {
 constexpr int kLinPass = kSampleThreads * 8;      // tokens per residual pass
 constexpr int kLinMaxPass = 64 * DDTREE_R_BLOCK / kLinPass;
 
-// residual weight of token y (0 past the row)
+// 8 consecutive logits of a row as floats (one 16-byte load when `vec` and
+// the 8 lie inside the row); past V read as -inf
 template <typename T>
-__device__ __forceinline__ u128 residual_w(const T* qrow, const T* prow, long y, int V, float mq,
-                                           float mp, uint64_t Rq, uint64_t Rp,
-                                           const WeightConsts& wc) {
-  if (y >= V) return 0;
-  const uint64_t wq = weight(Elem<T>::get(qrow, y), mq, wc);
-  const uint64_t wp = weight(Elem<T>::get(prow, y), mp, wc);
-  const u128 a = static_cast<u128>(wq) * Rp, b = static_cast<u128>(wp) * Rq;
-  return a > b ? a - b : 0;
+__device__ __forceinline__ void lin_load8(const T* row, long y0, int V, bool vec, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    if (vec && y0 + 8 <= V) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + y0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+      return;
+    }
+  } else {
+    if (vec && y0 + 8 <= V) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(row + y0 + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * h + e] = __uint_as_float(w[e]);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = y0 + e < V ? Elem<T>::get(row, y0 + e) : -__builtin_huge_valf();
 }
 
 // inclusive scan of a u128 over the workgroup in token (= thread) order;
@@ -617,8 +632,11 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
     const float* __restrict__ maxp, const uint64_t* __restrict__ Rp, WeightConsts wc,
     const uint64_t* __restrict__ uniforms, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ out_tokens, int32_t* __restrict__ bonus) {
+  constexpr bool kTab = sizeof(T) == 2;   // bf16: weights from LDS tables
   __shared__ u128 s_w[kSampleWaves];
   __shared__ u128 s_pass[kLinMaxPass];
+  __shared__ u128 s_pw[kLinMaxPass][kSampleWaves];
+  __shared__ uint64_t s_tq[kTab ? kTabEntries : 1], s_tp[kTab ? kTabEntries : 1];
   __shared__ uint64_t s_wave[kSampleWaves];
   __shared__ int s_k, s_mode, s_pick, s_blk;
   __shared__ u128 s_t;
@@ -653,29 +671,68 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
   const long rq = static_cast<long>(b) * (D + 1) + k;
   const T* qrow = tlog + rq * V;
   const uint64_t u1 = uniforms[rq * 2 + 1];
-  if (s_mode == 1) {
-    const long rp = static_cast<long>(b) * D + k;
+  const float mq = maxq[rq];
+  // bf16: the weights of target row k (and, for a residual, of draft row k)
+  // from tables of weight() in LDS (common.hpp); outside a table's window,
+  // weight() itself
+  WeightTable tq{0u, 0u}, tp{0u, 0u};
+  const int mode = s_mode;
+  const long rp = static_cast<long>(b) * D + k;
+  const float mp = mode == 1 ? maxp[rp] : 0.f;
+  if constexpr (kTab) {
+    tq = fill_weight_table(s_tq, mq, wc, tid, kSampleThreads);
+    if (mode == 1) tp = fill_weight_table(s_tp, mp, wc, tid, kSampleThreads);
+    __syncthreads();
+  }
+  auto wq_of = [&](float l) -> uint64_t {
+    if constexpr (kTab) {
+      bool in;
+      const uint64_t w = table_weight(s_tq, tq, __float_as_uint(l) >> 16, in);
+      return in ? w : weight(l, mq, wc);
+    } else {
+      return weight(l, mq, wc);
+    }
+  };
+  auto wp_of = [&](float l) -> uint64_t {
+    if constexpr (kTab) {
+      bool in;
+      const uint64_t w = table_weight(s_tp, tp, __float_as_uint(l) >> 16, in);
+      return in ? w : weight(l, mp, wc);
+    } else {
+      return weight(l, mp, wc);
+    }
+  };
+  if (mode == 1) {
     const T* prow = dlog + rp * V;
-    const float mq = maxq[rq], mp = maxp[rp];
     const uint64_t Rqk = Rq[rq], Rpk = Rp[rp];
     const int npass = (V + kLinPass - 1) / kLinPass;
-    // pass sums of the residual
+    const bool vq = aligned16(qrow) && V % 8 == 0, vp = aligned16(prow) && V % 8 == 0;
+    // residual weight of one token from its two logits (0 past V: both -inf)
+    auto rw = [&](float lq, float lp) -> u128 {
+      const u128 a2 = static_cast<u128>(wq_of(lq)) * Rpk, b2 = static_cast<u128>(wp_of(lp)) * Rqk;
+      return a2 > b2 ? a2 - b2 : 0;
+    };
+    // pass sums of the residual: each wave's share of a pass goes to LDS, one
+    // barrier after the last pass
     for (int p = 0; p < npass; ++p) {
       const long y0 = static_cast<long>(p) * kLinPass + static_cast<long>(tid) * 8;
+      float lq[8], lp[8];
+      lin_load8<T>(qrow, y0, V, vq, lq);
+      lin_load8<T>(prow, y0, V, vp, lp);
       u128 s = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s += residual_w<T>(qrow, prow, y0 + e, V, mq, mp, Rqk, Rpk, wc);
+      for (int e = 0; e < 8; ++e) s += rw(lq[e], lp[e]);
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) s += shfl_xor_u128(s, m);
-      if (lane == 0) s_w[wave] = s;
-      __syncthreads();
-      if (tid == 0) {
-        u128 t = 0;
-        for (int w = 0; w < kSampleWaves; ++w) t += s_w[w];
-        s_pass[p] = t;
-      }
-      __syncthreads();
+      if (lane == 0) s_pw[p][wave] = s;
     }
+    __syncthreads();
+    if (tid < npass) {
+      u128 t = 0;
+      for (int w = 0; w < kSampleWaves; ++w) t += s_pw[tid][w];
+      s_pass[tid] = t;
+    }
+    __syncthreads();
     if (tid == 0) {
       u128 Rr = 0;
       for (int p = 0; p < npass; ++p) Rr += s_pass[p];
@@ -695,10 +752,13 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
       // rescan the pass holding the draw, in token order
       const u128 t = s_t;
       const long y0 = static_cast<long>(s_blk) * kLinPass + static_cast<long>(tid) * 8;
+      float lq[8], lp[8];
+      lin_load8<T>(qrow, y0, V, vq, lq);
+      lin_load8<T>(prow, y0, V, vp, lp);
       u128 r[8], s = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        r[e] = residual_w<T>(qrow, prow, y0 + e, V, mq, mp, Rqk, Rpk, wc);
+        r[e] = rw(lq[e], lp[e]);
         s += r[e];
       }
       u128 tot;
@@ -734,13 +794,12 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
     }
     __syncthreads();
     const uint64_t trem = s_trem;
-    const float m = maxq[rq];
     const long x0 = static_cast<long>(s_blk) * DDTREE_R_BLOCK + static_cast<long>(tid) * kTokPerThread;
     float v[32];
     load32<T>(qrow, x0, V, v);
     uint64_t sum = 0;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) sum += weight(v[e], m, wc);
+    for (int e = 0; e < 32; ++e) sum += wq_of(v[e]);
     const uint64_t incl = wave_incl_scan_u64(sum, lane);
     if (lane == kWave - 1) s_wave[wave] = incl;
     __syncthreads();
@@ -751,7 +810,7 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
       uint64_t acc = excl;
       int pick = -1;
       for (int e = 0; e < 32 && pick < 0; ++e) {
-        acc += weight(v[e], m, wc);
+        acc += wq_of(v[e]);
         if (acc > trem) pick = static_cast<int>(x0) + e;
       }
       s_pick = pick;
