@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on the GPU machine only; elsewhere they are skipped, never faked.
+    # GPU tests run only where a GPU is present; elsewhere they are skipped, never faked.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
