@@ -114,7 +114,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes, int S,
     int chunk, uint64_t* __restrict__ ws_key, float2* __restrict__ ws_ms,
     int32_t* __restrict__ argmax, float* __restrict__ maxv,
-    float* __restrict__ lse) {
+    float* __restrict__ lse,
+    uint64_t* __restrict__ zero_R) {
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kSplitThreads / kWave;
   __shared__ uint64_t s_key[kWaves];
@@ -191,6 +192,8 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
   }
   __syncthreads();
   if (tid == 0) {
+    // the streamed sampling pass adds its weight sums into R: slice 0 clears it
+    if (zero_R && s == 0) zero_R[row] = 0;
     for (int w = 1; w < kWaves; ++w) {
       key = s_key[w] > key ? s_key[w] : key;
       if (kLse) lse_merge(m, sum, s_ms[w].x, s_ms[w].y);
@@ -512,11 +515,12 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
 
 // Sampling weights of bf16 rows whose maximum is already known (maxv from the
 // greedy pass: the same maximum and lowest index the sampling row kernel
-// finds).  With m known the row need not stay in registers: one 1024-thread
-// workgroup per row streams it block by block (DDTREE_R_BLOCK tokens, four
-// 16-byte vectors per thread, the next block's loads in flight while the
-// current one is weighed), so two workgroups share a CU and the loads of one
-// overlap the arithmetic of the other.  Weights come from the LDS table of
+// finds).  With m known the row need not stay in registers: one or two
+// 1024-thread workgroups per row (two take half of the row's blocks each, so
+// that 528 rows do not leave a second round of 16 on 512 workgroup slots)
+// stream it block by block (DDTREE_R_BLOCK tokens, four 16-byte vectors per thread, the next
+// block's loads in flight while the current one is weighed); two workgroups
+// share a CU, and the loads of one overlap the arithmetic of the other.  Weights come from the LDS table of
 // weight() (common.hpp); a logit outside its window is re-read and weighed
 // with weight() itself.
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void wsum_kernel(
@@ -533,10 +537,13 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
   const int b = row / N, n = row % N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
-  if (n >= num_nodes[b]) {
-    if (tid == 0) R[row] = 0;
+  // workgroup y of gridDim.y takes blocks [blk0, blk1) of the row
+  const int per = (nb + gridDim.y - 1) / gridDim.y;
+  const int blk0 = blockIdx.y * per, blk1 = min(nb, blk0 + per);
+  if (blk0 >= blk1) return;
+  if (n >= num_nodes[b]) {   // R was cleared by the greedy pass
     if (Rb)
-      for (int k = tid; k < nb; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
+      for (int k = blk0 + tid; k < blk1; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
     return;
   }
   const float m = maxv[row];
@@ -550,11 +557,11 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
     }
   };
   u32x4_t cur[kQ], nxt[kQ];
-  load_block(0, cur);
+  load_block(blk0, cur);
   const WeightTable tb = fill_weight_table(s_tab, m, wc, tid, kRowThreads);
   __syncthreads();
-  for (int blk = 0; blk < nb; ++blk) {
-    if (blk + 1 < nb) load_block(blk + 1, nxt);
+  for (int blk = blk0; blk < blk1; ++blk) {
+    if (blk + 1 < blk1) load_block(blk + 1, nxt);
     uint64_t bsum = 0;
     uint32_t miss = 0;
 #pragma unroll
@@ -577,21 +584,22 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
       }
     }
     const uint64_t ws = wave_sum_u64(bsum);
-    if (lane == 0) s_blk[blk][wave] = ws;
+    if (lane == 0) s_blk[blk - blk0][wave] = ws;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) cur[q] = nxt[q];
   }
   __syncthreads();
-  // block sums, then the row total as the sum of the blocks (one wave)
+  // block sums, then this workgroup's share of the row total, added into R
+  // (cleared by the greedy pass; integer sums, so the order is immaterial)
   if (wave == 0) {
     uint64_t bt = 0;
-    if (lane < nb) {
+    if (lane < blk1 - blk0) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) bt += s_blk[lane][w];
-      if (Rb) Rb[static_cast<long>(row) * nb + lane] = bt;
+      if (Rb) Rb[static_cast<long>(row) * nb + blk0 + lane] = bt;
     }
     const uint64_t tot = wave_sum_u64(bt);
-    if (lane == 0) R[row] = tot;
+    if (lane == 0) atomicAdd(reinterpret_cast<unsigned long long*>(R + row), static_cast<unsigned long long>(tot));
   }
 }
 
@@ -718,18 +726,19 @@ size_t greedy_ws_bytes(int rows, int S) {
 
 template <typename T>
 void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
-                   int S, int chunk, void* ws, int32_t* am, float* mx, float* lse) {
+                   int S, int chunk, void* ws, int32_t* am, float* mx, float* lse,
+                   uint64_t* zero_R = nullptr) {
   uint64_t* ws_key = static_cast<uint64_t*>(ws);
   float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<size_t>(rows) * S);
   const dim3 grid(S, rows);
   if (lse)
     hipLaunchKernelGGL((split_kernel<T, true>), grid, dim3(kSplitThreads), 0, st,
                        static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
-                       lse);
+                       lse, zero_R);
   else
     hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
                        static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
-                       lse);
+                       lse, zero_R);
   if (S > 1) {
     if (lse)
       hipLaunchKernelGGL((finalize_kernel<true>), dim3(rows), dim3(kWave), 0, st, N, nn, S, ws_key,
@@ -783,8 +792,14 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
                                       aligned16(workspace)));
     if (streamed) {
       launch_greedy<uint16_t>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
-                              maxv, nullptr);
-      hipLaunchKernelGGL(wsum_kernel, dim3(rows), dim3(kRowThreads), 0, stream,
+                              maxv, nullptr, R);
+      // two workgroups per row while the rows fill under two rounds of the
+      // chip's 512 slots (batched: 528 rows 87 -> 83 us); with many rounds the
+      // second table fill per row costs more than the balance gains (ragged:
+      // 2112 rows, 265 -> 282 us)
+      const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
+      const int halves = nb > 1 && rows < 1024 ? 2 : 1;
+      hipLaunchKernelGGL(wsum_kernel, dim3(rows, halves), dim3(kRowThreads), 0, stream,
                          static_cast<const uint16_t*>(logits), N, V, num_nodes, wc, maxv, R,
                          R_blocks);
     } else if (dtype == DDTREE_BF16)
@@ -842,11 +857,11 @@ extern "C" ddtree_status ddtree_vocab_verify_greedy(const void* logits, ddtree_d
   if (dtype == DDTREE_BF16)
     hipLaunchKernelGGL((split_kernel<uint16_t, false>), grid, dim3(kSplitThreads), 0, stream,
                        static_cast<const uint16_t*>(logits), tree->N, V, tree->num_nodes, S, chunk,
-                       ws_key, ws_ms, argmax, maxv, nullptr);
+                       ws_key, ws_ms, argmax, maxv, nullptr, nullptr);
   else
     hipLaunchKernelGGL((split_kernel<float, false>), grid, dim3(kSplitThreads), 0, stream,
                        static_cast<const float*>(logits), tree->N, V, tree->num_nodes, S, chunk,
-                       ws_key, ws_ms, argmax, maxv, nullptr);
+                       ws_key, ws_ms, argmax, maxv, nullptr, nullptr);
   if (S == 1)   // the split pass wrote argmax and max itself: the plain walk follows
     return ddtree_verify_greedy(tree, argmax, accept_len, path_nodes, out_tokens, bonus, stream);
   hipLaunchKernelGGL(merge_walk_kernel, dim3(tree->B), dim3(kMergeWalkThreads), 0, stream, *tree,
