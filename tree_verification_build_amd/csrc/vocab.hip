@@ -513,9 +513,10 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
   }
 }
 
-// Sampling weights of bf16 rows whose maximum is already known (maxv from the
+// Sampling weights of bf16 rows whose maximum is already known (from the
 // greedy pass: the same maximum and lowest index the sampling row kernel
-// finds).  With m known the row need not stay in registers: one or two
+// finds; when that pass split the rows, this kernel merges its slice keys and
+// writes argmax and max itself, which saves the merge kernel's launch).  With m known the row need not stay in registers: one or two
 // 1024-thread workgroups per row (two take half of the row's blocks each, so
 // that 528 rows do not leave a second round of 16 on 512 workgroup slots)
 // stream it block by block (DDTREE_R_BLOCK tokens, four 16-byte vectors per thread, the next
@@ -525,14 +526,15 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
 // with weight() itself.
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void wsum_kernel(
     const uint16_t* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
-    WeightConsts wc, const float* __restrict__ maxv, uint64_t* __restrict__ R,
-    uint64_t* __restrict__ Rb) {
+    WeightConsts wc, int S, const uint64_t* __restrict__ ws_key, int32_t* __restrict__ argmax,
+    float* __restrict__ maxv, uint64_t* __restrict__ R, uint64_t* __restrict__ Rb) {
   constexpr int E = 8;
   constexpr int kWaves = kRowThreads / kWave;
   constexpr int kQ = DDTREE_R_BLOCK / (kRowThreads * E);   // vectors per thread per block
   static_assert(kQ * E <= 32, "miss bits of one block fit a word");
   __shared__ uint64_t s_tab[kTabEntries];
   __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
+  __shared__ uint64_t s_rowkey;
   const int row = blockIdx.x;
   const int b = row / N, n = row % N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -541,12 +543,36 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
   const int per = (nb + gridDim.y - 1) / gridDim.y;
   const int blk0 = blockIdx.y * per, blk1 = min(nb, blk0 + per);
   if (blk0 >= blk1) return;
-  if (n >= num_nodes[b]) {   // R was cleared by the greedy pass
+  const bool valid = n < num_nodes[b];
+  float m;
+  if (S > 1) {
+    // the greedy pass left S slice keys per row: merged here, as its merge
+    // kernel would (largest packed key: argmax and max), and written once
+    if (wave == 0) {
+      uint64_t key = 0;
+      for (int k = lane; k < S; k += kWave) {
+        const uint64_t kk = ws_key[static_cast<long>(row) * S + k];
+        key = kk > key ? kk : key;
+      }
+      key = wave_max_u64(key);
+      if (lane == 0) {
+        s_rowkey = key;
+        if (blockIdx.y == 0) {
+          argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
+          maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
+        }
+      }
+    }
+    __syncthreads();
+    m = unord_f32(static_cast<uint32_t>(s_rowkey >> 32));
+  } else {
+    m = maxv[row];
+  }
+  if (!valid) {   // R was cleared by the greedy pass
     if (Rb)
       for (int k = blk0 + tid; k < blk1; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
     return;
   }
-  const float m = maxv[row];
   const uint16_t* rp = logits + static_cast<long>(row) * V;
   auto load_block = [&](int blk, u32x4_t (&dst)[kQ]) {
 #pragma unroll
@@ -727,7 +753,7 @@ size_t greedy_ws_bytes(int rows, int S) {
 template <typename T>
 void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
                    int S, int chunk, void* ws, int32_t* am, float* mx, float* lse,
-                   uint64_t* zero_R = nullptr) {
+                   uint64_t* zero_R = nullptr, bool merge = true) {
   uint64_t* ws_key = static_cast<uint64_t*>(ws);
   float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<size_t>(rows) * S);
   const dim3 grid(S, rows);
@@ -739,7 +765,7 @@ void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, c
     hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
                        static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
                        lse, zero_R);
-  if (S > 1) {
+  if (S > 1 && merge) {
     if (lse)
       hipLaunchKernelGGL((finalize_kernel<true>), dim3(rows), dim3(kWave), 0, st, N, nn, S, ws_key,
                          ws_ms, am, mx, lse);
@@ -792,7 +818,7 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
                                       aligned16(workspace)));
     if (streamed) {
       launch_greedy<uint16_t>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
-                              maxv, nullptr, R);
+                              maxv, nullptr, R, /*merge=*/false);
       // two workgroups per row while the rows fill under two rounds of the
       // chip's 512 slots (batched: 528 rows 87 -> 83 us); with many rounds the
       // second table fill per row costs more than the balance gains (ragged:
@@ -800,8 +826,8 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
       const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
       const int halves = nb > 1 && rows < 1024 ? 2 : 1;
       hipLaunchKernelGGL(wsum_kernel, dim3(rows, halves), dim3(kRowThreads), 0, stream,
-                         static_cast<const uint16_t*>(logits), N, V, num_nodes, wc, maxv, R,
-                         R_blocks);
+                         static_cast<const uint16_t*>(logits), N, V, num_nodes, wc, S,
+                         static_cast<const uint64_t*>(workspace), argmax, maxv, R, R_blocks);
     } else if (dtype == DDTREE_BF16)
       launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R,
                                 R_blocks, lse);
