@@ -103,8 +103,8 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
   __shared__ int32_t s_tok[kMaxN], s_fc[kMaxN], s_ns[kMaxN];
   __shared__ int32_t s_rej[DDTREE_MAX_TOPK];
   __shared__ uint64_t s_wave[kSampleWaves];
-  __shared__ int s_nrej, s_cur, s_a, s_blk, s_found_thread;
-  __shared__ uint64_t s_trem, s_found_excl;
+  __shared__ int s_nrej, s_cur, s_a, s_blk;
+  __shared__ uint64_t s_trem;
   __shared__ uint64_t s_tab[sizeof(T) == 2 ? kTabEntries : 1];
 
   const int b = blockIdx.x;
@@ -142,7 +142,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
     s_u0[j] = uniforms[(base + j) * 2 + 0];
     s_u1[j] = uniforms[(base + j) * 2 + 1];
   }
-  if (tid == 0) s_found_thread = -1;
   __syncthreads();
 
   if (wave == 0) {
