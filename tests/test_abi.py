@@ -102,6 +102,21 @@ def test_host_validation_rejects_bad_arguments():
                                    None, None, 0, None) == 1
     # walks
     assert lib.ddtree_verify_greedy(ctypes.byref(t), None, fake, fake, fake, fake, None) == 1
+    # vocabulary reduction + greedy walk in one call
+    vvg = lib.ddtree_vocab_verify_greedy
+    assert vvg(None, 1, 100, ctypes.byref(t), fake, fake, fake, fake, fake, fake, fake, 1 << 20,
+               None) == 1                                                      # null logits
+    assert vvg(fake, 1, 0, ctypes.byref(t), fake, fake, fake, fake, fake, fake, fake, 1 << 20,
+               None) == 1                                                      # V < 1
+    assert vvg(fake, 7, 100, ctypes.byref(t), fake, fake, fake, fake, fake, fake, fake, 1 << 20,
+               None) == 1                                                      # dtype
+    assert vvg(fake, 1, 163840, ctypes.byref(t), fake, fake, fake, fake, fake, fake, None, 0,
+               None) == 1                                                      # split rows, no workspace
+    assert vvg(fake, 1, 100, ctypes.byref(t), fake, fake, None, fake, fake, fake, fake, 1 << 20,
+               None) == 1                                                      # null accept_len
+    bad = _fake_tree(N=200)
+    assert vvg(fake, 1, 100, ctypes.byref(bad), fake, fake, fake, fake, fake, fake, fake, 1 << 20,
+               None) == 1                                                      # N > 128
     assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, fake, 0.0, fake,
                                     fake, fake, fake, fake, None) == 1      # T <= 0
     assert lib.ddtree_verify_sample(ctypes.byref(t), fake, 1, 100, fake, fake, None, 0.7, fake,
