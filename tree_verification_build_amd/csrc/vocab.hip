@@ -513,17 +513,18 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
   }
 }
 
-// Sampling weights of bf16 rows whose maximum is already known (from the
-// greedy pass: the same maximum and lowest index the sampling row kernel
-// finds; when that pass split the rows, this kernel merges its slice keys and
-// writes argmax and max itself, which saves the merge kernel's launch).  With m known the row need not stay in registers: one or two
-// 1024-thread workgroups per row (two take half of the row's blocks each, so
-// that 528 rows do not leave a second round of 16 on 512 workgroup slots)
-// stream it block by block (DDTREE_R_BLOCK tokens, four 16-byte vectors per thread, the next
-// block's loads in flight while the current one is weighed); two workgroups
-// share a CU, and the loads of one overlap the arithmetic of the other.  Weights come from the LDS table of
-// weight() (common.hpp); a logit outside its window is re-read and weighed
-// with weight() itself.
+// Sampling weights of bf16 rows whose maximum is already known from the greedy
+// pass (the same maximum and lowest index the sampling row kernel finds; when
+// that pass split the rows, this kernel merges their slice keys and writes
+// argmax and max itself, which saves the merge kernel's launch).  With m
+// known the row need not stay in registers: one or two 1024-thread workgroups
+// per row (two take half of the row's blocks each, so that 528 rows do not
+// leave a second round of 16 on 512 workgroup slots) stream it block by block
+// (DDTREE_R_BLOCK tokens, four 16-byte vectors per thread, the next block's
+// loads in flight while the current one is weighed); two workgroups share a
+// CU, and the loads of one overlap the arithmetic of the other.  Weights come
+// from the LDS table of weight() (common.hpp); a logit outside its window is
+// re-read and weighed with weight() itself.
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void wsum_kernel(
     const uint16_t* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
     WeightConsts wc, int S, const uint64_t* __restrict__ ws_key, int32_t* __restrict__ argmax,
@@ -625,7 +626,8 @@ __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 
       if (Rb) Rb[static_cast<long>(row) * nb + blk0 + lane] = bt;
     }
     const uint64_t tot = wave_sum_u64(bt);
-    if (lane == 0) atomicAdd(reinterpret_cast<unsigned long long*>(R + row), static_cast<unsigned long long>(tot));
+    if (lane == 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(R + row), static_cast<unsigned long long>(tot));
   }
 }
 
