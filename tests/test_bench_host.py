@@ -1,0 +1,54 @@
+"""bench.py's host logic (no GPU): the algorithmic bytes behind roofline.achieved,
+the HBM-traffic figure's source check, and the one-GPU guard."""
+import os
+import subprocess
+import sys
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_algorithmic_bytes_single_workload():
+    cfg = workloads.config("single")
+    ctx = 8192
+    b = bench.algorithmic_bytes(cfg, ctx)
+    # context K and V once: 2 tensors x 8192 keys x 8 KV heads x 128 dims x 2 bytes
+    kv = 2 * 8192 * 8 * 128 * 2
+    # tree q and out (8 query heads) and tree k, v (8 KV heads): 33 nodes x 128 dims x 2 bytes
+    tree = 33 * 128 * 2 * (8 + 8 + 8 + 8)
+    assert b["attention"] == kv + tree == 33_824_768
+    # every node's target row once: 33 x 163840 bf16 logits
+    assert b["vocab"] == 33 * 163840 * 2 == 10_813_440
+    assert b["residual"] == 0                      # greedy: no residual row
+    assert b["total"] == b["attention"] + b["vocab"]
+
+
+def test_algorithmic_bytes_sampling_adds_one_residual_row_per_request():
+    cfg = workloads.config("batched")
+    b = bench.algorithmic_bytes(cfg, 16 * 4096)
+    assert b["residual"] == 16 * 163840 * 2
+    assert b["vocab"] == 16 * 33 * 163840 * 2
+    assert b["attention"] == 2 * 16 * 4096 * 8 * 128 * 2 + 16 * 33 * 128 * 2 * 32
+
+
+def test_traffic_figure_only_for_the_profiled_source():
+    # the committed profile names the attention source it was measured on
+    prof = open(bench.TRAFFIC_PROFILE).read()
+    digest = [l.split(":", 1)[1].strip() for l in prof.splitlines()
+              if l.startswith("source_digest:")][0]
+    t = bench.measured_traffic("single")
+    if bench.attention_source_digest() == digest:
+        assert isinstance(t, int) and t > bench.algorithmic_bytes(
+            workloads.config("single"), 8192)["attention"]
+    else:
+        assert t is None
+    assert bench.measured_traffic("batched") is None   # no counters for that workload
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
