@@ -438,7 +438,12 @@ def run_copy_calibration(mib, reps=20):
             "copy_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "tree_attention_single_hbm_traffic.md")
+def traffic_profile(cfg_name):
+    """The committed counter summary of the tree-attention call on this workload."""
+    return os.path.join(ROOT, "profiles", f"tree_attention_{cfg_name}_hbm_traffic.md")
+
+
+TRAFFIC_PROFILE = traffic_profile("single")
 
 
 def attention_source_digest():
@@ -451,7 +456,7 @@ def measured_traffic(cfg_name):
     """HBM bytes per tree-attention call from the committed counter summary, or
     None when it covers another workload or an older attention source."""
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(traffic_profile(cfg_name)).read()
     except OSError:
         return None
     vals = dict(line.split(":", 1) for line in text.splitlines()

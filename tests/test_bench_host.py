@@ -34,17 +34,22 @@ def test_algorithmic_bytes_sampling_adds_one_residual_row_per_request():
 
 
 def test_traffic_figure_only_for_the_profiled_source():
-    # the committed profile names the attention source it was measured on
-    prof = open(bench.TRAFFIC_PROFILE).read()
-    digest = [l.split(":", 1)[1].strip() for l in prof.splitlines()
-              if l.startswith("source_digest:")][0]
-    t = bench.measured_traffic("single")
-    if bench.attention_source_digest() == digest:
-        assert isinstance(t, int) and t > bench.algorithmic_bytes(
-            workloads.config("single"), 8192)["attention"]
-    else:
-        assert t is None
-    assert bench.measured_traffic("batched") is None   # no counters for that workload
+    # each committed profile names its workload and the attention source it was measured on
+    for name in ("single", "batched", "long", "ragged"):
+        path = bench.traffic_profile(name)
+        if not os.path.exists(path):
+            assert bench.measured_traffic(name) is None
+            continue
+        prof = open(path).read()
+        digest = [l.split(":", 1)[1].strip() for l in prof.splitlines()
+                  if l.startswith("source_digest:")][0]
+        assert ("workload: " + name) in prof
+        t = bench.measured_traffic(name)
+        if bench.attention_source_digest() == digest:
+            assert isinstance(t, int) and t > 0
+        else:
+            assert t is None
+    assert bench.measured_traffic("tiny") is None   # no counters for that workload
 
 
 def test_more_than_one_gpu_is_refused():
