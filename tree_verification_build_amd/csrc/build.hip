@@ -86,7 +86,10 @@ __device__ __forceinline__ float put_lane(float old, float val, int lane) {
                                                      __builtin_bit_cast(int, old)));
 }
 
-template <int REGS, bool TWO>
+// TWO: node records in two register sets (N > 64); SLOTS2: the frontier's
+// slots too (N > 65: with N = 65 the last pop writes slot 64, which no pop
+// reads, so the frontier fits one set).
+template <int REGS, bool TWO, bool SLOTS2>
 __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ draft_lp,
                                                    const int32_t* __restrict__ draft_tok,
                                                    const int32_t* __restrict__ root_tok,
@@ -174,12 +177,12 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
   for (int i = 1; i < total; ++i) {
     float cs0, ss0, cs1 = 0.0f, ss1 = 0.0f;
     offers(kl0, ks0, rs0, cs0, ss0);
-    if (TWO) offers(kl1, ks1, rs1, cs1, ss1);
+    if (SLOTS2) offers(kl1, ks1, rs1, cs1, ss1);
     // the best slot: largest key; the high word (score) decides unless tied
     uint32_t mh = kh0, ml = kl0;
     float mcs = cs0, mss = ss0, mks = ks0;
     bool in1 = false;
-    if (TWO) {
+    if (SLOTS2) {
       in1 = ((static_cast<uint64_t>(kh1) << 32) | kl1) > ((static_cast<uint64_t>(kh0) << 32) | kl0);
       mh = in1 ? kh1 : kh0;
       ml = in1 ? kl1 : kl0;
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
     const float cs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mcs), w));
     const float ss = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mss), w));
     const float sc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mks), w));
-    const int parent = TWO ? w + 64 * (__builtin_amdgcn_readlane(in1 ? 1 : 0, w) & 1) : w;
+    const int parent = SLOTS2 ? w + 64 * (__builtin_amdgcn_readlane(in1 ? 1 : 0, w) & 1) : w;
     const int depth = static_cast<int>((lo >> 8) & 0xFF);
     // node i = the taken offer; slot i gets node i's best child, slot parent
     // the parent's next child
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
       kl1 = put_lane(kl1, lo_c, il);
       ks1 = put_lane(ks1, cs, il);
     }
-    if (!TWO || parent < 64) {
+    if (!SLOTS2 || parent < 64) {
       kh0 = put_lane(kh0, sh, pl);
       kl0 = put_lane(kl0, lo_s, pl);
       ks0 = put_lane(ks0, ss, pl);
@@ -349,20 +352,22 @@ extern "C" ddtree_status ddtree_build(const float* draft_lp, const int32_t* draf
     return fail(DDTREE_EINVAL, "ddtree_build: tree sizes do not match B/D/K/budget");
   if (D * K > 256)
     return fail(DDTREE_EUNSUPPORTED, "ddtree_build: depth * top-k = %d exceeds 256", D * K);
-  const bool small_table = D * K <= 64, one_list = budget + 1 <= 64;
+  const bool small_table = D * K <= 64, one_list = budget + 1 <= 64,
+             one_frontier = budget + 1 <= 65;
   const dim3 g(B), blk(kWave);
   const size_t lds = static_cast<size_t>(D + 2) * kRow * sizeof(float);
-  if (small_table && one_list)
-    hipLaunchKernelGGL((build_kernel<1, false>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
-                       prefix_len, D, K, budget, *tree);
-  else if (small_table)
-    hipLaunchKernelGGL((build_kernel<1, true>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
-                       prefix_len, D, K, budget, *tree);
-  else if (one_list)
-    hipLaunchKernelGGL((build_kernel<4, false>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
-                       prefix_len, D, K, budget, *tree);
-  else
-    hipLaunchKernelGGL((build_kernel<4, true>), g, blk, lds, stream, draft_lp, draft_tok, root_tok,
-                       prefix_len, D, K, budget, *tree);
+#define DDT_BUILD(R_, T_, S_)                                                                  \
+  hipLaunchKernelGGL((build_kernel<R_, T_, S_>), g, blk, lds, stream, draft_lp, draft_tok,     \
+                     root_tok, prefix_len, D, K, budget, *tree)
+  if (small_table) {
+    if (one_list) DDT_BUILD(1, false, false);
+    else if (one_frontier) DDT_BUILD(1, true, false);
+    else DDT_BUILD(1, true, true);
+  } else {
+    if (one_list) DDT_BUILD(4, false, false);
+    else if (one_frontier) DDT_BUILD(4, true, false);
+    else DDT_BUILD(4, true, true);
+  }
+#undef DDT_BUILD
   return check_launch("ddtree_build");
 }
