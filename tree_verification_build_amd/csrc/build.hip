@@ -43,13 +43,16 @@ __device__ __forceinline__ uint64_t make_key_bits(uint32_t ord_score, int parent
 
 // Maximum over the wavefront with DPP: within each row of 16 lanes (quad_perm
 // swaps, row_ror 4 and 8), then row_bcast15 / row_bcast31 carry the running
-// maximum into the last row; lane 63 ends with the total.
+// maximum into the last row; lane 63 ends with the total.  HALF: only lanes
+// 0-31 hold candidates, so row_bcast15 alone brings their maximum to lane 31.
+template <bool HALF = false>
 __device__ __forceinline__ uint32_t wave_max_bcast_u32(uint32_t v) {
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xF, 0xF, false)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xF, 0xF, false)));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x142, 0xA, 0xF, false)));
+  if constexpr (HALF) return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 31));
   v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x143, 0xC, 0xF, false)));
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(v, 63));
 }
@@ -88,8 +91,9 @@ __device__ __forceinline__ float put_lane(float old, float val, int lane) {
 
 // TWO: node records in two register sets (N > 64); SLOTS2: the frontier's
 // slots too (N > 65: with N = 65 the last pop writes slot 64, which no pop
-// reads, so the frontier fits one set).
-template <int REGS, bool TWO, bool SLOTS2>
+// reads, so the frontier fits one set); HALF: N <= 33, so the slots a pop
+// reads (0 .. N - 2) lie in lanes 0-31.
+template <int REGS, bool TWO, bool SLOTS2, bool HALF>
 __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ draft_lp,
                                                    const int32_t* __restrict__ draft_tok,
                                                    const int32_t* __restrict__ root_tok,
@@ -190,11 +194,11 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
       mss = in1 ? ss1 : ss0;
       mks = in1 ? ks1 : ks0;
     }
-    const uint32_t bh = wave_max_bcast_u32(mh);
+    const uint32_t bh = wave_max_bcast_u32<HALF>(mh);
     const uint64_t tied = __ballot(mh == bh);
     int w = __builtin_ctzll(tied);
     if (__builtin_expect(__builtin_popcountll(tied) > 1, 0))
-      w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32(mh == bh ? ml : 0u)));
+      w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32<HALF>(mh == bh ? ml : 0u)));
     // readlane yields a signed int: cast before widening, or the low word sign-extends
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(ml, w));
     const float cs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mcs), w));
@@ -353,20 +357,22 @@ extern "C" ddtree_status ddtree_build(const float* draft_lp, const int32_t* draf
   if (D * K > 256)
     return fail(DDTREE_EUNSUPPORTED, "ddtree_build: depth * top-k = %d exceeds 256", D * K);
   const bool small_table = D * K <= 64, one_list = budget + 1 <= 64,
-             one_frontier = budget + 1 <= 65;
+             one_frontier = budget + 1 <= 65, half = budget + 1 <= 33;
   const dim3 g(B), blk(kWave);
   const size_t lds = static_cast<size_t>(D + 2) * kRow * sizeof(float);
-#define DDT_BUILD(R_, T_, S_)                                                                  \
-  hipLaunchKernelGGL((build_kernel<R_, T_, S_>), g, blk, lds, stream, draft_lp, draft_tok,     \
+#define DDT_BUILD(R_, T_, S_, H_)                                                              \
+  hipLaunchKernelGGL((build_kernel<R_, T_, S_, H_>), g, blk, lds, stream, draft_lp, draft_tok, \
                      root_tok, prefix_len, D, K, budget, *tree)
   if (small_table) {
-    if (one_list) DDT_BUILD(1, false, false);
-    else if (one_frontier) DDT_BUILD(1, true, false);
-    else DDT_BUILD(1, true, true);
+    if (half) DDT_BUILD(1, false, false, true);
+    else if (one_list) DDT_BUILD(1, false, false, false);
+    else if (one_frontier) DDT_BUILD(1, true, false, false);
+    else DDT_BUILD(1, true, true, false);
   } else {
-    if (one_list) DDT_BUILD(4, false, false);
-    else if (one_frontier) DDT_BUILD(4, true, false);
-    else DDT_BUILD(4, true, true);
+    if (half) DDT_BUILD(4, false, false, true);
+    else if (one_list) DDT_BUILD(4, false, false, false);
+    else if (one_frontier) DDT_BUILD(4, true, false, false);
+    else DDT_BUILD(4, true, true, false);
   }
 #undef DDT_BUILD
   return check_launch("ddtree_build");
