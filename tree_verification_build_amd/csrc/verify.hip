@@ -310,6 +310,25 @@ __device__ __forceinline__ void lazy_load16(const T* row, long i, int V, bool ve
   }
 }
 
+// loads in flight per thread in the lazy walk's maximum pass
+constexpr int kLazyU = 4;
+
+// 16 bytes of -inf (past the row end) and the floats of 16 raw bytes
+template <typename T>
+__device__ __forceinline__ u32x4_t lazy_neg_inf() {
+  const uint32_t z = sizeof(T) == 2 ? 0xFF80FF80u : 0xFF800000u;
+  return u32x4_t{z, z, z, z};
+}
+template <typename T>
+__device__ __forceinline__ void lazy_unpack(const u32x4_t& w, float* v) {
+  constexpr int E = Elem<T>::kPer16;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (E == 8) v[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    else v[e] = __uint_as_float(w[e]);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
     ddtree_tree t, const T* __restrict__ logits, int V, WeightConsts wc,
@@ -381,12 +400,32 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
     const bool vec = aligned16(row) && (V % E == 0);
     // the row maximum (float maximum; -0 read as +0, as in the vocab pass)
     float vmax = -__builtin_huge_valf();
-#pragma unroll 8
-    for (int p = 0; p < npass; ++p) {   // unrolled: eight 16-byte loads in flight per thread
-      float v[E];
-      lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
+    if (vec) {
+      // whole 16-byte vectors (V is a multiple of E): kLazyU loads in flight
+      // per thread, then their maxima
+      for (int p0 = 0; p0 < npass; p0 += kLazyU) {
+        u32x4_t raw[kLazyU];
 #pragma unroll
-      for (int e = 0; e < E; ++e) vmax = max(vmax, v[e]);
+        for (int u = 0; u < kLazyU; ++u) {
+          const long i = static_cast<long>(p0 + u) * kPass + static_cast<long>(tid) * E;
+          raw[u] = p0 + u < npass && i < V ? *reinterpret_cast<const u32x4_t*>(row + i)
+                                           : lazy_neg_inf<T>();
+        }
+#pragma unroll
+        for (int u = 0; u < kLazyU; ++u) {
+          float v[E];
+          lazy_unpack<T>(raw[u], v);
+#pragma unroll
+          for (int e = 0; e < E; ++e) vmax = max(vmax, v[e]);
+        }
+      }
+    } else {
+      for (int p = 0; p < npass; ++p) {
+        float v[E];
+        lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) vmax = max(vmax, v[e]);
+      }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) vmax = max(vmax, shfl_xor_f32(vmax, o));
@@ -403,20 +442,36 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
     }
     // the weights, summed per block of DDTREE_R_BLOCK tokens
     uint64_t bsum = 0;
-#pragma unroll 4
-    for (int p = 0; p < npass; ++p) {
-      float v[E];
-      lazy_load16<T>(row, static_cast<long>(p) * kPass + static_cast<long>(tid) * E, V, vec, v);
+    // one block of passes at a time (kPassPerBlock vectors per thread), its
+    // loads issued together when the row is whole vectors
+    for (int p0 = 0; p0 < npass; p0 += kPassPerBlock) {
+      float v[kPassPerBlock][E];
+      if (vec) {
+        u32x4_t raw[kPassPerBlock];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        bsum += wt(v[e]);
-        if (e & 1) __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < kPassPerBlock; ++u) {
+          const long i = static_cast<long>(p0 + u) * kPass + static_cast<long>(tid) * E;
+          raw[u] = p0 + u < npass && i < V ? *reinterpret_cast<const u32x4_t*>(row + i)
+                                           : lazy_neg_inf<T>();
+        }
+#pragma unroll
+        for (int u = 0; u < kPassPerBlock; ++u) lazy_unpack<T>(raw[u], v[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kPassPerBlock; ++u)
+          lazy_load16<T>(row, static_cast<long>(p0 + u) * kPass + static_cast<long>(tid) * E, V,
+                         vec, v[u]);
       }
-      if ((p + 1) % kPassPerBlock == 0 || p == npass - 1) {
-        const uint64_t ws = wave_sum_u64(bsum);
-        if (lane == 0) s_blkw[p / kPassPerBlock][wave] = ws;
-        bsum = 0;
-      }
+#pragma unroll
+      for (int u = 0; u < kPassPerBlock; ++u)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          bsum += wt(v[u][e]);
+          if (e & 1) __builtin_amdgcn_sched_barrier(0);
+        }
+      const uint64_t ws = wave_sum_u64(bsum);
+      if (lane == 0) s_blkw[p0 / kPassPerBlock][wave] = ws;
+      bsum = 0;
     }
     __syncthreads();
     if (tid < nb) {
