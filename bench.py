@@ -1,28 +1,36 @@
-"""Benchmark: DDTree tree-verify steps/s on one MI355X.
+"""Benchmark: DDTree tree-verify steps/s on one MI355X, every workload.
 
 One step = ddtree_build -> ddtree_tree_attention -> ddtree_vocab_reduce ->
 ddtree_verify_greedy (or ddtree_verify_sample when the workload samples), then
 accept_len and bonus reaching the host and a stream synchronisation (the
-serving loop's per-step sync).  By default the walk kernel stores the two
-results straight into pinned host memory and the host busy-polls for the
-synchronisation; --result-copy adds an explicit device-to-host copy instead,
---host-wait auto sleeps until signalled.  By default each step is a captured HIP
-graph replayed once per step (--eager launches every call from Python).  Inputs are seeded synthetic tensors of
-the workload's shapes, resident in HBM before timing starts; several copies
-of the input set are rotated so that consecutive steps do not find their
+serving loop's per-step sync).  The walk kernel stores the two results straight
+into pinned host memory and the host busy-polls for the synchronisation
+(--result-copy adds an explicit device-to-host copy instead, --host-wait auto
+sleeps until signalled).  Each step is a captured HIP graph replayed once per
+step (--eager launches every call from Python).  Inputs are seeded synthetic
+tensors of the workload's shapes, resident in HBM before timing starts; several
+copies of the input set are rotated so that consecutive steps do not find their
 inputs in the 256 MB last-level cache.
 
 The build's inputs are the draft top-K of the synthetic draft logits, computed
 once with ddtree_draft_topk before timing (the draft side of a real step); the
 same call is timed on its own and reported as "draft_topk" (not in the step).
 
-Prints one JSON line: steps/s, a roofline entry for the tree-attention call
-(algorithmic bytes / measured duration vs 8 TB/s), and the CPU oracle timed on
-the host cores for the same workload.
+Default run (--config all): the single-request workload gives the headline
+line's fields (value, roofline, cpu_baseline); every workload (tiny, single,
+batched, long, ragged) also gets an entry in "configs" with its steps/s,
+kernel rooflines and CPU baseline.  Timing protocol per workload: --warmup
+untimed steps, then --reps repetitions of exactly --steps synchronised steps
+(value = median rate); a sustained figure times repetitions of at least
+max(--steps, 200) steps and 1 s each; kernel durations come from HIP events
+around graphs of back-to-back calls on the calls' stream.  The CPU baseline is
+the oracle on a bounded sample of the same workload, timed single-threaded on
+one core and on all cores of the process's affinity set.
 """
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +43,9 @@ METRIC = "tree-verify steps/s at 1 GPU (budget=32); KV+vocab HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15         # dense bf16
 MFMA_F32_PEAK = 157.3e12
+HEADLINE = "single"
+ALL_CONFIGS = ("tiny", "single", "batched", "long", "ragged")
+TOP_P = 0.9   # nucleus mass of the top-p figure (sampling workloads)
 
 
 def describe(cfg):
@@ -75,267 +86,275 @@ def set_host_wait(mode):
         return "auto"
 
 
-TOP_P = 0.9   # nucleus mass of the top-p figure (sampling workloads)
+def summary(rates):
+    """Median, spread and count of per-repetition rates."""
+    return {"median": round(statistics.median(rates), 2), "min": round(min(rates), 2),
+            "max": round(max(rates), 2), "reps": len(rates)}
 
 
-def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
-    import torch
-    import tree_verification_build_amd as lib
-    import workloads
+# ---------------------------------------------------------------------------- GPU side
 
-    dev = "cuda:0"
-    inp = workloads.make_inputs(cfg)
-    tot_ctx = int(inp["ctx_offsets"][-1])
+class Workload:
+    """Device inputs, buffers and the step functions of one workload."""
 
-    def d(x, dt=None):
+    def __init__(self, cfg, rotate, result_copy=False):
+        import torch
+        import tree_verification_build_amd as lib
+        import workloads
+        self.cfg, self.lib, self.torch = cfg, lib, torch
+        dev = self.dev = "cuda:0"
+        inp = self.inp = workloads.make_inputs(cfg)
+        self.total_ctx = int(inp["ctx_offsets"][-1])
+        d = self.d
+        base = {k: d(inp[k], cfg.dtype) for k in ("q", "k_ctx", "v_ctx", "k_tree", "v_tree")}
+        small = self.small = {k: d(inp[k]) for k in ("root_tok", "prefix_len", "ctx_offsets",
+                                                     "uniforms")}
+        # the build's inputs: the draft top-K of the first D draft rows, computed on the
+        # GPU over every row (the target-logit planting reads the draft ranking)
+        dl = self.draft_logits = d(inp["draft_logits"])
+        tok_all, lp_all = lib.ddtree_draft_topk(dl, cfg.K)
+        torch.cuda.synchronize()
+        self.tok_all = tok_all
+        inp["draft_tok_all"] = tok_all.cpu().numpy()
+        small["draft_tok"] = tok_all[:, :cfg.D].contiguous()
+        small["draft_lp"] = lp_all[:, :cfg.D].contiguous()
+        # the target logits depend on the tree shape: build it once on the GPU
+        t0 = lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
+                              small["prefix_len"], cfg.budget)
+        torch.cuda.synchronize()
+        tn = t0.to_numpy()
+        logits_np, _ = workloads.make_target_logits(cfg, inp, tn["depth"], tn["num_nodes"])
+        base["logits"] = d(logits_np, cfg.dtype)
+        del logits_np
+        self.rotate = rotate
+        self.sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(rotate - 1)]
+        self.tree = lib.alloc_tree(cfg.B, cfg.budget, cfg.D, cfg.K, dev)
+        # accept_len and bonus land in pinned host memory, written by the walk kernel
+        # itself (the device-to-host transfer is its stores); with result_copy they stay
+        # on the device and one copy per step brings them over
+        self.result_copy = result_copy
+        if result_copy:
+            self.result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
+            self.host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
+        else:
+            self.result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
+            self.host_result = self.result
+        self.outputs = {"accept_len": self.result[0],
+                        "path_nodes": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32,
+                                                  device=dev),
+                        "out_tokens": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32,
+                                                  device=dev),
+                        "bonus": self.result[1]}
+        self.attn_out = torch.empty_like(base["q"])
+        self.ws_a = torch.empty(max(16, lib.ddtree_tree_attention_workspace_size(
+            cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, inp["ctx_offsets"])), dtype=torch.uint8,
+            device=dev)
+        self.ws_v = torch.empty(max(16, lib.ddtree_vocab_reduce_workspace_size(
+            cfg.B, cfg.N, cfg.V)), dtype=torch.uint8, device=dev)
+        self.f_am = torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev)
+        self.f_mx = torch.empty((cfg.B, cfg.N), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.nuc = None
+
+    def d(self, x, dt=None):
+        torch = self.torch
         x = np.ascontiguousarray(x)
         if dt == "bf16":
-            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(x.view(np.int64) if x.dtype == np.uint64 else x).to(dev)
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        return torch.from_numpy(x.view(np.int64) if x.dtype == np.uint64 else x).to(self.dev)
 
-    base = {k: d(inp[k], cfg.dtype) for k in ("q", "k_ctx", "v_ctx", "k_tree", "v_tree")}
-    small = {k: d(inp[k]) for k in ("root_tok", "prefix_len", "ctx_offsets", "uniforms")}
-    # the build's inputs: the draft top-K of the first D draft rows, computed on the
-    # GPU over every row (the target-logit planting reads the draft ranking)
-    dl = d(inp["draft_logits"])
-    tok_all, lp_all = lib.ddtree_draft_topk(dl, cfg.K)
-    torch.cuda.synchronize()
-    inp["draft_tok_all"] = tok_all.cpu().numpy()
-    small["draft_tok"] = tok_all[:, :cfg.D].contiguous()
-    small["draft_lp"] = lp_all[:, :cfg.D].contiguous()
-    # the target logits depend on the tree shape: build it once on the GPU
-    t0 = lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
-                          small["prefix_len"], cfg.budget)
-    torch.cuda.synchronize()
-    tn = t0.to_numpy()
-    logits_np, _ = workloads.make_target_logits(cfg, inp, tn["depth"], tn["num_nodes"])
-    base["logits"] = d(logits_np, cfg.dtype)
-    del logits_np
+    # -- the calls of a step
+    def build(self):
+        s = self.small
+        self.lib.ddtree_build(s["draft_lp"], s["draft_tok"], s["root_tok"], s["prefix_len"],
+                              self.cfg.budget, tree=self.tree)
 
-    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(rotate - 1)]
-    tree = lib.alloc_tree(cfg.B, cfg.budget, cfg.D, cfg.K, dev)
-    # accept_len and bonus land in pinned host memory, written by the walk
-    # kernel itself (the device-to-host transfer is its stores); with
-    # --result-copy they stay on the device and one copy per step brings them over
-    if result_copy:
-        result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
-    else:
-        result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
-    outputs = {"accept_len": result[0],
-               "path_nodes": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
-               "out_tokens": torch.empty((cfg.B, cfg.D + 1), dtype=torch.int32, device=dev),
-               "bonus": result[1]}
-    attn_out = torch.empty_like(base["q"])
-    ws_a = torch.empty(max(16, lib.ddtree_tree_attention_workspace_size(
-        cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, inp["ctx_offsets"])), dtype=torch.uint8,
-        device=dev)
-    ws_v = torch.empty(max(16, lib.ddtree_vocab_reduce_workspace_size(cfg.B, cfg.N, cfg.V)),
-                       dtype=torch.uint8, device=dev)
-    host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True) if result_copy \
-        else result
-    stream = torch.cuda.current_stream()
-    T = cfg.temperature
+    def attention(self, s):
+        self.lib.ddtree_tree_attention(s["q"], s["k_ctx"], s["v_ctx"], self.small["ctx_offsets"],
+                                       self.inp["ctx_offsets"], s["k_tree"], s["v_tree"],
+                                       self.tree, out=self.attn_out, workspace=self.ws_a)
 
-    def attention(s):
-        lib.ddtree_tree_attention(s["q"], s["k_ctx"], s["v_ctx"], small["ctx_offsets"],
-                                  inp["ctx_offsets"], s["k_tree"], s["v_tree"], tree,
-                                  out=attn_out, workspace=ws_a)
+    def vocab(self, s):
+        return self.lib.ddtree_vocab_reduce(s["logits"], self.tree.num_nodes,
+                                            self.cfg.temperature, workspace=self.ws_v)
 
-    def vocab(s):
-        return lib.ddtree_vocab_reduce(s["logits"], tree.num_nodes, T, workspace=ws_v)
-
-    def step(i):
-        s = sets[i % rotate]
-        lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
-                         small["prefix_len"], cfg.budget, tree=tree)
-        attention(s)
-        v = vocab(s)
+    def step(self, i):
+        """build -> attention -> vocabulary reduction -> walk (the survey's step)."""
+        s = self.sets[i % self.rotate]
+        lib, T = self.lib, self.cfg.temperature
+        self.build()
+        self.attention(s)
+        v = self.vocab(s)
         if T > 0:
-            lib.ddtree_verify_sample(tree, s["logits"], v["maxv"], v["R"], v["R_blocks"], T,
-                                     small["uniforms"], outputs=outputs)
+            lib.ddtree_verify_sample(self.tree, s["logits"], v["maxv"], v["R"], v["R_blocks"], T,
+                                     self.small["uniforms"], outputs=self.outputs)
         else:
-            lib.ddtree_verify_greedy(tree, v["argmax"], outputs=outputs)
-        if result_copy:
-            host_result.copy_(result, non_blocking=True)
+            lib.ddtree_verify_greedy(self.tree, v["argmax"], outputs=self.outputs)
+        if self.result_copy:
+            self.host_result.copy_(self.result, non_blocking=True)
 
-    for i in range(warmup):
-        step(i)
-        stream.synchronize()
-    torch.cuda.synchronize()
-    if graph:
-        # one captured step per input set; replaying it is the serving loop
-        graphs = []
-        for i in range(rotate):
+    def step_fused(self, i):
+        """greedy: the vocabulary reduction and the walk in one call."""
+        s = self.sets[i % self.rotate]
+        self.build()
+        self.attention(s)
+        self.lib.ddtree_vocab_verify_greedy(s["logits"], self.tree, workspace=self.ws_v,
+                                            outputs=self.outputs, argmax=self.f_am,
+                                            maxv=self.f_mx)
+
+    def step_lazy(self, i):
+        """sampling: the walk reduces only the target rows it visits."""
+        s = self.sets[i % self.rotate]
+        self.build()
+        self.attention(s)
+        self.lib.ddtree_verify_sample_lazy(self.tree, s["logits"], self.cfg.temperature,
+                                           self.small["uniforms"], outputs=self.outputs)
+
+    def step_topp(self, i):
+        """sampling with top-p nuclei: vocabulary pass, nucleus per node, walk."""
+        s = self.sets[i % self.rotate]
+        lib, T = self.lib, self.cfg.temperature
+        self.build()
+        self.attention(s)
+        v = self.vocab(s)
+        self.nuc = lib.ddtree_vocab_top_p(s["logits"], self.tree.num_nodes, v["maxv"], v["R"], T,
+                                          TOP_P, outputs=self.nuc)
+        lib.ddtree_verify_sample_top_p(self.tree, s["logits"], v["maxv"], self.nuc, T,
+                                       self.small["uniforms"], outputs=self.outputs)
+
+    # -- timing helpers
+    def graphs_of(self, fn):
+        """One captured graph per input set; replaying graph i % rotate is step i."""
+        torch = self.torch
+        gs = []
+        for i in range(self.rotate):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(i)
-            graphs.append(g)
+                fn(i)
+            gs.append(g)
         torch.cuda.synchronize()
-        for i in range(warmup):
-            graphs[i % rotate].replay()
-            stream.synchronize()
-        run = lambda i: graphs[i % rotate].replay()  # noqa: E731
-    else:
-        run = step
-    # timed: per-step synchronised serving loop (step + D2H of accept_len/bonus + sync)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(steps):
-        run(i)
-        stream.synchronize()
-    t_sync = time.perf_counter() - t_start
-    # pipelined: the same steps without the per-step synchronisation
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(steps):
-        run(i)
-    torch.cuda.synchronize()
-    t_pipe = time.perf_counter() - t_start
+        return lambda i: gs[i % self.rotate].replay()
 
-    # sampling workloads: the same step with the lazy walk, which reduces only the
-    # target rows it visits (no vocabulary pass over every node); same sync loop
-    t_lazy = None
-    if T > 0:
-        def step_lazy(i):
-            s = sets[i % rotate]
-            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
-                             small["prefix_len"], cfg.budget, tree=tree)
-            attention(s)
-            lib.ddtree_verify_sample_lazy(tree, s["logits"], T, small["uniforms"],
-                                          outputs=outputs)
-        run_lazy = step_lazy
-        if graph:
-            lazy_graphs = []
-            for i in range(rotate):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    step_lazy(i)
-                lazy_graphs.append(g)
-            run_lazy = lambda i: lazy_graphs[i % rotate].replay()  # noqa: E731
-        for i in range(warmup):
-            run_lazy(i)
-            stream.synchronize()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            run_lazy(i)
-            stream.synchronize()
-        t_lazy = time.perf_counter() - t_start
+    def loop_rates(self, run, steps, reps, sync_each=True):
+        """`reps` repetitions of exactly `steps` steps; steps/s of each."""
+        torch, stream = self.torch, self.stream
+        rates = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                run(i)
+                if sync_each:
+                    stream.synchronize()
+            torch.cuda.synchronize()
+            rates.append(steps / (time.perf_counter() - t0))
+        return rates
 
-    # greedy workloads: the same step with the vocabulary reduction and the walk in
-    # one call (ddtree_vocab_verify_greedy: the slice merge and the walk share a
-    # launch; same outputs); same synchronised loop
-    t_fused = None
-    if T == 0:
-        f_am = torch.empty((cfg.B, cfg.N), dtype=torch.int32, device=dev)
-        f_mx = torch.empty((cfg.B, cfg.N), dtype=torch.float32, device=dev)
+    def sustained(self, run, min_steps, min_seconds, reps):
+        """Repetitions of at least min_steps steps and min_seconds each."""
+        est = self.loop_rates(run, min_steps, 1)[0]
+        steps = max(min_steps, int(np.ceil(est * min_seconds)))
+        return steps, self.loop_rates(run, steps, reps)
 
-        def step_fused(i):
-            s = sets[i % rotate]
-            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
-                             small["prefix_len"], cfg.budget, tree=tree)
-            attention(s)
-            lib.ddtree_vocab_verify_greedy(s["logits"], tree, workspace=ws_v, outputs=outputs,
-                                           argmax=f_am, maxv=f_mx)
-        run_fused = step_fused
-        if graph:
-            fused_graphs = []
-            for i in range(rotate):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    step_fused(i)
-                fused_graphs.append(g)
-            run_fused = lambda i: fused_graphs[i % rotate].replay()  # noqa: E731
-        for i in range(warmup):
-            run_fused(i)
-            stream.synchronize()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            run_fused(i)
-            stream.synchronize()
-        t_fused = time.perf_counter() - t_start
-
-    # sampling workloads: the step with top-p (p = 0.9) nuclei: vocabulary pass, the
-    # per-node nucleus, then the walk on it; same synchronised loop
-    t_topp = None
-    if T > 0:
-        nuc = None
-
-        def step_topp(i):
-            nonlocal nuc
-            s = sets[i % rotate]
-            lib.ddtree_build(small["draft_lp"], small["draft_tok"], small["root_tok"],
-                             small["prefix_len"], cfg.budget, tree=tree)
-            attention(s)
-            v = vocab(s)
-            nuc = lib.ddtree_vocab_top_p(s["logits"], tree.num_nodes, v["maxv"], v["R"], T,
-                                         TOP_P, outputs=nuc)
-            lib.ddtree_verify_sample_top_p(tree, s["logits"], v["maxv"], nuc, T,
-                                           small["uniforms"], outputs=outputs)
-        step_topp(0)                 # eager once: allocates the nucleus outputs
-        torch.cuda.synchronize()
-        run_topp = step_topp
-        if graph:
-            topp_graphs = []
-            for i in range(rotate):
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    step_topp(i)
-                topp_graphs.append(g)
-            run_topp = lambda i: topp_graphs[i % rotate].replay()  # noqa: E731
-        for i in range(warmup):
-            run_topp(i)
-            stream.synchronize()
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            run_topp(i)
-            stream.synchronize()
-        t_topp = time.perf_counter() - t_start
-
-    # kernel durations: a HIP graph of back-to-back calls over the rotated input sets,
-    # replayed between two HIP events on this stream (no host gaps fall inside)
-    def timed_calls(fn, reps):
+    def call_ms(self, fn, min_calls=200, reps=5):
+        """Average duration of one call: a graph of back-to-back calls over the
+        rotated input sets, replayed between two HIP events on this stream;
+        median over repetitions of at least min_calls calls."""
+        torch, stream = self.torch, self.stream
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(rotate):
-                fn(sets[i])
+            for i in range(self.rotate):
+                fn(self.sets[i])
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        per = max(1, -(-min_calls // self.rotate))
+        out = []
         for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * rotate)
-    reps = max(1, steps // rotate)
-    attn_ms = timed_calls(attention, reps)
-    vocab_ms = timed_calls(vocab, reps)
-    # the commit that follows a step (not part of it): the last step's walk, its
-    # path rows into a compact cache (request b's position p at row
-    # b * (D + 1) + p - prefix_len[b])
-    walk = {k: v.to(dev) for k, v in outputs.items()}
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(per):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1) / (per * self.rotate))
+        return statistics.median(out), out
+
+
+def run_gpu(cfg, args, rotate):
+    """Every GPU figure of one workload."""
+    import torch
+    w = Workload(cfg, rotate, result_copy=args.result_copy)
+    T = cfg.temperature
+    for i in range(args.warmup):
+        w.step(i)
+        w.stream.synchronize()
+    run = w.step if args.eager else w.graphs_of(w.step)
+    for i in range(args.warmup):
+        run(i)
+        w.stream.synchronize()
+    r = {"total_ctx": w.total_ctx}
+    # the contract's loop: --reps repetitions of exactly --steps synchronised steps
+    r["rates"] = w.loop_rates(run, args.steps, args.reps)
+    r["accept_len_mean"] = float(w.host_result[0].float().mean())
+    r["sustained_steps"], r["sustained"] = w.sustained(run, max(args.steps, 200),
+                                                       args.min_seconds, args.reps)
+    # the same steps without the per-step synchronisation
+    r["pipelined"] = w.loop_rates(run, r["sustained_steps"], 3, sync_each=False)
+    # kernel durations
+    r["attn_ms"], r["attn_reps"] = w.call_ms(w.attention)
+    r["vocab_ms"], r["vocab_reps"] = w.call_ms(w.vocab)
+    if not args.no_extras:
+        extra_steps = max(args.steps, 100)
+        if T == 0:
+            f = w.step_fused if args.eager else w.graphs_of(w.step_fused)
+            f(0)
+            r["fused"] = w.loop_rates(f, extra_steps, 3)
+        else:
+            f = w.step_lazy if args.eager else w.graphs_of(w.step_lazy)
+            f(0)
+            r["lazy"] = w.loop_rates(f, extra_steps, 3)
+            w.step_topp(0)        # eager once: allocates the nucleus outputs
+            torch.cuda.synchronize()
+            f = w.step_topp if args.eager else w.graphs_of(w.step_topp)
+            f(0)
+            r["topp"] = w.loop_rates(f, extra_steps, 3)
+            r["linear"] = run_linear(w)
+        r.update(run_commit(w))
+        r.update(run_topk(w))
+    r["inputs"] = w.inp       # host copies, reused by the CPU baseline
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return r
+
+
+def run_commit(w):
+    """ddtree_commit of the last step's walk into a compact cache (request b's
+    position p at row b * (D + 1) + p - prefix_len[b]); not part of the step."""
+    torch, lib, cfg = w.torch, w.lib, w.cfg
+    dev = w.dev
+    walk = {k: v.to(dev) for k, v in w.outputs.items()}
     cb = (torch.arange(cfg.B, dtype=torch.int64, device=dev) * (cfg.D + 1)
-          - small["prefix_len"].to(torch.int64))
-    kcache = torch.empty((cfg.B * (cfg.D + 1), cfg.Hkv, cfg.Dh), dtype=base["k_tree"].dtype,
+          - w.small["prefix_len"].to(torch.int64))
+    kcache = torch.empty((cfg.B * (cfg.D + 1), cfg.Hkv, cfg.Dh), dtype=w.sets[0]["k_tree"].dtype,
                          device=dev)
     vcache = torch.empty_like(kcache)
     nxt = torch.empty((cfg.B,), dtype=torch.int32, device=dev)
     nroot = torch.empty_like(nxt)
-    commit_ms = timed_calls(lambda s: lib.ddtree_commit(
-        tree, walk, s["k_tree"], s["v_tree"], kcache, vcache, cb, 1 << 30,
-        next_prefix_len=nxt, next_root=nroot), reps)
-    commit_rows = int(walk["accept_len"].sum().item()) + cfg.B
-    commit_bytes = commit_rows * 2 * 2 * cfg.Hkv * cfg.Dh * base["k_tree"].element_size()
-    del sets
-    if graph:
-        del graphs
-    lin = run_linear(cfg, inp, tok_all, stream) if T > 0 else None
-    # the draft top-K over the D draft rows of each request (outside the step),
-    # over enough copies that the last-level cache does not hold them
-    rows_d = dl[:, :cfg.D].contiguous()
+    ms, _ = w.call_ms(lambda s: lib.ddtree_commit(
+        w.tree, walk, s["k_tree"], s["v_tree"], kcache, vcache, cb, 1 << 30,
+        next_prefix_len=nxt, next_root=nroot), reps=3)
+    rows = int(walk["accept_len"].sum().item()) + cfg.B
+    return {"commit_ms": ms, "commit_rows": rows,
+            "commit_bytes": rows * 2 * 2 * cfg.Hkv * cfg.Dh * kcache.element_size()}
+
+
+def run_topk(w):
+    """The draft top-K over the D draft rows of each request (outside the step),
+    over enough copies that the last-level cache does not hold them."""
+    torch, lib, cfg = w.torch, w.lib, w.cfg
+    dev = w.dev
+    rows_d = w.draft_logits[:, :cfg.D].contiguous()
     ncopy = max(2, min(64, -(-(1 << 30) // (rows_d.numel() * 4))))
     dsets = [rows_d] + [rows_d.clone() for _ in range(ncopy - 1)]
     tk_ws = torch.empty(max(16, lib.ddtree_draft_topk_workspace_size(
@@ -350,30 +369,25 @@ def run_gpu(cfg, steps, warmup, rotate, graph=True, result_copy=False):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     treps = max(1, 200 // ncopy)
-    e0.record(stream)
+    e0.record(w.stream)
     for _ in range(treps):
         g.replay()
-    e1.record(stream)
+    e1.record(w.stream)
     torch.cuda.synchronize()
-    topk_ms = e0.elapsed_time(e1) / (treps * ncopy)
-    return {"t_sync": t_sync, "t_pipe": t_pipe, "t_lazy": t_lazy, "t_topp": t_topp,
-            "t_fused": t_fused, "linear": lin,
-            "attn_ms": attn_ms, "vocab_ms": vocab_ms, "commit_ms": commit_ms,
-            "commit_rows": commit_rows, "commit_bytes": commit_bytes,
-            "topk_ms": topk_ms, "topk_bytes": rows_d.numel() * 4,
-            "total_ctx": tot_ctx, "accept_len_mean": float(host_result[0].float().mean())}
+    ms = e0.elapsed_time(e1) / (treps * ncopy)
+    del dsets
+    return {"topk_ms": ms, "topk_bytes": rows_d.numel() * 4}
 
 
-def run_linear(cfg, inp, tok_all, stream, reps=50):
+def run_linear(w, reps=50):
     """Linear speculative sampling on the workload's draft rows: a chain of D
     drafted tokens per request (the draft's top-1 at each depth), target rows =
     the draft rows plus the workload's target noise, both in the workload's dtype.
     Times the vocabulary pass over the D+1 target and D draft rows plus the walk
     (graph of back-to-back calls between two HIP events)."""
-    import torch
-    import tree_verification_build_amd as lib
     import workloads
-    dev = "cuda:0"
+    torch, lib, cfg, inp = w.torch, w.lib, w.cfg, w.inp
+    dev = w.dev
     B, D, T = cfg.B, cfg.D, cfg.temperature
     chain = workloads.config(cfg.name, budget=D)
     depth = np.tile(np.arange(D + 1, dtype=np.int32), (B, 1))
@@ -385,7 +399,7 @@ def run_linear(cfg, inp, tok_all, stream, reps=50):
         dg = torch.from_numpy(dl.view(np.int16)).view(torch.bfloat16).to(dev)
     else:
         tg, dg = torch.from_numpy(tl).to(dev), torch.from_numpy(dl).to(dev)
-    x = tok_all[:, :D, 0].contiguous()
+    x = w.tok_all[:, :D, 0].contiguous()
     u = torch.from_numpy(np.ascontiguousarray(inp["uniforms"][:, :D + 1]).view(np.int64)).to(dev)
     nq = torch.full((B,), D + 1, dtype=torch.int32, device=dev)
     npd = torch.full((B,), D, dtype=torch.int32, device=dev)
@@ -406,10 +420,10 @@ def run_linear(cfg, inp, tok_all, stream, reps=50):
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    e0.record(w.stream)
     for _ in range(reps):
         g.replay()
-    e1.record(stream)
+    e1.record(w.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     return {"ms_per_call": round(ms, 4), "accept_len_mean": float(out["accept_len"].float().mean()),
@@ -438,31 +452,40 @@ def run_copy_calibration(mib, reps=20):
             "copy_GBs": round(2 * n / (ms * 1e-3) / 1e9, 1)}
 
 
-def traffic_profile(cfg_name):
-    """The committed counter summary of the tree-attention call on this workload."""
-    return os.path.join(ROOT, "profiles", f"tree_attention_{cfg_name}_hbm_traffic.md")
+# ---------------------------------------------------------------------------- counter summaries
+
+KERNEL_SOURCES = {"tree_attention": "attention.hip", "vocab_reduce": "vocab.hip"}
+
+
+def traffic_profile(cfg_name, kernel="tree_attention"):
+    """The committed counter summary of a call on this workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel}_{cfg_name}_hbm_traffic.md")
 
 
 TRAFFIC_PROFILE = traffic_profile("single")
 
 
-def attention_source_digest():
+def source_digest(kernel="tree_attention"):
     import hashlib
-    p = os.path.join(ROOT, "tree_verification_build_amd", "csrc", "attention.hip")
+    p = os.path.join(ROOT, "tree_verification_build_amd", "csrc", KERNEL_SOURCES[kernel])
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(cfg_name):
-    """HBM bytes per tree-attention call from the committed counter summary, or
-    None when it covers another workload or an older attention source."""
+def attention_source_digest():
+    return source_digest("tree_attention")
+
+
+def measured_traffic(cfg_name, kernel="tree_attention"):
+    """HBM bytes per call from the committed counter summary, or None when it
+    covers another workload or an older kernel source."""
     try:
-        text = open(traffic_profile(cfg_name)).read()
+        text = open(traffic_profile(cfg_name, kernel)).read()
     except OSError:
         return None
     vals = dict(line.split(":", 1) for line in text.splitlines()
                 if line.startswith(("workload:", "source_digest:", "traffic_bytes_per_call:")))
     vals = {k.strip(): v.strip() for k, v in vals.items()}
-    if vals.get("workload") != cfg_name or vals.get("source_digest") != attention_source_digest():
+    if vals.get("workload") != cfg_name or vals.get("source_digest") != source_digest(kernel):
         return None
     try:
         return int(vals["traffic_bytes_per_call"])
@@ -470,53 +493,204 @@ def measured_traffic(cfg_name):
         return None
 
 
-def run_cpu_baseline(cfg, seconds):
-    """The oracle as it stands, same workload, on the host cores (one step = build,
-    float64 attention, vocabulary pass, walk)."""
+# ---------------------------------------------------------------------------- CPU baseline
+
+# Oracle sample per workload: the first `requests` requests of the batch and, for
+# attention, the first `heads` query heads (None: all).  Times are scaled to the
+# whole step: attention by (total context x query heads) over the sample's, the
+# other stages by requests.
+CPU_SAMPLE = {"tiny": (None, None), "single": (None, None), "batched": (2, None),
+              "long": (None, 1), "ragged": (2, None)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _subset_inputs(cfg, inp, reqs):
+    """The workload's inputs restricted to requests `reqs` (contexts repacked)."""
+    import dataclasses
+    offs = inp["ctx_offsets"]
+    sub = {k: np.ascontiguousarray(inp[k][reqs]) for k in
+           ("q", "k_tree", "v_tree", "draft_logits", "root_tok", "uniforms", "prefix_len",
+            "ctx_lens")}
+    sub["k_ctx"] = np.concatenate([inp["k_ctx"][offs[b]:offs[b + 1]] for b in reqs])
+    sub["v_ctx"] = np.concatenate([inp["v_ctx"][offs[b]:offs[b + 1]] for b in reqs])
+    sub["ctx_offsets"] = np.concatenate([[0], np.cumsum(sub["ctx_lens"])]).astype(np.int32)
+    return dataclasses.replace(cfg, B=len(reqs)), sub
+
+
+def cpu_sample_step(cfg, inp, reqs, heads):
+    """One oracle step on the sample; returns the seconds of each stage (the
+    draft top-K and the target logits are inputs, outside the timed stages)."""
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    # the oracle's draft top-K gives the build's inputs (outside the timed step,
-    # as on the GPU)
-    inp = oracle.attach_draft_topk(workloads.make_inputs(cfg), cfg.D, cfg.K)
-    t = oracle.build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"], inp["prefix_len"],
-                          cfg.budget)
-    logits, _ = workloads.make_target_logits(cfg, inp, t["depth"], t["num_nodes"])
-    n = 0
+    scfg, sub = _subset_inputs(cfg, inp, reqs)
+    oracle.attach_draft_topk(sub, cfg.D, cfg.K)
     t0 = time.perf_counter()
-    while True:
-        tr = oracle.build_tree(inp["draft_lp"], inp["draft_tok"], inp["root_tok"],
-                               inp["prefix_len"], cfg.budget)
-        oracle.tree_attention(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"],
-                              inp["k_tree"], inp["v_tree"], tr["vis"], tr["num_nodes"],
-                              dtype=cfg.dtype)
-        vr = oracle.vocab_reduce(logits, tr["num_nodes"], cfg.temperature, dtype=cfg.dtype)
-        if cfg.temperature > 0:
-            oracle.verify_sample(tr, logits, vr["maxv"], vr["R"], cfg.temperature,
-                                 inp["uniforms"], cfg.D, dtype=cfg.dtype)
-        else:
-            oracle.verify_greedy(tr, vr["argmax"], cfg.D)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or n >= 1000:
-            break
-    return {"value": n / el, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} full oracle steps of the {cfg.name} workload in {el:.1f} s"}
+    tr = oracle.build_tree(sub["draft_lp"], sub["draft_tok"], sub["root_tok"], sub["prefix_len"],
+                           cfg.budget)
+    t1 = time.perf_counter()
+    logits, _ = workloads.make_target_logits(scfg, sub, tr["depth"], tr["num_nodes"])
+    t2 = time.perf_counter()
+    oracle.tree_attention(sub["q"], sub["k_ctx"], sub["v_ctx"], sub["ctx_offsets"], sub["k_tree"],
+                          sub["v_tree"], tr["vis"], tr["num_nodes"], dtype=cfg.dtype, heads=heads)
+    t3 = time.perf_counter()
+    vr = oracle.vocab_reduce(logits, tr["num_nodes"], cfg.temperature, dtype=cfg.dtype)
+    t4 = time.perf_counter()
+    if cfg.temperature > 0:
+        oracle.verify_sample(tr, logits, vr["maxv"], vr["R"], cfg.temperature, sub["uniforms"],
+                             cfg.D, dtype=cfg.dtype)
+    else:
+        oracle.verify_greedy(tr, vr["argmax"], cfg.D)
+    t5 = time.perf_counter()
+    return {"build": t1 - t0, "attention": t3 - t2, "vocab": t4 - t3, "walk": t5 - t4,
+            "ctx": int(sub["ctx_offsets"][-1])}
+
+
+def cpu_leg(cfg, inp, seconds, cores):
+    """Oracle steps/s (scaled from the sample) with `cores` CPUs: the BLAS/OpenMP
+    pools limited to that many threads and the process pinned to that many CPUs
+    of its affinity set."""
+    from threadpoolctl import threadpool_limits
+    nreq, nheads = CPU_SAMPLE.get(cfg.name, (None, None))
+    reqs = list(range(cfg.B if nreq is None else min(nreq, cfg.B)))
+    heads = None if nheads is None else list(range(min(nheads, cfg.Hq)))
+    total_ctx = int(inp["ctx_offsets"][-1])
+    allowed = sorted(os.sched_getaffinity(0))
+    use = allowed[:cores]
+    os.sched_setaffinity(0, use)
+    try:
+        with threadpool_limits(limits=len(use)):
+            runs, t_start = [], time.perf_counter()
+            while True:
+                runs.append(cpu_sample_step(cfg, inp, reqs, heads))
+                if time.perf_counter() - t_start >= seconds:
+                    break
+    finally:
+        os.sched_setaffinity(0, allowed)
+    st = {k: statistics.median(r[k] for r in runs) for k in ("build", "attention", "vocab",
+                                                               "walk")}
+    fr = cfg.B / len(reqs)
+    fa = (total_ctx * cfg.Hq) / (max(1, runs[0]["ctx"]) * (cfg.Hq if heads is None else len(heads)))
+    step = (st["build"] + st["vocab"] + st["walk"]) * fr + st["attention"] * fa
+    sample = (f"oracle step on requests 0..{len(reqs) - 1} of {cfg.B}"
+              + ("" if heads is None else f", attention on {len(heads)} of {cfg.Hq} query heads")
+              + f"; median of {len(runs)} runs, stage times scaled to the whole step "
+                "(attention by context x heads, other stages by requests)")
+    if len(reqs) == cfg.B and heads is None:
+        sample = f"full oracle step of the {cfg.name} workload; median of {len(runs)} runs"
+    return {"value": 1.0 / step, "unit": "steps/s", "cores": len(use), "kind": "oracle",
+            "sample": sample, "stage_seconds_per_step": {
+                "build": round(st["build"] * fr, 5), "attention": round(st["attention"] * fa, 5),
+                "vocab": round(st["vocab"] * fr, 5), "walk": round(st["walk"] * fr, 5)}}
+
+
+def run_cpu_baseline(cfg, seconds, inp=None):
+    """The oracle as it stands on the host cores: single-threaded on one core,
+    and on every core of the affinity set (both scaled from the same sample)."""
+    import workloads
+    if inp is None:
+        inp = workloads.make_inputs(cfg)
+    ncores = len(os.sched_getaffinity(0))
+    one = cpu_leg(cfg, inp, seconds, 1)
+    allc = cpu_leg(cfg, inp, seconds, ncores)
+    out = dict(allc)
+    out["single_core"] = {"value": one["value"], "cores": 1,
+                          "stage_seconds_per_step": one["stage_seconds_per_step"]}
+    out["cpu_model"] = cpu_model()
+    return out
+
+
+# ---------------------------------------------------------------------------- records
+
+def config_record(cfg, r, args, rotate):
+    ab = algorithmic_bytes(cfg, r["total_ctx"])
+    med = statistics.median(r["rates"])
+    attn_gbs = ab["attention"] / (r["attn_ms"] * 1e-3) / 1e9
+    vocab_gbs = ab["vocab"] / (r["vocab_ms"] * 1e-3) / 1e9
+    mfma_peak = MFMA_BF16_PEAK if cfg.dtype == "bf16" else MFMA_F32_PEAK
+    flops = attention_flops(cfg, r["total_ctx"])
+    rec = {
+        "workload": describe(cfg),
+        "steps_per_s": round(med, 2),
+        "ms_per_step": round(1e3 / med, 4),
+        "steps": args.steps,
+        "reps": summary(r["rates"]),
+        "sustained": dict(summary(r["sustained"]), steps_per_rep=r["sustained_steps"]),
+        "pipelined_steps_per_s": round(statistics.median(r["pipelined"]), 2),
+        "ctx_tokens": r["total_ctx"],
+        "input_sets_rotated": rotate,
+        "attention": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic(cfg.name, "tree_attention"),
+                      "bytes_per_launch": ab["attention"], "avg_ms": round(r["attn_ms"], 5),
+                      "avg_ms_reps": [round(x, 5) for x in r["attn_reps"]]},
+        "vocab_reduce": {"bound": "hbm", "achieved": round(vocab_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(vocab_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(cfg.name, "vocab_reduce"),
+                         "bytes_per_launch": ab["vocab"], "avg_ms": round(r["vocab_ms"], 5),
+                         "avg_ms_reps": [round(x, 5) for x in r["vocab_reps"]]},
+        "attention_plus_vocab": {
+            "achieved_GBs": round((ab["attention"] + ab["vocab"]) /
+                                  ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9, 1),
+            "frac": round((ab["attention"] + ab["vocab"]) /
+                          ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "mfma_util": round(flops / (r["attn_ms"] * 1e-3) / mfma_peak, 4),
+        "accept_len_mean": r["accept_len_mean"],
+    }
+    if "fused" in r:
+        m = statistics.median(r["fused"])
+        rec["fused_greedy_step"] = {
+            "steps_per_s": round(m, 2), "ms_per_step": round(1e3 / m, 4),
+            "step": "build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
+                    "greedy walk in one call; same outputs)"}
+    if "lazy" in r:
+        m = statistics.median(r["lazy"])
+        rec["lazy_sampling_walk"] = {
+            "steps_per_s": round(m, 2), "ms_per_step": round(1e3 / m, 4),
+            "step": "build, attention, ddtree_verify_sample_lazy (target rows reduced only "
+                    "where the walk goes; same outputs)"}
+    if "topp" in r:
+        m = statistics.median(r["topp"])
+        rec["top_p_sampling_walk"] = {
+            "top_p": TOP_P, "steps_per_s": round(m, 2), "ms_per_step": round(1e3 / m, 4),
+            "step": "build, attention, ddtree_vocab_reduce, ddtree_vocab_top_p, "
+                    "ddtree_verify_sample_top_p"}
+    if "linear" in r:
+        rec["linear_speculative_sampling"] = r["linear"]
+    if "commit_ms" in r:
+        rec["commit"] = {"avg_ms": round(r["commit_ms"], 5), "rows": r["commit_rows"],
+                         "bytes_per_launch": r["commit_bytes"], "in_step": False}
+    if "topk_ms" in r:
+        rec["draft_topk"] = {"achieved_GBs": round(r["topk_bytes"] / (r["topk_ms"] * 1e-3) / 1e9, 1),
+                             "avg_ms": round(r["topk_ms"], 5), "bytes_per_launch": r["topk_bytes"],
+                             "in_step": False}
+    return rec
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps per repetition")
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="single")
+    ap.add_argument("--reps", type=int, default=5, help="repetitions of --steps steps")
+    ap.add_argument("--min-seconds", type=float, default=1.0,
+                    help="minimum length of a sustained repetition")
+    ap.add_argument("--config", default="all", help="a workload name, or 'all'")
     ap.add_argument("--rotate", type=int, default=0, help="input sets (0: >= 1 GiB in total)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=3.0,
+                    help="oracle time per CPU leg and workload (at least one sample step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the figures outside the step (fused, lazy, top-p, linear, commit, "
+                         "draft top-K)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every call from Python instead of replaying a HIP graph")
     ap.add_argument("--host-wait", choices=("spin", "auto"), default="spin",
@@ -537,76 +711,60 @@ def main():
         sys.exit(2)
     host_wait = set_host_wait(args.host_wait)
     import workloads
-    cfg = workloads.config(args.config)
-    offs = np.concatenate([[0], np.cumsum(workloads.ctx_lengths(cfg))])
-    ab = algorithmic_bytes(cfg, int(offs[-1]))
-    rotate = args.rotate or int(max(1, min(32, np.ceil(2 ** 30 / ab["total"]))))
-    r = run_gpu(cfg, args.steps, args.warmup, rotate, graph=not args.eager,
-                result_copy=args.result_copy)
-    steps_s = args.steps / r["t_sync"]
-    attn_gbs = ab["attention"] / (r["attn_ms"] * 1e-3) / 1e9
-    vocab_gbs = ab["vocab"] / (r["vocab_ms"] * 1e-3) / 1e9
-    flops = attention_flops(cfg, r["total_ctx"])
-    mfma_peak = MFMA_BF16_PEAK if cfg.dtype == "bf16" else MFMA_F32_PEAK
+    names = ALL_CONFIGS if args.config == "all" else (args.config,)
+    head = HEADLINE if HEADLINE in names else names[0]
+    order = [head] + [n for n in names if n != head]
+    records = {}
+    for name in order:
+        cfg = workloads.config(name)
+        offs = np.concatenate([[0], np.cumsum(workloads.ctx_lengths(cfg))])
+        ab = algorithmic_bytes(cfg, int(offs[-1]))
+        rotate = args.rotate or int(max(1, min(32, np.ceil(2 ** 30 / ab["total"]))))
+        print(f"[bench] {name}: GPU", file=sys.stderr, flush=True)
+        r = run_gpu(cfg, args, rotate)
+        rec = config_record(cfg, r, args, rotate)
+        if not args.no_cpu_baseline:
+            print(f"[bench] {name}: CPU oracle", file=sys.stderr, flush=True)
+            rec["cpu_baseline"] = run_cpu_baseline(cfg, args.cpu_seconds, r["inputs"])
+        del r
+        records[name] = rec
+        print(f"[bench] {name}: {rec['steps_per_s']} steps/s", file=sys.stderr, flush=True)
+    h = records[head]
+    hcfg = workloads.config(head)
     line = {
         "metric": METRIC,
-        "value": round(steps_s, 2),
+        "value": h["steps_per_s"],
         "unit": "steps/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(1e3 * r["t_sync"] / args.steps, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": hcfg.dtype,
         "data": "synthetic",
-        "config": {"workload": describe(cfg), "B": cfg.B, "ctx_tokens": r["total_ctx"],
-                   "heads_q": cfg.Hq, "heads_kv": cfg.Hkv, "head_dim": cfg.Dh, "depth": cfg.D,
-                   "budget": cfg.budget, "topk_cap": cfg.K, "vocab": cfg.V,
-                   "temperature": cfg.temperature, "input_sets_rotated": rotate,
+        "config": {"workload": h["workload"], "B": hcfg.B, "ctx_tokens": h["ctx_tokens"],
+                   "heads_q": hcfg.Hq, "heads_kv": hcfg.Hkv, "head_dim": hcfg.Dh,
+                   "depth": hcfg.D, "budget": hcfg.budget, "topk_cap": hcfg.K,
+                   "vocab": hcfg.V, "temperature": hcfg.temperature,
+                   "input_sets_rotated": h["input_sets_rotated"],
                    "launch": "eager" if args.eager else "hip_graph", "host_wait": host_wait,
-                   "result_to_host": "copy" if args.result_copy else "pinned_store"},
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(cfg.name), "kernel": "ddtree_tree_attention",
-                     "bytes_per_launch": ab["attention"], "avg_ms": round(r["attn_ms"], 5)},
-        "pipelined_steps_per_s": round(args.steps / r["t_pipe"], 2),
-        "vocab_reduce": {"achieved_GBs": round(vocab_gbs, 1), "avg_ms": round(r["vocab_ms"], 5),
-                         "bytes_per_launch": ab["vocab"]},
-        "attention_plus_vocab_GBs": round((ab["attention"] + ab["vocab"]) /
-                                          ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9, 1),
-        "mfma_util": round(flops / (r["attn_ms"] * 1e-3) / mfma_peak, 4),
-        "draft_topk": {"achieved_GBs": round(r["topk_bytes"] / (r["topk_ms"] * 1e-3) / 1e9, 1),
-                       "avg_ms": round(r["topk_ms"], 5), "bytes_per_launch": r["topk_bytes"],
-                       "in_step": False},
-        "commit": {"avg_ms": round(r["commit_ms"], 5), "rows": r["commit_rows"],
-                   "bytes_per_launch": r["commit_bytes"], "in_step": False},
-        "accept_len_mean": r["accept_len_mean"],
+                   "result_to_host": "copy" if args.result_copy else "pinned_store",
+                   "value_is": f"median steps/s over {args.reps} repetitions of {args.steps} "
+                               "synchronised steps"},
+        "roofline": dict(h["attention"], kernel="ddtree_tree_attention"),
+        "reps": h["reps"],
+        "sustained": h["sustained"],
+        "pipelined_steps_per_s": h["pipelined_steps_per_s"],
+        "vocab_reduce": h["vocab_reduce"],
+        "attention_plus_vocab": h["attention_plus_vocab"],
+        "mfma_util": h["mfma_util"],
+        "accept_len_mean": h["accept_len_mean"],
     }
-    if r["linear"] is not None:
-        line["linear_speculative_sampling"] = r["linear"]
-    if r["t_fused"] is not None:
-        line["fused_greedy_step"] = {
-            "steps_per_s": round(args.steps / r["t_fused"], 2),
-            "ms_per_step": round(r["t_fused"] / args.steps * 1e3, 4),
-            "step": "build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
-                    "greedy walk in one call; same outputs)"}
-    if r["t_lazy"] is not None:
-        line["lazy_sampling_walk"] = {
-            "steps_per_s": round(args.steps / r["t_lazy"], 2),
-            "ms_per_step": round(r["t_lazy"] / args.steps * 1e3, 4),
-            "step": "build, attention, ddtree_verify_sample_lazy (target rows reduced only "
-                    "where the walk goes; same outputs)"}
-    if r["t_topp"] is not None:
-        line["top_p_sampling_walk"] = {
-            "top_p": TOP_P,
-            "steps_per_s": round(args.steps / r["t_topp"], 2),
-            "ms_per_step": round(r["t_topp"] / args.steps * 1e3, 4),
-            "step": "build, attention, ddtree_vocab_reduce, ddtree_vocab_top_p, "
-                    "ddtree_verify_sample_top_p"}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = run_cpu_baseline(cfg, args.cpu_seconds)
+    if "cpu_baseline" in h:
+        line["cpu_baseline"] = h["cpu_baseline"]
+    line["configs"] = [dict(name=n, **records[n]) for n in names]
     print(json.dumps(line), flush=True)
 
 

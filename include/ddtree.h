@@ -40,9 +40,10 @@
  *     errors (DDTREE_EDEVICE).  ddtree_last_error() gives a thread-local message
  *     for the last non-OK status of the calling thread.
  *   - Preconditions not checked (undefined results otherwise): inputs are
- *     finite; draft log-probs are non-increasing along the top-k axis; the
- *     draft tokens of one (request, depth) are distinct; ctx_offsets_host holds
- *     the same values as ctx_offsets.
+ *     finite (draft log-probs may be -inf, e.g. masked tokens); draft
+ *     log-probs are non-increasing along the top-k axis; the draft tokens of
+ *     one (request, depth) are distinct; host copies of context offsets and
+ *     lengths (the *_host arrays) hold the same values as the device arrays.
  *   - Tensors are dense, row-major, with 16-byte aligned base pointers.
  *   - Calls are thread-safe (no shared state); calls on one stream are ordered.
  */
@@ -160,12 +161,19 @@ ddtree_status ddtree_build(const float* draft_lp, const int32_t* draft_tok,
  *   M = N * Hq / Hkv <= 1024 query rows per KV head.  Up to 128 rows share
  *   one pass over the context; larger M is processed in 128-row slices, each
  *   of which reads the context once more.
- *   scale        score scale (1/sqrt(Dh) is the usual choice)
+ *   scale        score scale > 0, or 0 for 1/sqrt(Dh) (the pages give no scale;
+ *                1/sqrt(Dh) is the usual one)
  *   out          [B, N, Hq, Dh] dtype; padding nodes get 0
  *   lse          [B, N, Hq] fp32 natural-log softmax denominator, or NULL
  *   workspace    device scratch of at least
  *                ddtree_tree_attention_workspace_size(...) bytes (contents
  *                need no initialisation and are garbage afterwards)
+ * Context lengths: the host copy decides the work split and the grid.  For
+ * B <= 64 the kernels take every context range from the host copy (the device
+ * array is not read), so a call captured in a HIP graph keeps the ranges it
+ * was captured with.  For B > 64 the kernels look their ranges up in the
+ * device array, which must then hold the host copy's values; if it does not,
+ * the output is undefined but no workspace access leaves the planned splits.
  * Errors: DDTREE_EINVAL (null pointers, sizes, small workspace),
  *         DDTREE_EUNSUPPORTED (other Dh, too many query rows per KV head).
  */
@@ -178,6 +186,40 @@ ddtree_status ddtree_tree_attention(const void* q, const void* k_ctx, const void
                                     const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh,
                                     ddtree_dtype dtype, float scale, void* out, float* lse,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ddtree_tree_attention_tuned -- ddtree_tree_attention with its work split
+ * chosen by the caller instead of planned (a tuning and test entry point: the
+ * split size changes the order in which partial sums meet, so outputs differ
+ * from the planned call's within rounding).  Source: as ddtree_tree_attention.
+ *   tuning->split_keys  context keys per workgroup, rounded up to whole
+ *                       key tiles; 0 keeps the planned size
+ *   tuning->stages      LDS ring depth of the bf16 head_dim-128 kernel when the
+ *                       query rows of a KV head fit four waves (2, 3 or 4);
+ *                       0 keeps 2
+ *   workspace           ddtree_tree_attention_tuned_workspace_size(..., tuning)
+ * tuning == NULL is ddtree_tree_attention.  Every other argument as there.
+ * Errors: as ddtree_tree_attention; DDTREE_EINVAL for negative split_keys or a
+ *         stage count other than 0, 2, 3, 4.
+ */
+typedef struct {
+  int32_t split_keys;
+  int32_t stages;
+} ddtree_attention_tuning;
+
+size_t ddtree_tree_attention_tuned_workspace_size(int32_t B, int32_t N, int32_t Hq, int32_t Hkv,
+                                                  int32_t Dh, const int32_t* ctx_offsets_host,
+                                                  const ddtree_attention_tuning* tuning);
+
+ddtree_status ddtree_tree_attention_tuned(const void* q, const void* k_ctx, const void* v_ctx,
+                                          const int32_t* ctx_offsets,
+                                          const int32_t* ctx_offsets_host, const void* k_tree,
+                                          const void* v_tree, const ddtree_tree* tree, int32_t Hq,
+                                          int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale,
+                                          void* out, float* lse, void* workspace,
+                                          size_t workspace_bytes,
+                                          const ddtree_attention_tuning* tuning,
+                                          hipStream_t stream);
 
 /*
  * ddtree_tree_attention_ranges -- the same tree attention with each request's

@@ -82,7 +82,11 @@ class Case:
 def assert_tree_equal(got: dict, ref: dict):
     for k in ("token", "parent", "depth", "rank", "position", "first_child", "next_sibling",
               "num_nodes"):
-        assert np.array_equal(got[k], ref[k]), k
+        if not np.array_equal(got[k], ref[k]):
+            bad = np.argwhere(got[k] != ref[k])[:4]
+            raise AssertionError(f"{k}: first mismatches at {bad.tolist()}: got "
+                                 f"{[got[k][tuple(i)] for i in bad]}, expected "
+                                 f"{[ref[k][tuple(i)] for i in bad]}")
     assert np.array_equal(got["score"].view(np.uint32), ref["score"].view(np.uint32)), "score bits"
     assert np.array_equal(got["vis"], ref["vis"]), "vis"
 

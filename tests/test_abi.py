@@ -172,11 +172,21 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.ddtree_tree_attention(*args, 128, 1, 64, 1, 0.125, fake, None, None, 0, None) == 2
     assert lib.ddtree_tree_attention(*args, 4, 4, 64, 1, -1.0, fake, None, None, 0, None) == 1
     assert lib.ddtree_tree_attention(*args, 4, 4, 64, 5, 0.125, fake, None, None, 0, None) == 1
+    assert lib.ddtree_tree_attention(*args, 4, 4, 64, 1, float("nan"), fake, None, None, 0,
+                                     None) == 1
     mis = ctypes.c_void_p(24)
     assert lib.ddtree_tree_attention(mis, *args[1:], 4, 4, 64, 1, 0.125, fake, None, None, 0,
                                      None) == 1
     lib.ddtree_last_error.restype = ctypes.c_char_p
     assert b"aligned" in lib.ddtree_last_error()
+    # tuned form: bad tuning values are rejected before any launch
+    from tree_verification_build_amd._lib import _CTuning
+    for sk, ns in ((-1, 0), (0, 1), (0, 5), (64, -2)):
+        tu = _CTuning(sk, ns)
+        assert lib.ddtree_tree_attention_tuned(*args, 4, 4, 64, 1, 0.0, fake, None, None, 0,
+                                               ctypes.byref(tu), None) == 1, (sk, ns)
+    assert lib.ddtree_tree_attention_tuned(*args, 4, 4, 96, 1, 0.0, fake, None, None, 0, None,
+                                           None) == 2
 
 
 def test_workspace_sizes_are_host_only_and_sane():
@@ -190,6 +200,12 @@ def test_workspace_sizes_are_host_only_and_sane():
     packed = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     assert t.ddtree_tree_attention_ranges_workspace_size(4, 33, 8, 2, 128, lens) == \
         t.ddtree_tree_attention_workspace_size(4, 33, 8, 2, 128, packed) > 0
+    # a tuned split size sizes its own workspace: smaller splits, more partials
+    assert t.ddtree_tree_attention_tuned_workspace_size(1, 33, 8, 8, 128, offs) == ws
+    assert t.ddtree_tree_attention_tuned_workspace_size(1, 33, 8, 8, 128, offs,
+                                                        split_keys=64) > ws
+    assert t.ddtree_tree_attention_tuned_workspace_size(1, 33, 8, 8, 128, offs,
+                                                        split_keys=8192) == 0
     assert t.ddtree_vocab_reduce_workspace_size(1, 33, 163840) > 0
     assert t.ddtree_vocab_reduce_workspace_size(64, 33, 163840) == 0
     # draft top-k: slices of 1024..8192 elements, K keys and one (max, sum) pair each

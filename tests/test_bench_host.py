@@ -57,3 +57,31 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_legs_and_sample_scaling():
+    """The CPU baseline: a single-core leg and an all-core leg, the CPU model, and
+    a sample whose stage times are scaled to the whole step."""
+    cfg = workloads.config("tiny")
+    r = bench.run_cpu_baseline(cfg, 0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "steps/s" and r["value"] > 0
+    assert r["cores"] == len(os.sched_getaffinity(0))
+    assert r["single_core"]["cores"] == 1 and r["single_core"]["value"] > 0
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
+    assert "full oracle step" in r["sample"]
+    st = r["stage_seconds_per_step"]
+    assert abs(sum(st.values()) - 1.0 / r["value"]) <= 1e-4 + 0.01 / r["value"]
+
+
+def test_subset_inputs_repack_the_contexts():
+    import numpy as np
+    cfg = workloads.config("ragged", B=5, ctx=(3, 40), V=64, Hq=2, Hkv=2, Dh=64)
+    inp = workloads.make_inputs(cfg)
+    scfg, sub = bench._subset_inputs(cfg, inp, [0, 1, 2])
+    assert scfg.B == 3
+    offs = inp["ctx_offsets"]
+    assert list(sub["ctx_offsets"]) == [int(x) for x in offs[:4]]
+    assert np.array_equal(sub["k_ctx"], inp["k_ctx"][:offs[3]])
+    scfg, sub = bench._subset_inputs(cfg, inp, [3])
+    assert np.array_equal(sub["v_ctx"], inp["v_ctx"][offs[3]:offs[4]])
+    assert np.array_equal(sub["q"], inp["q"][3:4])

@@ -5,7 +5,7 @@ order with gaps filled with NaN (a read outside a request's range would poison
 its output).  The range form must give bit-for-bit the output of the packed
 form on the packed copy (same split plan, same kernels) and match the oracle
 within the attention tolerance; batches above and below the size at which the
-split plan is passed in the kernel arguments (16 requests) are covered, and a
+split plan is passed in the kernel arguments (64 requests) are covered, and a
 batched two-step loop runs the range form over per-request slabs after
 ddtree_commit has appended each request's accepted path.
 """
@@ -28,6 +28,11 @@ CFGS = {
                                        seed_index=43),
     "ranges_b18_f32": workloads.config("tiny", B=18, ctx=(0, 600), Hq=2, Hkv=2, Dh=128,
                                        seed_index=44),
+    # past 64 requests the splits are looked up on the device
+    "ranges_b70_bf16": workloads.config("ragged", B=70, ctx=(0, 400), Hq=2, Hkv=2, Dh=128,
+                                        V=1024, seed_index=45),
+    "ranges_b66_f32": workloads.config("tiny", B=66, ctx=(0, 300), Hq=2, Hkv=2, Dh=64,
+                                       seed_index=46),
 }
 _cases = {}
 
@@ -152,3 +157,38 @@ def test_batched_commit_then_ranges_attention():
     o_ref, _ = oracle.tree_attention(q2, packed_k, packed_v, offs2, kt2, vt2, tree2["vis"],
                                      tree2["num_nodes"], dtype="bf16")
     assert_attention_close(attn_to_f64(o2), o_ref, "bf16")
+
+
+@pytest.mark.parametrize("direction", ["shorter", "longer"])
+def test_device_lengths_disagreeing_with_host_copy(direction):
+    """Past 64 requests the kernels read the device context offsets while the
+    grid and the workspace follow the host copy.  When the two disagree (a
+    broken precondition) the output is undefined, but no access may leave the
+    planned splits' workspace: the call completes, and a following call with
+    agreeing copies is exact again.  Device ranges stay inside the K/V buffer."""
+    import tree_verification_build_amd as lib
+    c = _case("ranges_b70_bf16")
+    cfg, i = c.cfg, c.inp
+    t = c.gpu_tree()
+    lens = i["ctx_lens"].astype(np.int64)
+    rng = np.random.default_rng(5)
+    if direction == "shorter":
+        bad = np.maximum(lens - rng.integers(0, 300, size=cfg.B), 0)
+    else:
+        bad = lens + rng.integers(0, 900, size=cfg.B)
+    bad_offs = np.concatenate([[0], np.cumsum(bad)]).astype(np.int32)
+    rows = max(int(bad_offs[-1]), int(i["ctx_offsets"][-1]))
+    kc = np.zeros((rows, cfg.Hkv, cfg.Dh), np.uint16)
+    vc = np.zeros((rows, cfg.Hkv, cfg.Dh), np.uint16)
+    kc[:i["k_ctx"].shape[0]] = i["k_ctx"]
+    vc[:i["v_ctx"].shape[0]] = i["v_ctx"]
+    kd, vd = dev_tensor(kc, "bf16"), dev_tensor(vc, "bf16")
+    say("attention, device offsets", direction, "than the host copy", "B", cfg.B)
+    lib.ddtree_tree_attention(c.d("q"), kd, vd, dev_tensor(bad_offs, None), i["ctx_offsets"],
+                              c.d("k_tree"), c.d("v_tree"), t)
+    torch.cuda.synchronize()
+    out, _ = lib.ddtree_tree_attention(c.d("q"), kd, vd, c.d("ctx_offsets"), i["ctx_offsets"],
+                                       c.d("k_tree"), c.d("v_tree"), t)
+    torch.cuda.synchronize()
+    ref, _ = c.oracle_attention()
+    assert_attention_close(attn_to_f64(out), ref, "bf16")

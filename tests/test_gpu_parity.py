@@ -55,6 +55,58 @@ def test_build(name):
     assert_tree_equal(t.to_numpy(), c.tree)
 
 
+@pytest.mark.parametrize("D,K,budget", [(4, 3, 120), (3, 4, 84), (2, 8, 72)])
+def test_build_small_table_two_slot_sets(D, K, budget):
+    """D * K <= 64 (one register of log-probs per lane) with more than 65 nodes
+    (the frontier's second slot set)."""
+    import tree_verification_build_amd as lib
+    rng = np.random.default_rng(D * 100 + K)
+    B = 2
+    lp = -np.sort(np.abs(rng.standard_normal((B, D, K))), axis=-1).astype(np.float32)
+    tok = np.stack([np.stack([rng.choice(5000, K, replace=False) for _ in range(D)])
+                    for _ in range(B)]).astype(np.int32)
+    root = rng.integers(0, 5000, size=B).astype(np.int32)
+    prefix = rng.integers(0, 100, size=B).astype(np.int32)
+    say("build small table, two slot sets", D, K, budget)
+    ref = oracle.build_tree(lp, tok, root, prefix, budget)
+    t = lib.ddtree_build(*(torch.from_numpy(x).to("cuda:0") for x in (lp, tok, root, prefix)),
+                         budget)
+    torch.cuda.synchronize()
+    assert_tree_equal(t.to_numpy(), ref)
+
+
+def test_build_minus_inf_logprobs():
+    """Draft log-probs of -inf (masked tokens) in the top-k: real offers that
+    score -inf tie one another and are taken by parent, then rank, exactly as
+    the oracle takes them; entries below depth D or past rank K - 1, which do
+    not exist, are never taken."""
+    import tree_verification_build_amd as lib
+    for seed, (D, K, budget) in enumerate([(2, 2, 6), (4, 3, 120), (3, 4, 84), (8, 4, 32),
+                                           (16, 8, 127)]):
+        rng = np.random.default_rng(300 + seed)
+        B = 3
+        lp = -np.sort(np.abs(rng.standard_normal((B, D, K))), axis=-1).astype(np.float32)
+        # trailing ranks of some depths masked (-inf keeps them non-increasing)
+        for b in range(B):
+            for d in range(D):
+                r = int(rng.integers(0, K + 1))
+                if r < K and (b + d) % 2 == 0:
+                    lp[b, d, max(r, 1 if d == 0 and b == 0 else 0):] = -np.inf
+        tok = np.stack([np.stack([rng.choice(5000, K, replace=False) for _ in range(D)])
+                        for _ in range(B)]).astype(np.int32)
+        root = rng.integers(0, 5000, size=B).astype(np.int32)
+        prefix = rng.integers(0, 100, size=B).astype(np.int32)
+        say("build -inf log-probs", D, K, budget)
+        ref = oracle.build_tree(lp, tok, root, prefix, budget)
+        t = lib.ddtree_build(*(torch.from_numpy(x).to("cuda:0") for x in (lp, tok, root, prefix)),
+                             budget)
+        torch.cuda.synchronize()
+        assert_tree_equal(t.to_numpy(), ref)
+        if budget == sum(K ** d for d in range(1, D + 1)):
+            # every rank sequence fits the budget: the -inf ones are in the tree
+            assert np.isneginf(ref["score"][ref["depth"] > 0]).any()
+
+
 def _temps(c):
     return sorted({0.0, c.cfg.temperature, 0.8 if c.cfg.V <= 4096 else c.cfg.temperature})
 
@@ -252,14 +304,14 @@ def test_verify_sample_lazy(name):
 
 
 def _attn_sample(c):
-    """(requests, heads) for the oracle: everything when small, a sample at full size."""
+    """Oracle calls as (requests, heads) pairs: everything when small; at full
+    size every request on one head (head b % Hq for request b) and so, with
+    B >= Hq, every head on several requests; a single request on all heads."""
     cfg = c.cfg
     if name_is_full(cfg):
-        rng = np.random.default_rng(7)
-        reqs = sorted(set([0, cfg.B - 1] + list(rng.integers(0, cfg.B, size=min(cfg.B, 2)))))
-        heads = sorted(set([0, cfg.Hq - 1]))
-        return reqs, heads
-    return None, None
+        return [([b for b in range(cfg.B) if b % cfg.Hq == h] or [0], [h])
+                for h in range(cfg.Hq)]
+    return [(None, None)]
 
 
 def name_is_full(cfg):
@@ -273,8 +325,20 @@ def test_tree_attention(name):
     t = c.gpu_tree()
     out, lse = c.gpu_attention(t)
     torch.cuda.synchronize()
-    reqs, heads = _attn_sample(c)
-    o_ref, lse_ref = c.oracle_attention(reqs, heads)
+    o_ref = lse_ref = None
+    for reqs, heads in _attn_sample(c):
+        say("attention oracle", name, "requests", reqs, "heads", heads)
+        o1, l1 = c.oracle_attention(reqs, heads)
+        if o_ref is None:
+            o_ref, lse_ref = o1, l1
+        else:
+            m = ~np.isnan(o1)
+            o_ref[m] = o1[m]
+            ml = ~np.isnan(l1)
+            lse_ref[ml] = l1[ml]
+    checked = ~np.isnan(o_ref[..., 0])
+    say("attention", name, "checked (request, node, head) rows", int(checked.sum()), "of",
+        checked.size)
     o = attn_to_f64(out)
     err, scale = assert_attention_close(o, o_ref, c.cfg.dtype)
     say("attention", name, "max abs err", err, "max |o|", scale)
@@ -282,6 +346,9 @@ def test_tree_attention(name):
     sel = ~np.isnan(lse_ref) & np.isfinite(lse_ref)
     assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
     assert np.all(np.isneginf(l[np.isneginf(lse_ref)]))
+    if name_is_full(c.cfg):
+        # every request and every head were compared
+        assert checked.any(axis=(1, 2)).all() and checked.any(axis=(0, 1)).all()
 
 
 # bf16 head dim 128 runs the DMA kernel in one variant per count of 16-row query
@@ -327,19 +394,22 @@ def test_attention_deterministic(name):
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
 
 
-def test_attention_split_size_invariance(monkeypatch):
-    """Other context split sizes change only rounding, within tolerance."""
+def test_attention_split_size_invariance():
+    """Other context split sizes and LDS ring depths (ddtree_tree_attention_tuned)
+    change only rounding, within tolerance."""
+    import tree_verification_build_amd as lib
     c = case("single")
     t = c.gpu_tree()
     base, _ = c.gpu_attention(t, want_lse=False)
-    for sk in ("64", "1024", "8192"):
-        monkeypatch.setenv("DDTREE_ATTN_SPLIT_KEYS", sk)
-        say("attention split keys", sk)
-        o, _ = c.gpu_attention(t, want_lse=False)
+    for tu in ({"split_keys": 64}, {"split_keys": 1024}, {"split_keys": 8192},
+               {"stages": 3}, {"stages": 4}, {"split_keys": 256, "stages": 4}):
+        say("attention tuning", tu)
+        o, _ = lib.ddtree_tree_attention_tuned(
+            c.d("q"), c.d("k_ctx"), c.d("v_ctx"), c.d("ctx_offsets"), c.inp["ctx_offsets"],
+            c.d("k_tree"), c.d("v_tree"), t, tuning=tu)
         torch.cuda.synchronize()
         d = (o.float() - base.float()).abs().max().item()
-        assert d <= 2e-2 * base.float().abs().max().item(), (sk, d)
-    monkeypatch.delenv("DDTREE_ATTN_SPLIT_KEYS")
+        assert d <= 2e-2 * base.float().abs().max().item(), (tu, d)
 
 
 @pytest.mark.parametrize("name", ["bf16_gqa", "batched"])

@@ -188,3 +188,22 @@ def test_wide_tree_two_vis_words():
     assert t["vis"].shape == (1, 65, 2)
     assert int(t["num_nodes"][0]) == 65
     assert (int(t["vis"][0, 64, 1]) & 1) == 1            # node 64 sees itself in word 1
+
+
+def test_hand_example_minus_inf_logprobs():
+    # A real log-prob may be -inf (a masked token).  D=2, K=2, depth-1 (-1, -inf),
+    # depth-2 (-1/2, -inf), budget 6 (every rank sequence fits: 2 + 4 nodes).
+    # Trace: n1=(p0,r0,-1); n2=(p1,r0,-1.5), which offers only its sibling (depth 2 = D);
+    # then four entries at -inf, taken by parent index, then rank: n3=(p0,r1),
+    # n4=(p1,r1), n5=(p3,r0), n6=(p3,r1).  No entry below depth D or past rank K-1
+    # is ever offered, so none can take a slot even though it would tie at -inf.
+    lp = np.array([[[-1.0, -np.inf], [-0.5, -np.inf]]], dtype=np.float32)
+    tok = np.array([[[1, 2], [3, 4]]], dtype=np.int32)
+    t = build_tree(lp, tok, np.array([9]), np.array([0]), 6)
+    assert int(t["num_nodes"][0]) == 7
+    assert list(t["parent"][0]) == [-1, 0, 1, 0, 1, 3, 3]
+    assert list(t["rank"][0]) == [-1, 0, 0, 1, 1, 0, 1]
+    assert list(t["depth"][0]) == [0, 1, 2, 1, 2, 2, 2]
+    assert list(t["token"][0]) == [9, 1, 3, 2, 4, 3, 4]
+    assert list(t["score"][0][:3]) == [0.0, -1.0, -1.5]
+    assert np.all(np.isneginf(t["score"][0][3:]))

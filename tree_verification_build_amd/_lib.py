@@ -42,6 +42,10 @@ lib.ddtree_tree_attention_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i3
 lib.ddtree_tree_attention_workspace_size.restype = _sz
 lib.ddtree_tree_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32, _i32,
                                       ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp]
+lib.ddtree_tree_attention_tuned_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp]
+lib.ddtree_tree_attention_tuned_workspace_size.restype = _sz
+lib.ddtree_tree_attention_tuned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32,
+                                            _i32, ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp, _vp]
 lib.ddtree_tree_attention_ranges_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp]
 lib.ddtree_tree_attention_ranges_workspace_size.restype = _sz
 lib.ddtree_tree_attention_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32,
@@ -68,6 +72,7 @@ lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c
                               ctypes.c_int64, _i32, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
+           "ddtree_tree_attention_tuned",
            "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_vocab_verify_greedy", "ddtree_verify_sample",
            "ddtree_verify_sample_lazy",
@@ -98,6 +103,18 @@ def _stream(stream):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _scratch(workspace, need, device, stream):
+    """The caller's workspace if it is large enough, else a new one.  A new one
+    is tied to `stream` when one is given, so that the caching allocator does
+    not hand its memory out again while the call's kernels may still use it."""
+    if workspace is not None and workspace.numel() >= need:
+        return workspace
+    ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
 
 
 def _dev(t, name, dtype=None, shape=None):
@@ -170,8 +187,7 @@ def ddtree_draft_topk(logits, K, tokens=None, logprobs=None, workspace=None, str
     _dev(tokens, "tokens", torch.int32, (*lead, K))
     _dev(logprobs, "logprobs", torch.float32, (*lead, K))
     need = int(lib.ddtree_draft_topk_workspace_size(rows, V, K))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    workspace = _scratch(workspace, need, dev, stream)
     _check(lib.ddtree_draft_topk(_ptr(logits), _dtype_code(logits), rows, V, K, _ptr(tokens),
                                  _ptr(logprobs), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
@@ -202,9 +218,32 @@ def ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, ctx_offsets_host) ->
     return int(lib.ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, p))
 
 
+class _CTuning(ctypes.Structure):
+    _fields_ = [("split_keys", ctypes.c_int32), ("stages", ctypes.c_int32)]
+
+
+def ddtree_tree_attention_tuned_workspace_size(B, N, Hq, Hkv, Dh, ctx_offsets_host, split_keys=0,
+                                               stages=0) -> int:
+    a, p = _host_offsets(ctx_offsets_host)
+    tu = _CTuning(split_keys, stages)
+    return int(lib.ddtree_tree_attention_tuned_workspace_size(B, N, Hq, Hkv, Dh, p,
+                                                              ctypes.byref(tu)))
+
+
 def ddtree_tree_attention(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree, v_tree, tree,
                           scale=None, out=None, want_lse=False, workspace=None, stream=None):
-    """Returns (out [B, N, Hq, Dh], lse [B, N, Hq] or None)."""
+    """Returns (out [B, N, Hq, Dh], lse [B, N, Hq] or None).  scale None: the
+    library's default, 1/sqrt(Dh)."""
+    return ddtree_tree_attention_tuned(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree,
+                                       v_tree, tree, scale=scale, out=out, want_lse=want_lse,
+                                       workspace=workspace, stream=stream, tuning=None)
+
+
+def ddtree_tree_attention_tuned(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree, v_tree,
+                                tree, scale=None, out=None, want_lse=False, workspace=None,
+                                stream=None, tuning=None):
+    """ddtree_tree_attention with a caller-chosen work split: tuning = dict(split_keys=...,
+    stages=...) (missing entries: 0, the planned choice), or None for the planned call."""
     B, N, Hq, Dh = q.shape
     Hkv = k_tree.shape[2]
     _dev(q, "q", (torch.bfloat16, torch.float32))
@@ -214,21 +253,23 @@ def ddtree_tree_attention(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree
     _dev(v_ctx, "v_ctx", q.dtype, tuple(k_ctx.shape))
     _dev(ctx_offsets, "ctx_offsets", torch.int32, (B + 1,))
     hoff, hptr = _host_offsets(ctx_offsets_host)
+    if hoff.shape != (B + 1,) or int(hoff[0]) != 0:
+        raise ValueError(f"ctx_offsets_host must hold B + 1 = {B + 1} offsets starting at 0")
     if k_ctx.shape[0] < int(hoff[-1]) or tuple(k_ctx.shape[1:]) != (Hkv, Dh):
         raise ValueError("k_ctx must be [ctx_offsets[B], Hkv, Dh]")
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype, tuple(q.shape))
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device) if want_lse else None
-    need = int(lib.ddtree_tree_attention_workspace_size(B, N, Hq, Hkv, Dh, hptr))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    if scale is None:
-        scale = 1.0 / float(Dh) ** 0.5
-    _check(lib.ddtree_tree_attention(
+    tu = None if tuning is None else _CTuning(int(tuning.get("split_keys", 0)),
+                                              int(tuning.get("stages", 0)))
+    tup = None if tu is None else ctypes.byref(tu)
+    need = int(lib.ddtree_tree_attention_tuned_workspace_size(B, N, Hq, Hkv, Dh, hptr, tup))
+    workspace = _scratch(workspace, need, q.device, stream)
+    _check(lib.ddtree_tree_attention_tuned(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), hptr, _ptr(k_tree), _ptr(v_tree),
-        tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), float(scale), _ptr(out), _ptr(lse),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+        tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), 0.0 if scale is None else float(scale),
+        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), tup, _stream(stream)))
     return out, lse
 
 
@@ -263,14 +304,11 @@ def ddtree_tree_attention_ranges(q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_
     _dev(out, "out", q.dtype, tuple(q.shape))
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device) if want_lse else None
     need = int(lib.ddtree_tree_attention_ranges_workspace_size(B, N, Hq, Hkv, Dh, hlp))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
-    if scale is None:
-        scale = 1.0 / float(Dh) ** 0.5
+    workspace = _scratch(workspace, need, q.device, stream)
     _check(lib.ddtree_tree_attention_ranges(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len), hsp, hlp,
-        _ptr(k_tree), _ptr(v_tree), tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), float(scale),
-        _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
+        _ptr(k_tree), _ptr(v_tree), tree.cstruct, Hq, Hkv, Dh, _dtype_code(q),
+        0.0 if scale is None else float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
 
 
@@ -293,8 +331,7 @@ def ddtree_vocab_reduce(logits, num_nodes, temperature=0.0, want_lse=False, work
     Rb = torch.empty((B, N, nb), dtype=torch.int64, device=dev) if temperature > 0 else None
     lse = torch.empty((B, N), dtype=torch.float32, device=dev) if want_lse else None
     need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    workspace = _scratch(workspace, need, dev, stream)
     _check(lib.ddtree_vocab_reduce(_ptr(logits), _dtype_code(logits), B, N, V, _ptr(num_nodes),
                                    float(temperature), _ptr(argmax), _ptr(maxv), _ptr(R),
                                    _ptr(Rb), _ptr(lse), _ptr(workspace), workspace.numel(),
@@ -334,8 +371,7 @@ def ddtree_vocab_verify_greedy(logits, tree, workspace=None, outputs=None, argma
     _dev(argmax, "argmax", torch.int32, (B, N))
     _dev(maxv, "maxv", torch.float32, (B, N))
     need = int(lib.ddtree_vocab_reduce_workspace_size(B, N, V))
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    workspace = _scratch(workspace, need, dev, stream)
     o = outputs or _walk_outputs(tree)
     _check(lib.ddtree_vocab_verify_greedy(_ptr(logits), _dtype_code(logits), V, tree.cstruct,
                                           _ptr(argmax), _ptr(maxv), _ptr(o["accept_len"]),

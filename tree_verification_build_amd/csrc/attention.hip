@@ -27,7 +27,7 @@
 // with an online softmax in base 2.  bf16 uses v_mfma_f32_16x16x32_bf16,
 // fp32 uses v_mfma_f32_16x16x4_f32.
 #include <algorithm>
-#include <cstdlib>
+#include <cmath>
 #include <vector>
 
 #include "common.hpp"
@@ -46,7 +46,9 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 of masked keys is 0
 
-constexpr int kTabMax = 16;
+// Requests whose split plan travels in the kernel arguments (about 0.8 KB of
+// table); larger batches look their splits up on the device.
+constexpr int kTabMax = 64;
 
 struct AttnArgs {
   const void* q;
@@ -62,13 +64,16 @@ struct AttnArgs {
   int B, N, W, Hq, Hkv, G, M;
   float scale_log2;   // scale * log2(e)
   int split_keys;
+  int total_splits;   // splits of the host plan: the grid's x extent and the rows of ws_o / ws_ml
   void* out;
   float* lse;
   void* ws_o;         // [total_splits * Hkv, M, Dh] unnormalised partial outputs
                       // (bf16 from the DMA kernel, fp32 from the register kernel)
   float2* ws_ml;      // [total_splits * Hkv, M] (running max in log2 units, sum)
   // split plan for B <= kTabMax (tab_n = B, else 0): request b owns splits
-  // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b] + tab_len[b])
+  // [tab_split0[b], tab_split0[b+1]) and context rows [tab_off[b], tab_off[b] + tab_len[b]).
+  // With the table the kernels never read the device context arrays, so the
+  // host copies alone decide what is read.
   int tab_n;
   int tab_split0[kTabMax + 1];
   int tab_off[kTabMax];
@@ -240,11 +245,15 @@ __device__ __forceinline__ void find_split(const AttnArgs& a, int sid, int SK, i
 __device__ __forceinline__ SplitItem lookup_split(const AttnArgs& a, int sid, int wave, int lane,
                                                   SplitItem* shared_item) {
   if (a.tab_n > 0) {
-    int b = 0;
-    while (b + 1 < a.tab_n && sid >= a.tab_split0[b + 1]) ++b;
     if (sid >= a.tab_split0[a.tab_n]) return SplitItem{-1, 0, 0, 0, 0};
-    return SplitItem{b, sid - a.tab_split0[b], a.tab_split0[b + 1] - a.tab_split0[b], a.tab_off[b],
-                     a.tab_len[b]};
+    // the last request whose first split is <= sid (every request has one)
+    int lo = 0, hi = a.tab_n;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.tab_split0[mid] <= sid) lo = mid; else hi = mid;
+    }
+    return SplitItem{lo, sid - a.tab_split0[lo], a.tab_split0[lo + 1] - a.tab_split0[lo],
+                     a.tab_off[lo], a.tab_len[lo]};
   }
   if (wave == 0) find_split(a, sid, a.split_keys, lane, shared_item);
   __syncthreads();
@@ -839,8 +848,12 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     for (int bb = lane; bb < b; bb += 64) start += nsplits(bb);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) start += __shfl_xor(start, o, 64);
+    // the device lengths must match the host copy the grid was planned from;
+    // if they do not, never read partials past the planned ones
+    if (start >= a.total_splits) return;
+    ns = min(ns, a.total_splits - start);
   }
-  if (ns == 1) return;
+  if (ns <= 1) return;
   const int node = r / a.G, head = kvh * a.G + r % a.G;
   const long orow = (static_cast<long>(b) * a.N + node) * a.Hq + head;
   elem* dst = static_cast<elem*>(a.out) + orow * DH;
@@ -924,24 +937,22 @@ int keys_per_tile(ddtree_dtype dt, int Dh, int /*qb*/) {
   return 1024 / ch;
 }
 
-// Keys per split: about `target` workgroups over the whole context (two per CU),
+// Keys per split: about 512 workgroups over the whole context (two per CU),
 // at least 320 keys (five 64-key tiles: each workgroup's prologue latency and
 // each partial's combine cost are spread over enough tiles; on an 8192-token
 // context 320 measured 6% faster than 256 and 4% faster than 384) and at most
-// 2048 (bounds the imbalance of ragged batches); whole tiles.
-int plan_split_keys(const int32_t* lens, int B, int Hkv, int kt) {
+// 2048 (bounds the imbalance of ragged batches); whole tiles.  A tuning
+// request (ddtree_tree_attention_tuned) replaces the plan with its own split
+// size.
+int plan_split_keys(const int32_t* lens, int B, int Hkv, int kt, const ddtree_attention_tuning* tu) {
   long total = 0;
   for (int b = 0; b < B; ++b) total += lens[b];
-  int target = 512;
-  if (const char* env = std::getenv("DDTREE_ATTN_TARGET_WGS")) target = std::max(1, atoi(env));
-  long sk = (total * Hkv + target - 1) / target;
+  constexpr int kTargetWorkgroups = 512;
+  long sk = (total * Hkv + kTargetWorkgroups - 1) / kTargetWorkgroups;
   sk = std::min<long>(std::max<long>(sk, 320), 2048);
   sk = std::max<long>(sk, kt);
   sk = (sk + kt - 1) / kt * kt;
-  if (const char* env = std::getenv("DDTREE_ATTN_SPLIT_KEYS")) {
-    const long v = atol(env);
-    if (v > 0) sk = (v + kt - 1) / kt * kt;
-  }
+  if (tu && tu->split_keys > 0) sk = (static_cast<long>(tu->split_keys) + kt - 1) / kt * kt;
   return static_cast<int>(std::min<long>(sk, 1L << 30));
 }
 
@@ -983,15 +994,8 @@ void launch_qb(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
 // LDS ring depth.  Two stages (64 KB) let two workgroups share a CU, each
 // with one tile in flight while it computes the other.  Three and four
 // stages (4-wave form only) measured no faster, also for grids of at most one
-// workgroup per CU, where they would not cost occupancy; DDTREE_ATTN_STAGES
+// workgroup per CU, where they would not cost occupancy; a tuning request
 // selects them.
-int dma_stages(int qb) {
-  int ns = 2;
-  if (const char* env = std::getenv("DDTREE_ATTN_STAGES")) ns = atoi(env);
-  if (qb > 4 || ns < 2 || ns > 4) ns = 2;
-  return ns;
-}
-
 template <int QB, int NS>
 void launch_dma_qbs(const AttnArgs& a, int total_splits, hipStream_t st) {
   constexpr int NW = QB <= 4 ? 4 : 8;
@@ -1001,9 +1005,9 @@ void launch_dma_qbs(const AttnArgs& a, int total_splits, hipStream_t st) {
 }
 
 template <int QB>
-void launch_dma_qb(const AttnArgs& a, int total_splits, hipStream_t st) {
+void launch_dma_qb(const AttnArgs& a, int total_splits, int stages, hipStream_t st) {
   if constexpr (QB <= 4) {
-    switch (dma_stages(QB)) {
+    switch (stages) {
       case 3: launch_dma_qbs<QB, 3>(a, total_splits, st); return;
       case 4: launch_dma_qbs<QB, 4>(a, total_splits, st); return;
       default: break;
@@ -1012,25 +1016,26 @@ void launch_dma_qb(const AttnArgs& a, int total_splits, hipStream_t st) {
   launch_dma_qbs<QB, 2>(a, total_splits, st);
 }
 
-void launch_dma(int qb, const AttnArgs& a, int total_splits, hipStream_t st) {
+void launch_dma(int qb, const AttnArgs& a, int total_splits, int stages, hipStream_t st) {
   switch (qb) {
-    case 1: launch_dma_qb<1>(a, total_splits, st); break;
-    case 2: launch_dma_qb<2>(a, total_splits, st); break;
-    case 3: launch_dma_qb<3>(a, total_splits, st); break;
-    case 4: launch_dma_qb<4>(a, total_splits, st); break;
-    case 5: launch_dma_qb<5>(a, total_splits, st); break;
-    case 6: launch_dma_qb<6>(a, total_splits, st); break;
-    case 7: launch_dma_qb<7>(a, total_splits, st); break;
-    default: launch_dma_qb<8>(a, total_splits, st); break;
+    case 1: launch_dma_qb<1>(a, total_splits, stages, st); break;
+    case 2: launch_dma_qb<2>(a, total_splits, stages, st); break;
+    case 3: launch_dma_qb<3>(a, total_splits, stages, st); break;
+    case 4: launch_dma_qb<4>(a, total_splits, stages, st); break;
+    case 5: launch_dma_qb<5>(a, total_splits, stages, st); break;
+    case 6: launch_dma_qb<6>(a, total_splits, stages, st); break;
+    case 7: launch_dma_qb<7>(a, total_splits, stages, st); break;
+    default: launch_dma_qb<8>(a, total_splits, stages, st); break;
   }
 }
 
-size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const int32_t* lens) {
+size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const int32_t* lens,
+                           const ddtree_attention_tuning* tu) {
   const int M = N * (Hq / Hkv);
   const int qb = (M + 15) / 16;
   size_t best = 0;
   for (ddtree_dtype dt : {DDTREE_BF16, DDTREE_F32}) {
-    const int sk = plan_split_keys(lens, B, Hkv, keys_per_tile(dt, Dh, qb));
+    const int sk = plan_split_keys(lens, B, Hkv, keys_per_tile(dt, Dh, qb), tu);
     bool multi;
     const int tot = count_splits(lens, B, sk, &multi);
     if (!multi) continue;
@@ -1048,7 +1053,7 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
                              const void* k_tree, const void* v_tree, const ddtree_tree* tree,
                              int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale,
                              void* out, float* lse, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+                             const ddtree_attention_tuning* tu, hipStream_t stream) {
   if (!q || !k_tree || !v_tree || !out) return fail(DDTREE_EINVAL, "%s: null pointer", who);
   if (dtype != DDTREE_BF16 && dtype != DDTREE_F32)
     return fail(DDTREE_EINVAL, "%s: unknown dtype %d", who, static_cast<int>(dtype));
@@ -1056,8 +1061,13 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     return fail(DDTREE_EINVAL, "%s: Hq=%d must be a multiple of Hkv=%d", who, Hq, Hkv);
   if (Dh != 64 && Dh != 128)
     return fail(DDTREE_EUNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", who, Dh);
+  // scale 0 selects the usual 1/sqrt(Dh)
+  if (scale == 0.0f) scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(Dh)));
   if (!(scale > 0.0f) || !(scale < __builtin_huge_valf()))
-    return fail(DDTREE_EINVAL, "%s: scale must be > 0 and finite", who);
+    return fail(DDTREE_EINVAL, "%s: scale must be > 0 and finite (or 0 for 1/sqrt(Dh))", who);
+  if (tu && (tu->split_keys < 0 || tu->stages < 0 || tu->stages == 1 || tu->stages > 4))
+    return fail(DDTREE_EINVAL, "%s: tuning: split_keys %d (>= 0), stages %d (0, 2, 3 or 4)", who,
+                tu->split_keys, tu->stages);
   const int B = tree->B, N = tree->N;
   const int M = N * (Hq / Hkv);
   if (M > 1024)
@@ -1071,7 +1081,7 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     return fail(DDTREE_EINVAL, "%s: tensors must be 16-byte aligned", who);
   const int qb = (std::min(M, 128) + 15) / 16;   // 16-row query blocks per slice
   const int kt = keys_per_tile(dtype, Dh, qb);
-  const int sk = plan_split_keys(lens, B, Hkv, kt);
+  const int sk = plan_split_keys(lens, B, Hkv, kt, tu);
   bool multi;
   const int splits = count_splits(lens, B, sk, &multi);
   a.q = q;
@@ -1090,6 +1100,7 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
   a.M = M;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.split_keys = sk;
+  a.total_splits = splits;
   a.tab_n = 0;
   if (B <= kTabMax) {
     a.tab_n = B;
@@ -1116,7 +1127,7 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     a.ws_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + need);
   }
   if (dtype == DDTREE_BF16) {
-    if (Dh == 128) launch_dma(qb, a, splits, stream);
+    if (Dh == 128) launch_dma(qb, a, splits, tu && tu->stages > 0 ? tu->stages : 2, stream);
     else launch_qb<PolicyBF16<64>>(qb, a, splits, stream);
   } else {
     if (Dh == 128) launch_qb<PolicyF32<128>>(qb, a, splits, stream);
@@ -1139,15 +1150,22 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
 }  // namespace
 }  // namespace ddt
 
-extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
-                                                       int32_t Hkv, int32_t Dh,
-                                                       const int32_t* ctx_offsets_host) {
+extern "C" size_t ddtree_tree_attention_tuned_workspace_size(int32_t B, int32_t N, int32_t Hq,
+                                                             int32_t Hkv, int32_t Dh,
+                                                             const int32_t* ctx_offsets_host,
+                                                             const ddtree_attention_tuning* tuning) {
   using namespace ddt;
   if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_offsets_host || (Dh != 64 && Dh != 128))
     return 0;
   std::vector<int32_t> lens(B);
   for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_offsets_host[b + 1] - ctx_offsets_host[b]);
-  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data());
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data(), tuning);
+}
+
+extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
+                                                       int32_t Hkv, int32_t Dh,
+                                                       const int32_t* ctx_offsets_host) {
+  return ddtree_tree_attention_tuned_workspace_size(B, N, Hq, Hkv, Dh, ctx_offsets_host, nullptr);
 }
 
 extern "C" size_t ddtree_tree_attention_ranges_workspace_size(int32_t B, int32_t N, int32_t Hq,
@@ -1158,17 +1176,17 @@ extern "C" size_t ddtree_tree_attention_ranges_workspace_size(int32_t B, int32_t
     return 0;
   std::vector<int32_t> lens(B);
   for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_len_host[b]);
-  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data());
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data(), nullptr);
 }
 
-extern "C" ddtree_status ddtree_tree_attention(
+extern "C" ddtree_status ddtree_tree_attention_tuned(
     const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_offsets,
     const int32_t* ctx_offsets_host, const void* k_tree, const void* v_tree,
     const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
     float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-    hipStream_t stream) {
+    const ddtree_attention_tuning* tuning, hipStream_t stream) {
   using namespace ddt;
-  const char* who = "ddtree_tree_attention";
+  const char* who = tuning ? "ddtree_tree_attention_tuned" : "ddtree_tree_attention";
   ddtree_status st = check_tree(tree, who);
   if (st != DDTREE_OK) return st;
   if (!ctx_offsets || !ctx_offsets_host) return fail(DDTREE_EINVAL, "%s: null pointer", who);
@@ -1185,7 +1203,18 @@ extern "C" ddtree_status ddtree_tree_attention(
   a.ctx_len = nullptr;
   return attention_impl(a, who, q, k_ctx, v_ctx, ctx_offsets_host, lens.data(), k_tree, v_tree,
                         tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
-                        stream);
+                        tuning, stream);
+}
+
+extern "C" ddtree_status ddtree_tree_attention(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_offsets,
+    const int32_t* ctx_offsets_host, const void* k_tree, const void* v_tree,
+    const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
+    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  return ddtree_tree_attention_tuned(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree,
+                                     v_tree, tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace,
+                                     workspace_bytes, nullptr, stream);
 }
 
 extern "C" ddtree_status ddtree_tree_attention_ranges(
@@ -1211,5 +1240,5 @@ extern "C" ddtree_status ddtree_tree_attention_ranges(
   a.ctx_len = ctx_len;
   return attention_impl(a, who, q, k_ctx, v_ctx, ctx_start_host, ctx_len_host, k_tree, v_tree,
                         tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
-                        stream);
+                        nullptr, stream);
 }

@@ -23,9 +23,9 @@
 // those two offers are computed beforehand by every lane for its own slot,
 // alongside the maximum, so the step's dependent chain after the maximum is
 // three lane reads and a few lane writes (~70 instructions per step in all).
-// Offers that do not exist score -inf through padding of the log-prob table
-// and are never taken: the loop runs exactly as many steps as the tree can
-// hold nodes.  Tokens, positions, child / sibling links and visibility rows
+// Offers that do not exist get key 0, below every real key (a real offer may
+// score -inf), and are never taken: the loop runs exactly as many steps as
+// the tree can hold nodes.  Tokens, positions, child / sibling links and visibility rows
 // are rebuilt afterwards, all lanes in parallel (visibility by pointer
 // jumping over parent links).
 #include "common.hpp"
@@ -124,8 +124,7 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
   // d, ranks 0..K-1, then -inf up to kRow; rows D and D + 1 (depths D + 1,
   // D + 2: children of depth-D nodes and their offers) are all -inf.
   // An offer that does not exist (a child below depth D, a sibling past rank
-  // K - 1) then simply scores -inf, which no real offer ties or trails, and
-  // the loop stops after the last real node, so such offers are never taken.
+  // K - 1) reads -inf here; its key is then set below every real key.
   float* s_T = s_table;
 #pragma unroll 1
   for (int e = lane; e < (D + 2) * kRow; e += 64) s_T[e] = -__builtin_huge_valf();
@@ -197,8 +196,13 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
     const uint32_t bh = wave_max_bcast_u32<HALF>(mh);
     const uint64_t tied = __ballot(mh == bh);
     int w = __builtin_ctzll(tied);
-    if (__builtin_expect(__builtin_popcountll(tied) > 1, 0))
-      w = __builtin_ctzll(__ballot(mh == bh && ml == wave_max_bcast_u32<HALF>(mh == bh ? ml : 0u)));
+    if (__builtin_expect(__builtin_popcountll(tied) > 1, 0)) {
+      // the cross-lane maximum runs with every lane active: written as the
+      // right operand of && it would run only in the lanes where the left one
+      // holds, and read stale values from the others
+      const uint32_t bl = wave_max_bcast_u32<HALF>(mh == bh ? ml : 0u);
+      w = __builtin_ctzll(__ballot(mh == bh && ml == bl));
+    }
     // readlane yields a signed int: cast before widening, or the low word sign-extends
     const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(ml, w));
     const float cs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mcs), w));
@@ -210,7 +214,12 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
     // the parent's next child
     const uint32_t lo_c = static_cast<uint32_t>(make_key_bits(0u, i, 0, depth + 1, i));
     const uint32_t lo_s = ((lo & 0xFFFFFF00u) - 0x10000u) | static_cast<uint32_t>(i);
-    const uint32_t ch = ord_f32(cs), sh = ord_f32(ss);
+    // an offer that does not exist (a child below depth D, a sibling past
+    // rank K - 1) gets key 0, below every real key, -inf scores included (a
+    // real log-prob may be -inf, e.g. a masked token): it is never taken
+    const int rank = 255 - static_cast<int>((lo >> 16) & 0xFF);
+    const uint32_t ch = depth < D ? ord_f32(cs) : 0u;
+    const uint32_t sh = rank + 1 < K ? ord_f32(ss) : 0u;
     const int il = i & 63, pl = parent & 63;
     if (!TWO || i < 64) {
       rh0 = put_lane(rh0, bh, il);
