@@ -222,6 +222,37 @@ ddtree_status ddtree_tree_attention_tuned(const void* q, const void* k_ctx, cons
                                           hipStream_t stream);
 
 /*
+ * ddtree_tree_attention_noalloc -- ddtree_tree_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels, split plan and
+ * outputs, bit for bit, with the split partials kept in a device array of the
+ * library instead of a caller workspace.  The call itself allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); the first call on a
+ * device looks the array's address up on that device.
+ *   Every argument except the workspace: as ddtree_tree_attention.
+ *   The array holds DDTREE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU for the life
+ *   of the process; a call whose split partials need more (see
+ *   ddtree_tree_attention_workspace_size; the five reference workloads need at
+ *   most ~41 MB) is rejected with DDTREE_EUNSUPPORTED before any launch.
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (different streams or host threads without ordering between them)
+ *   race and give undefined outputs; calls ordered on one stream do not.  The
+ *   kernels need no initialised contents (every partial they read was written
+ *   by the same call).
+ * Errors: as ddtree_tree_attention; DDTREE_EUNSUPPORTED when the partials do
+ *         not fit; DDTREE_EDEVICE when the array's address cannot be obtained.
+ */
+#define DDTREE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+ddtree_status ddtree_tree_attention_noalloc(const void* q, const void* k_ctx, const void* v_ctx,
+                                            const int32_t* ctx_offsets,
+                                            const int32_t* ctx_offsets_host, const void* k_tree,
+                                            const void* v_tree, const ddtree_tree* tree,
+                                            int32_t Hq, int32_t Hkv, int32_t Dh,
+                                            ddtree_dtype dtype, float scale, void* out,
+                                            float* lse, hipStream_t stream);
+
+/*
  * ddtree_tree_attention_ranges -- the same tree attention with each request's
  * context given as a (start, length) range of rows instead of packed offsets,
  * so that a batch can keep its caches in per-request slabs that grow in place

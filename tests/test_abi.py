@@ -189,6 +189,34 @@ def test_host_validation_rejects_bad_arguments():
                                            None) == 2
 
 
+def test_noalloc_attention_rejects_partials_beyond_its_scratch():
+    """ddtree_tree_attention_noalloc checks the plan against its fixed device
+    array on the host, before anything is launched (no GPU needed here)."""
+    from tree_verification_build_amd._lib import lib, NOALLOC_SCRATCH_BYTES
+    import tree_verification_build_amd as t
+    fake = ctypes.c_void_p(16)
+    tree = _fake_tree(B=64, N=33, D=8, K=4, W=1)
+    big = np.arange(65, dtype=np.int64) * 65536          # 64 requests x 65536 keys
+    offs = (ctypes.c_int32 * 65)(*[int(x) for x in big])
+    need = t.ddtree_tree_attention_workspace_size(64, 33, 8, 8, 128, big.astype(np.int32))
+    assert need > NOALLOC_SCRATCH_BYTES
+    assert lib.ddtree_tree_attention_noalloc(fake, fake, fake, fake, offs, fake, fake,
+                                             ctypes.byref(tree), 8, 8, 128, 1, 0.0, fake, None,
+                                             None) == 2
+    lib.ddtree_last_error.restype = ctypes.c_char_p
+    assert b"scratch" in lib.ddtree_last_error()
+    assert lib.ddtree_tree_attention_noalloc(fake, fake, fake, fake, offs, fake, fake,
+                                             ctypes.byref(tree), 8, 8, 96, 1, 0.0, fake, None,
+                                             None) == 2                     # head_dim 96
+    # the five workloads' partials fit
+    import workloads
+    for name in ("tiny", "single", "batched", "long", "ragged"):
+        cfg = workloads.config(name)
+        o = np.concatenate([[0], np.cumsum(workloads.ctx_lengths(cfg))]).astype(np.int32)
+        assert t.ddtree_tree_attention_workspace_size(cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh,
+                                                      o) <= NOALLOC_SCRATCH_BYTES, name
+
+
 def test_workspace_sizes_are_host_only_and_sane():
     import tree_verification_build_amd as t
     offs = np.array([0, 8192], np.int32)

@@ -46,6 +46,8 @@ lib.ddtree_tree_attention_tuned_workspace_size.argtypes = [_i32, _i32, _i32, _i3
 lib.ddtree_tree_attention_tuned_workspace_size.restype = _sz
 lib.ddtree_tree_attention_tuned.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32,
                                             _i32, ctypes.c_int, _f32, _vp, _vp, _vp, _sz, _vp, _vp]
+lib.ddtree_tree_attention_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32, _i32,
+                                              _i32, ctypes.c_int, _f32, _vp, _vp, _vp]
 lib.ddtree_tree_attention_ranges_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp]
 lib.ddtree_tree_attention_ranges_workspace_size.restype = _sz
 lib.ddtree_tree_attention_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32,
@@ -72,7 +74,7 @@ lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c
                               ctypes.c_int64, _i32, _vp, _vp, _vp]
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
-           "ddtree_tree_attention_tuned",
+           "ddtree_tree_attention_tuned", "ddtree_tree_attention_noalloc",
            "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_vocab_verify_greedy", "ddtree_verify_sample",
            "ddtree_verify_sample_lazy",
@@ -270,6 +272,37 @@ def ddtree_tree_attention_tuned(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, 
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), hptr, _ptr(k_tree), _ptr(v_tree),
         tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), 0.0 if scale is None else float(scale),
         _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), tup, _stream(stream)))
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DDTREE_NOALLOC_SCRATCH_BYTES
+
+
+def ddtree_tree_attention_noalloc(q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree, v_tree,
+                                  tree, out, lse=None, scale=None, stream=None):
+    """ddtree_tree_attention with the split partials in the library's device
+    array: the C call allocates nothing, so `out` (and `lse`, if wanted) must be
+    given.  Returns (out, lse)."""
+    B, N, Hq, Dh = q.shape
+    Hkv = k_tree.shape[2]
+    _dev(q, "q", (torch.bfloat16, torch.float32))
+    _dev(k_tree, "k_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(v_tree, "v_tree", q.dtype, (B, N, Hkv, Dh))
+    _dev(k_ctx, "k_ctx", q.dtype)
+    _dev(v_ctx, "v_ctx", q.dtype, tuple(k_ctx.shape))
+    _dev(ctx_offsets, "ctx_offsets", torch.int32, (B + 1,))
+    _dev(out, "out", q.dtype, tuple(q.shape))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (B, N, Hq))
+    hoff, hptr = _host_offsets(ctx_offsets_host)
+    if hoff.shape != (B + 1,) or int(hoff[0]) != 0:
+        raise ValueError(f"ctx_offsets_host must hold B + 1 = {B + 1} offsets starting at 0")
+    if k_ctx.shape[0] < int(hoff[-1]) or tuple(k_ctx.shape[1:]) != (Hkv, Dh):
+        raise ValueError("k_ctx must be [ctx_offsets[B], Hkv, Dh]")
+    _check(lib.ddtree_tree_attention_noalloc(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), hptr, _ptr(k_tree), _ptr(v_tree),
+        tree.cstruct, Hq, Hkv, Dh, _dtype_code(q), 0.0 if scale is None else float(scale),
+        _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

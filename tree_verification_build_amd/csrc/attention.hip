@@ -28,9 +28,15 @@
 // fp32 uses v_mfma_f32_16x16x4_f32.
 #include <algorithm>
 #include <cmath>
-#include <vector>
+#include <mutex>
 
 #include "common.hpp"
+
+// Split partials of ddtree_tree_attention_noalloc: a device array of fixed
+// size in place of a caller workspace (each GPU holds its own copy until the
+// process ends).  Its name in host code is only a stand-in: host code uses the
+// device address that scratch_address() looks up.
+static __device__ __align__(256) unsigned char scratch[DDTREE_NOALLOC_SCRATCH_BYTES];
 
 namespace ddt {
 
@@ -944,9 +950,19 @@ int keys_per_tile(ddtree_dtype dt, int Dh, int /*qb*/) {
 // 2048 (bounds the imbalance of ragged batches); whole tiles.  A tuning
 // request (ddtree_tree_attention_tuned) replaces the plan with its own split
 // size.
-int plan_split_keys(const int32_t* lens, int B, int Hkv, int kt, const ddtree_attention_tuning* tu) {
+// Host copy of the context ranges: packed offsets [B+1], or per-request
+// (start, length) pairs.  Read in place: the host side allocates nothing.
+struct HostRanges {
+  const int32_t* offs;    // packed form, or null
+  const int32_t* start;   // range form
+  const int32_t* len;
+  int start_of(int b) const { return offs ? offs[b] : start[b]; }
+  int len_of(int b) const { return std::max(0, offs ? offs[b + 1] - offs[b] : len[b]); }
+};
+
+int plan_split_keys(const HostRanges& hr, int B, int Hkv, int kt, const ddtree_attention_tuning* tu) {
   long total = 0;
-  for (int b = 0; b < B; ++b) total += lens[b];
+  for (int b = 0; b < B; ++b) total += hr.len_of(b);
   constexpr int kTargetWorkgroups = 512;
   long sk = (total * Hkv + kTargetWorkgroups - 1) / kTargetWorkgroups;
   sk = std::min<long>(std::max<long>(sk, 320), 2048);
@@ -956,11 +972,11 @@ int plan_split_keys(const int32_t* lens, int B, int Hkv, int kt, const ddtree_at
   return static_cast<int>(std::min<long>(sk, 1L << 30));
 }
 
-int count_splits(const int32_t* lens, int B, int sk, bool* any_multi) {
+int count_splits(const HostRanges& hr, int B, int sk, bool* any_multi) {
   int tot = 0;
   *any_multi = false;
   for (int b = 0; b < B; ++b) {
-    const int L = lens[b];
+    const int L = hr.len_of(b);
     const int nb = L > 0 ? (L + sk - 1) / sk : 1;
     *any_multi |= nb > 1;
     tot += nb;
@@ -1029,15 +1045,15 @@ void launch_dma(int qb, const AttnArgs& a, int total_splits, int stages, hipStre
   }
 }
 
-size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const int32_t* lens,
+size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const HostRanges& hr,
                            const ddtree_attention_tuning* tu) {
   const int M = N * (Hq / Hkv);
   const int qb = (M + 15) / 16;
   size_t best = 0;
   for (ddtree_dtype dt : {DDTREE_BF16, DDTREE_F32}) {
-    const int sk = plan_split_keys(lens, B, Hkv, keys_per_tile(dt, Dh, qb), tu);
+    const int sk = plan_split_keys(hr, B, Hkv, keys_per_tile(dt, Dh, qb), tu);
     bool multi;
-    const int tot = count_splits(lens, B, sk, &multi);
+    const int tot = count_splits(hr, B, sk, &multi);
     if (!multi) continue;
     const size_t need = static_cast<size_t>(tot) * Hkv * M * (Dh * sizeof(float) + sizeof(float2));
     best = std::max(best, need);
@@ -1045,11 +1061,17 @@ size_t workspace_bytes_for(int B, int N, int Hq, int Hkv, int Dh, const int32_t*
   return best;
 }
 
-// Shared body of the packed-offset and range forms.  starts/lens: host copies
-// of the context ranges (validated by the caller); a.ctx_offsets or
-// a.ctx_start/ctx_len already set to the device arrays.
+ddtree_status attention_impl_args_error(const char* who, int Hq, int Hkv, int Dh) {
+  if (Dh != 64 && Dh != 128)
+    return fail(DDTREE_EUNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", who, Dh);
+  return fail(DDTREE_EINVAL, "%s: Hq=%d must be a multiple of Hkv=%d", who, Hq, Hkv);
+}
+
+// Shared body of the packed-offset and range forms.  hr: host copy of the
+// context ranges (validated by the caller); a.ctx_offsets or a.ctx_start /
+// ctx_len already set to the device arrays.
 ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const void* k_ctx,
-                             const void* v_ctx, const int32_t* starts, const int32_t* lens,
+                             const void* v_ctx, const HostRanges& hr,
                              const void* k_tree, const void* v_tree, const ddtree_tree* tree,
                              int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale,
                              void* out, float* lse, void* workspace, size_t workspace_bytes,
@@ -1074,16 +1096,16 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     return fail(DDTREE_EUNSUPPORTED, "%s: %d query rows per KV head (N * Hq / Hkv) exceed 1024",
                 who, M);
   long total = 0;
-  for (int b = 0; b < B; ++b) total += lens[b];
+  for (int b = 0; b < B; ++b) total += hr.len_of(b);
   if (total > 0 && (!k_ctx || !v_ctx)) return fail(DDTREE_EINVAL, "%s: null context K/V", who);
   if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
       (k_ctx && !aligned16(k_ctx)) || (v_ctx && !aligned16(v_ctx)))
     return fail(DDTREE_EINVAL, "%s: tensors must be 16-byte aligned", who);
   const int qb = (std::min(M, 128) + 15) / 16;   // 16-row query blocks per slice
   const int kt = keys_per_tile(dtype, Dh, qb);
-  const int sk = plan_split_keys(lens, B, Hkv, kt, tu);
+  const int sk = plan_split_keys(hr, B, Hkv, kt, tu);
   bool multi;
-  const int splits = count_splits(lens, B, sk, &multi);
+  const int splits = count_splits(hr, B, sk, &multi);
   a.q = q;
   a.k_ctx = k_ctx;
   a.v_ctx = v_ctx;
@@ -1107,9 +1129,9 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     int acc = 0;
     for (int b = 0; b < B; ++b) {
       a.tab_split0[b] = acc;
-      a.tab_off[b] = starts[b];
-      a.tab_len[b] = lens[b];
-      acc += lens[b] > 0 ? (lens[b] + sk - 1) / sk : 1;
+      a.tab_off[b] = hr.start_of(b);
+      a.tab_len[b] = hr.len_of(b);
+      acc += a.tab_len[b] > 0 ? (a.tab_len[b] + sk - 1) / sk : 1;
     }
     a.tab_split0[B] = acc;
   }
@@ -1147,6 +1169,73 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
   return check_launch(who);
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU has its own copy of the array).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+ddtree_status scratch_address(void** out, const char* who) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DDTREE_EDEVICE, "%s: no current device (or device %d beyond %d)", who, dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DDTREE_EDEVICE, "%s: hipGetSymbolAddress of the scratch array: %s", who,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return DDTREE_OK;
+}
+
+// Validation and launch of the packed-offset form (planned, tuned or no-allocation).
+ddtree_status packed_attention(const char* who, const void* q, const void* k_ctx,
+                               const void* v_ctx, const int32_t* ctx_offsets,
+                               const int32_t* ctx_offsets_host, const void* k_tree,
+                               const void* v_tree, const ddtree_tree* tree, int32_t Hq,
+                               int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               const ddtree_attention_tuning* tuning, bool use_scratch,
+                               hipStream_t stream) {
+  ddtree_status st = check_tree(tree, who);
+  if (st != DDTREE_OK) return st;
+  if (!ctx_offsets || !ctx_offsets_host) return fail(DDTREE_EINVAL, "%s: null pointer", who);
+  const int B = tree->B;
+  if (ctx_offsets_host[0] != 0) return fail(DDTREE_EINVAL, "%s: ctx_offsets[0] must be 0", who);
+  for (int b = 0; b < B; ++b)
+    if (ctx_offsets_host[b + 1] < ctx_offsets_host[b])
+      return fail(DDTREE_EINVAL, "%s: ctx_offsets must be non-decreasing", who);
+  const HostRanges hr{ctx_offsets_host, nullptr, nullptr};
+  if (use_scratch) {
+    if (Hkv < 1 || Hq % Hkv != 0 || (Dh != 64 && Dh != 128))
+      return attention_impl_args_error(who, Hq, Hkv, Dh);
+    const size_t need = workspace_bytes_for(B, tree->N, Hq, Hkv, Dh, hr, nullptr);
+    if (need > DDTREE_NOALLOC_SCRATCH_BYTES)
+      return fail(DDTREE_EUNSUPPORTED,
+                  "%s: the split partials need %zu bytes, more than the %zu bytes of its device "
+                  "scratch (use ddtree_tree_attention with a workspace)",
+                  who, need, static_cast<size_t>(DDTREE_NOALLOC_SCRATCH_BYTES));
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      st = scratch_address(&workspace, who);
+      if (st != DDTREE_OK) return st;
+      workspace_bytes = DDTREE_NOALLOC_SCRATCH_BYTES;
+    }
+  }
+  AttnArgs a;
+  a.ctx_offsets = ctx_offsets;
+  a.ctx_start = nullptr;
+  a.ctx_len = nullptr;
+  return attention_impl(a, who, q, k_ctx, v_ctx, hr, k_tree, v_tree, tree, Hq, Hkv, Dh, dtype,
+                        scale, out, lse, workspace, workspace_bytes, tuning, stream);
+}
+
 }  // namespace
 }  // namespace ddt
 
@@ -1157,9 +1246,8 @@ extern "C" size_t ddtree_tree_attention_tuned_workspace_size(int32_t B, int32_t 
   using namespace ddt;
   if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_offsets_host || (Dh != 64 && Dh != 128))
     return 0;
-  std::vector<int32_t> lens(B);
-  for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_offsets_host[b + 1] - ctx_offsets_host[b]);
-  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data(), tuning);
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, HostRanges{ctx_offsets_host, nullptr, nullptr},
+                             tuning);
 }
 
 extern "C" size_t ddtree_tree_attention_workspace_size(int32_t B, int32_t N, int32_t Hq,
@@ -1174,9 +1262,8 @@ extern "C" size_t ddtree_tree_attention_ranges_workspace_size(int32_t B, int32_t
   using namespace ddt;
   if (B < 1 || N < 1 || Hkv < 1 || Hq % Hkv != 0 || !ctx_len_host || (Dh != 64 && Dh != 128))
     return 0;
-  std::vector<int32_t> lens(B);
-  for (int b = 0; b < B; ++b) lens[b] = std::max(0, ctx_len_host[b]);
-  return workspace_bytes_for(B, N, Hq, Hkv, Dh, lens.data(), nullptr);
+  return workspace_bytes_for(B, N, Hq, Hkv, Dh, HostRanges{nullptr, ctx_len_host, ctx_len_host},
+                             nullptr);
 }
 
 extern "C" ddtree_status ddtree_tree_attention_tuned(
@@ -1185,25 +1272,20 @@ extern "C" ddtree_status ddtree_tree_attention_tuned(
     const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
     float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
     const ddtree_attention_tuning* tuning, hipStream_t stream) {
-  using namespace ddt;
-  const char* who = tuning ? "ddtree_tree_attention_tuned" : "ddtree_tree_attention";
-  ddtree_status st = check_tree(tree, who);
-  if (st != DDTREE_OK) return st;
-  if (!ctx_offsets || !ctx_offsets_host) return fail(DDTREE_EINVAL, "%s: null pointer", who);
-  const int B = tree->B;
-  if (ctx_offsets_host[0] != 0) return fail(DDTREE_EINVAL, "%s: ctx_offsets[0] must be 0", who);
-  for (int b = 0; b < B; ++b)
-    if (ctx_offsets_host[b + 1] < ctx_offsets_host[b])
-      return fail(DDTREE_EINVAL, "%s: ctx_offsets must be non-decreasing", who);
-  std::vector<int32_t> lens(B);
-  for (int b = 0; b < B; ++b) lens[b] = ctx_offsets_host[b + 1] - ctx_offsets_host[b];
-  AttnArgs a;
-  a.ctx_offsets = ctx_offsets;
-  a.ctx_start = nullptr;
-  a.ctx_len = nullptr;
-  return attention_impl(a, who, q, k_ctx, v_ctx, ctx_offsets_host, lens.data(), k_tree, v_tree,
-                        tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
-                        tuning, stream);
+  return ddt::packed_attention(tuning ? "ddtree_tree_attention_tuned" : "ddtree_tree_attention",
+                               q, k_ctx, v_ctx, ctx_offsets, ctx_offsets_host, k_tree, v_tree,
+                               tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace,
+                               workspace_bytes, tuning, false, stream);
+}
+
+extern "C" ddtree_status ddtree_tree_attention_noalloc(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_offsets,
+    const int32_t* ctx_offsets_host, const void* k_tree, const void* v_tree,
+    const ddtree_tree* tree, int32_t Hq, int32_t Hkv, int32_t Dh, ddtree_dtype dtype,
+    float scale, void* out, float* lse, hipStream_t stream) {
+  return ddt::packed_attention("ddtree_tree_attention_noalloc", q, k_ctx, v_ctx, ctx_offsets,
+                               ctx_offsets_host, k_tree, v_tree, tree, Hq, Hkv, Dh, dtype, scale,
+                               out, lse, nullptr, 0, nullptr, true, stream);
 }
 
 extern "C" ddtree_status ddtree_tree_attention(
@@ -1238,7 +1320,8 @@ extern "C" ddtree_status ddtree_tree_attention_ranges(
   a.ctx_offsets = nullptr;
   a.ctx_start = ctx_start;
   a.ctx_len = ctx_len;
-  return attention_impl(a, who, q, k_ctx, v_ctx, ctx_start_host, ctx_len_host, k_tree, v_tree,
+  return attention_impl(a, who, q, k_ctx, v_ctx, HostRanges{nullptr, ctx_start_host, ctx_len_host},
+                        k_tree, v_tree,
                         tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
                         nullptr, stream);
 }
