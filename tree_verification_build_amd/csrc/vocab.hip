@@ -114,8 +114,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes, int S,
     int chunk, uint64_t* __restrict__ ws_key, float2* __restrict__ ws_ms,
     int32_t* __restrict__ argmax, float* __restrict__ maxv,
-    float* __restrict__ lse,
-    uint64_t* __restrict__ zero_R) {
+    float* __restrict__ lse) {
   constexpr int E = Vec<T>::E;
   constexpr int kWaves = kSplitThreads / kWave;
   __shared__ uint64_t s_key[kWaves];
@@ -192,8 +191,6 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(
   }
   __syncthreads();
   if (tid == 0) {
-    // the streamed sampling pass adds its weight sums into R: slice 0 clears it
-    if (zero_R && s == 0) zero_R[row] = 0;
     for (int w = 1; w < kWaves; ++w) {
       key = s_key[w] > key ? s_key[w] : key;
       if (kLse) lse_merge(m, sum, s_ms[w].x, s_ms[w].y);
@@ -513,122 +510,356 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
   }
 }
 
-// Sampling weights of bf16 rows whose maximum is already known from the greedy
-// pass (the same maximum and lowest index the sampling row kernel finds; when
-// that pass split the rows, this kernel merges their slice keys and writes
-// argmax and max itself, which saves the merge kernel's launch).  With m
-// known the row need not stay in registers: one or two 1024-thread workgroups
-// per row (two take half of the row's blocks each, so that 528 rows do not
-// leave a second round of 16 on 512 workgroup slots) stream it block by block
-// (DDTREE_R_BLOCK tokens, four 16-byte vectors per thread, the next block's
-// loads in flight while the current one is weighed); two workgroups share a
-// CU, and the loads of one overlap the arithmetic of the other.  Weights come
-// from the LDS table of weight() (common.hpp); a logit outside its window is
-// re-read and weighed with weight() itself.
-__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void wsum_kernel(
-    const uint16_t* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
-    WeightConsts wc, int S, const uint64_t* __restrict__ ws_key, int32_t* __restrict__ argmax,
+// Sampling mode for bf16 rows (no log-sum-exp): every logit leaves HBM once
+// and is weighed from registers.  Persistent workgroups of 1024 threads, one
+// per CU, take rows r, r + G, r + 2G, ... (G workgroups).  A row is held in
+// registers (MAXP 16-byte vectors per thread: vector p of thread t covers
+// tokens p * 8192 + 8t .. + 7).  Per row: the row maximum (a float maximum,
+// then the lowest index holding it), a table of weight() in LDS for the row's
+// window of bf16 patterns, then the weight pass, which, as soon as a vector's
+// eight logits are weighed, issues the load of the same vector of the
+// workgroup's next row into the same registers: the next row streams in
+// while this one is weighed, so HBM stays busy while the CU computes.
+//
+// Table lookup with packed 16-bit arithmetic, two logits per operation: for
+// the magnitude pattern a of a logit (its 15 low bits), off = hi - a wraps
+// to >= 0x8000 above the window (weight 0 there), lies in [0, span) inside it
+// and in [span, 0x7FFF] below it; min(off, span) is the entry within its
+// sign's half of the table (entry span of each half is 0), and the sign bit
+// of the pattern, kept in place, adds the negative half's 32768-byte offset.
+// Logits outside the window read a sentinel (2^56) that the sums count in
+// their top bits; below-window ones (tiny magnitudes) are then weighed with
+// weight() itself after the pass, above-window ones weigh 0, so every weight
+// is weight()'s own value.
+constexpr int kPipeNegEntries = 4096;                         // negative half: byte 32768
+constexpr uint64_t kOutside = 1ull << 56;   // sentinel of the outside entries
+constexpr int kPipeTabEntries = kPipeNegEntries + kTabSpan + 1;
+
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
+}
+typedef int16_t i16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2_t, a),
+                                                                __builtin_bit_cast(i16x2_t, b)));
+}
+__device__ __forceinline__ uint32_t pk_ashr15_i16(uint32_t a) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2_t, a) >> i16x2_t{15, 15});
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a),
+                                                                __builtin_bit_cast(u16x2_t, b)));
+}
+
+// Wave reductions by DPP row moves and lane reads: no shuffle-index
+// registers (the row kernel below has none to spare).
+__device__ __forceinline__ uint64_t wave_sum_u64_dpp(uint64_t v) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+#define DDT_ROW_ADD(ctrl)                                                                         \
+  do {                                                                                            \
+    const uint32_t l2 = static_cast<uint32_t>(                                                    \
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(lo), ctrl, 0xF, 0xF, false));             \
+    const uint32_t h2 = static_cast<uint32_t>(                                                    \
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(hi), ctrl, 0xF, 0xF, false));             \
+    const uint64_t t = ((static_cast<uint64_t>(hi) << 32) | lo) + ((static_cast<uint64_t>(h2) << 32) | l2); \
+    lo = static_cast<uint32_t>(t);                                                                \
+    hi = static_cast<uint32_t>(t >> 32);                                                          \
+  } while (0)
+  DDT_ROW_ADD(0xB1);    // quad_perm [1, 0, 3, 2]
+  DDT_ROW_ADD(0x4E);    // quad_perm [2, 3, 0, 1]
+  DDT_ROW_ADD(0x124);   // row_ror 4
+  DDT_ROW_ADD(0x128);   // row_ror 8
+#undef DDT_ROW_ADD
+  uint64_t tot = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    tot += (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 16 * r))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 16 * r));
+  return tot;
+}
+
+__device__ __forceinline__ float wave_max_f32_dpp(float x) { return unord_f32(wave_max_u32(ord_f32(x))); }
+__device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t x) { return ~wave_max_u32(~x); }
+
+template <int MAXP, bool WHOLE>
+__global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
+    const uint16_t* __restrict__ logits, int rows, int N, int V,
+    const int32_t* __restrict__ num_nodes, WeightConsts wc, int32_t* __restrict__ argmax,
     float* __restrict__ maxv, uint64_t* __restrict__ R, uint64_t* __restrict__ Rb) {
   constexpr int E = 8;
   constexpr int kWaves = kRowThreads / kWave;
   constexpr int kQ = DDTREE_R_BLOCK / (kRowThreads * E);   // vectors per thread per block
-  static_assert(kQ * E <= 32, "miss bits of one block fit a word");
-  __shared__ uint64_t s_tab[kTabEntries];
+  static_assert(kQ == 4, "four 8192-token vectors per weight block");
+  __shared__ uint64_t s_tab[kPipeTabEntries];
   __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
-  __shared__ uint64_t s_rowkey;
-  const int row = blockIdx.x;
-  const int b = row / N, n = row % N;
+  __shared__ float s_f[kWaves];
+  __shared__ uint32_t s_i[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
-  // workgroup y of gridDim.y takes blocks [blk0, blk1) of the row
-  const int per = (nb + gridDim.y - 1) / gridDim.y;
-  const int blk0 = blockIdx.y * per, blk1 = min(nb, blk0 + per);
-  if (blk0 >= blk1) return;
-  const bool valid = n < num_nodes[b];
-  float m;
-  if (S > 1) {
-    // the greedy pass left S slice keys per row: merged here, as its merge
-    // kernel would (largest packed key: argmax and max), and written once
-    if (wave == 0) {
-      uint64_t key = 0;
-      for (int k = lane; k < S; k += kWave) {
-        const uint64_t kk = ws_key[static_cast<long>(row) * S + k];
-        key = kk > key ? kk : key;
+  int row = blockIdx.x;
+  if (row >= rows) return;
+  constexpr uint32_t kNegInf2 = Vec<uint16_t>::kNegInfWord;
+  // Loads are unconditional, from addresses that are always inside the
+  // logits: a load under a condition becomes a load into other registers
+  // plus a copy, and the copy waits for the load.  Vector p of a row past its
+  // end (WHOLE false) re-reads the row's last vector and is masked to -inf
+  // where it is used; with no next row, the loads re-read vector 0 of this
+  // row (cached, and never used).
+  // t8: this thread's first token of each vector, redefined opaquely every row
+  // so that the compiler computes each vector's offset where it loads it
+  // instead of keeping MAXP offsets live across the row loop
+  uint32_t t8 = tid * E;
+  auto vload = [&](int r, int p) -> u32x4_t {
+    uint32_t i = t8 + static_cast<uint32_t>(p * kRowThreads * E);
+    if (!WHOLE) i = min(i, static_cast<uint32_t>(V - E));
+    return *reinterpret_cast<const u32x4_t*>(logits + static_cast<long>(r) * V + i);
+  };
+  auto inrow = [&](int p) { return WHOLE || t8 + static_cast<uint32_t>(p * kRowThreads * E) < static_cast<uint32_t>(V); };
+  auto word = [&](const u32x4_t& v, int p, int k) { return inrow(p) ? v[k] : kNegInf2; };
+  // The running maximum of a thread's logits, kept as two signed 16-bit keys
+  // that order bf16 values as floats do (a negative pattern's magnitude bits
+  // flipped, so that larger magnitudes rank lower; -0 ranks just below +0):
+  // three packed operations per two logits.  vec_max folds a vector into it.
+  auto vec_max = [&](uint32_t acc2, const u32x4_t& v, int p) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t w = word(v, p, k);
+      const uint32_t neg2 = pk_ashr15_i16(w);                    // 0xFFFF where negative
+      acc2 = pk_max_i16(acc2, w ^ (neg2 & 0x7FFF7FFFu));
+    }
+    return acc2;
+  };
+  // back to a float: the larger key of the two halves, then its pattern
+  auto key_to_float = [](uint32_t acc2) {
+    const int32_t a = static_cast<int16_t>(acc2 & 0xFFFFu), b = static_cast<int16_t>(acc2 >> 16);
+    const int32_t kmax = max(a, b);
+    const uint32_t u = static_cast<uint32_t>(kmax) & 0xFFFFu;
+    const uint32_t pat = (u & 0x8000u) ? (u ^ 0x7FFFu) : u;
+    return __uint_as_float(pat << 16);
+  };
+  constexpr uint32_t kKeyNegInf = 0x807F807Fu;   // the key of -inf (0xFF80), both halves
+  u32x4_t raw[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) raw[p] = vload(row, p);
+  // this thread's maximum over its logits of the row in raw: for the first
+  // row here, for the next ones during the previous row's weight pass
+  uint32_t vkey = kKeyNegInf;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    vkey = vec_max(vkey, raw[p], p);
+    __builtin_amdgcn_sched_barrier(0);   // one vector at a time: bounds live registers
+  }
+  // the weight pass takes the maximum of the next row's vector p - kLag: kLag
+  // vectors of weighing after its load was issued
+  constexpr int kLag = MAXP > 6 ? 6 : MAXP - 1;
+
+  for (; row < rows; row += gridDim.x) {
+    __asm__ volatile("" : "+v"(t8));
+    const int next = row + gridDim.x;
+    const bool has_next = next < rows;
+    const int lrow = has_next ? next : row;   // the row the weight pass loads
+    const bool valid = row % N < num_nodes[row / N];
+    const uint16_t* rp = logits + static_cast<long>(row) * V;
+    // ---- the row maximum (this thread's part: vkey), then the lowest index holding it
+    const float vmax = key_to_float(vkey);
+    const float bm = wave_max_f32_dpp(vmax);
+    if (lane == 0) s_f[wave] = bm;
+    __syncthreads();
+    float m = s_f[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, s_f[w]);
+    m = m + 0.0f;   // -0 -> +0
+    // bf16 patterns equal to m as floats: m's own pattern, or either zero when m is 0
+    uint32_t first = 0xFFFFFFFFu;
+    if (vmax == m) {
+      // patterns equal to m as floats, compared with the zero patterns folded
+      // together when m is 0; vectors are tested whole first
+      const uint32_t zm = m == 0.0f ? 0x7FFFu : 0xFFFFu;
+      const uint32_t mb = (__float_as_uint(m) >> 16) & zm;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) {
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t w = word(raw[p], p, k);
+          any |= (w & zm) == mb || ((w >> 16) & zm) == mb;
+        }
+        if (any && first == 0xFFFFFFFFu) {
+#pragma unroll
+          for (int k = E - 1; k >= 0; --k) {
+            const uint32_t u = (word(raw[p], p, k >> 1) >> (16 * (k & 1))) & zm;
+            first = u == mb ? t8 + static_cast<uint32_t>(p * kRowThreads * E + k) : first;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      key = wave_max_u64(key);
-      if (lane == 0) {
-        s_rowkey = key;
-        if (blockIdx.y == 0) {
-          argmax[row] = valid ? static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key)) : -1;
-          maxv[row] = valid ? unord_f32(static_cast<uint32_t>(key >> 32)) : -__builtin_huge_valf();
+    }
+    first = wave_min_u32_dpp(first);
+    if (lane == 0) s_i[wave] = first;
+    // ---- the weight table of this row (both halves; entry span of each is 0)
+    const float big = max(fabsf(m), fabsf(m - 32.0f / wc.c));
+    const int e_top = static_cast<int>((__float_as_uint(big) >> 23) & 0xFFu);
+    const int e_hi = min(e_top, 254), e_lo = max(e_top - kTabE + 1, 1);
+    const uint32_t hi = (static_cast<uint32_t>(e_hi) << 7) | 127u;
+    const uint32_t span = e_hi >= e_lo ? hi - (static_cast<uint32_t>(e_lo) << 7) + 1u : 0u;
+    for (int e = tid; e < kPipeTabEntries; e += kRowThreads) {
+      const uint32_t neg = e >= kPipeNegEntries ? 1u : 0u;
+      const uint32_t off = static_cast<uint32_t>(e) - neg * kPipeNegEntries;
+      // entry span of each half (every logit outside the window) holds a
+      // sentinel that counts such logits in bits 56 and up of the sums
+      uint64_t wv = off == span ? kOutside : 0ull;
+      if (off < span) {
+        const float l = __uint_as_float(((neg << 15) | (hi - off)) << 16);
+        // patterns above m occur in no row with this maximum
+        if (l <= m) wv = weight(l, m, wc);
+      }
+      s_tab[e] = wv;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
+    // ---- weights, per block of DDTREE_R_BLOCK tokens, loading the next row behind them
+    const uint32_t hi2 = hi | (hi << 16), span2 = span | (span << 16);
+    const uint32_t lo_mag = hi + 1u - span;   // magnitudes below this are below the window
+    const unsigned char* tab = reinterpret_cast<const unsigned char*>(s_tab);
+    constexpr int kBlocks = (MAXP + kQ - 1) / kQ;
+    uint64_t bsum[kBlocks];
+    uint32_t nkey = kKeyNegInf;   // the next row's maximum, as its vectors arrive
+    uint32_t missed = 0;   // bit b: a logit of block b lies outside the window
+#pragma unroll
+    for (int blk = 0; blk < kBlocks; ++blk) {
+      uint64_t acc = 0;
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        const int p = blk * kQ + q;
+        if (p < MAXP) {
+          // opaque to the optimiser: keeps it from holding unpacked copies of
+          // several vectors at once (the row already takes 4 * MAXP registers)
+          __asm__ volatile("" : "+v"(raw[p]));
+          // the vector's eight table addresses, then its eight lookups in flight
+          // together, then their sum
+          uint32_t a[E];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t w = word(raw[p], p, k);
+            const uint32_t mag2 = w & 0x7FFF7FFFu;
+            const uint32_t c2 = pk_min_u16(pk_sub_u16(hi2, mag2), span2);
+            const uint32_t addr2 = (c2 << 3) | (w & 0x80008000u);   // byte offsets, both halves
+            a[2 * k] = addr2 & 0xFFFFu;
+            a[2 * k + 1] = addr2 >> 16;
+          }
+          uint64_t t[E];
+#pragma unroll
+          for (int j = 0; j < E; ++j) t[j] = *reinterpret_cast<const uint64_t*>(tab + a[j]);
+          acc += ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+          // the sums stay per vector (reassociated across vectors they would
+          // keep every lookup of the block live at once)
+          __asm__ volatile("" : "+v"(acc));
+          // this vector is weighed: its registers take the next row's vector
+          raw[p] = vload(lrow, p);
+          if (p >= kLag) {
+            nkey = vec_max(nkey, raw[p - kLag], p - kLag);
+            // pinned here (the compiler would otherwise sink it to the next
+            // row's start, where the loads would be waited for with no work)
+            __asm__ volatile("" : "+v"(nkey));
+          }
+        }
+      }
+      missed |= acc >= kOutside ? 1u << blk : 0u;
+      bsum[blk] = acc & (kOutside - 1u);
+    }
+#pragma unroll
+    for (int p = MAXP - kLag; p < MAXP; ++p) nkey = vec_max(nkey, raw[p], p);
+    vkey = nkey;
+    // logits outside the window (rare): those below it weighed directly (those
+    // above it weigh 0), re-read from memory after the whole pass, so that no
+    // load of the stream waits for them
+    if (__builtin_amdgcn_ballot_w64(missed != 0)) {
+#pragma unroll
+      for (int blk = 0; blk < kBlocks; ++blk) {
+        if (missed & (1u << blk)) {
+#pragma unroll 1
+          for (int j = 0; j < kQ * E; ++j) {
+            const uint32_t i = t8 + static_cast<uint32_t>((blk * kQ + j / E) * kRowThreads * E + j % E);
+            if (i < static_cast<uint32_t>(V)) {
+              const uint32_t u = rp[i];
+              if ((u & 0x7FFFu) < lo_mag) bsum[blk] += weight(__uint_as_float(u << 16), m, wc);
+            }
+          }
         }
       }
     }
+#pragma unroll
+    for (int blk = 0; blk < kBlocks; ++blk) {
+      const uint64_t ws = wave_sum_u64_dpp(bsum[blk]);
+      if (lane == 0 && blk < nb) s_blk[blk][wave] = ws;
+    }
     __syncthreads();
-    m = unord_f32(static_cast<uint32_t>(s_rowkey >> 32));
-  } else {
-    m = maxv[row];
-  }
-  if (!valid) {   // R was cleared by the greedy pass
-    if (Rb)
-      for (int k = blk0 + tid; k < blk1; k += kRowThreads) Rb[static_cast<long>(row) * nb + k] = 0;
-    return;
-  }
-  const uint16_t* rp = logits + static_cast<long>(row) * V;
-  auto load_block = [&](int blk, u32x4_t (&dst)[kQ]) {
+    if (wave == 0) {
+      uint64_t bt = 0;
+      if (lane < nb) {
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const long i = (static_cast<long>(blk) * kQ + q) * kRowThreads * E + tid * E;
-      const uint32_t z = Vec<uint16_t>::kNegInfWord;
-      dst[q] = i < V ? *reinterpret_cast<const u32x4_t*>(rp + i) : u32x4_t{z, z, z, z};
-    }
-  };
-  u32x4_t cur[kQ], nxt[kQ];
-  load_block(blk0, cur);
-  const WeightTable tb = fill_weight_table(s_tab, m, wc, tid, kRowThreads);
-  __syncthreads();
-  for (int blk = blk0; blk < blk1; ++blk) {
-    if (blk + 1 < blk1) load_block(blk + 1, nxt);
-    uint64_t bsum = 0;
-    uint32_t miss = 0;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        bool in0, in1;
-        bsum += table_weight(s_tab, tb, cur[q][k] & 0xFFFFu, in0);
-        bsum += table_weight(s_tab, tb, cur[q][k] >> 16, in1);
-        miss |= (in0 ? 0u : 1u << (q * E + 2 * k)) | (in1 ? 0u : 1u << (q * E + 2 * k + 1));
+        for (int w = 0; w < kWaves; ++w) bt += s_blk[lane][w];
+        if (Rb) Rb[static_cast<long>(row) * nb + lane] = valid ? bt : 0ull;
       }
-    if (__builtin_amdgcn_ballot_w64(miss != 0)) {
-#pragma unroll 1
-      while (miss) {
-        const int j = __builtin_ctz(miss);
-        miss &= miss - 1u;
-        const long i = (static_cast<long>(blk) * kQ + j / E) * kRowThreads * E + tid * E + j % E;
-        // past the row end: the -inf padding, weight 0
-        if (i < V) bsum += weight(__uint_as_float(static_cast<uint32_t>(rp[i]) << 16), m, wc);
+      const uint64_t tot = wave_sum_u64_dpp(bt);
+      if (lane == 0) {
+        R[row] = valid ? tot : 0ull;
+        argmax[row] = valid ? static_cast<int32_t>(first) : -1;
+        maxv[row] = valid ? m : -__builtin_huge_valf();
       }
     }
-    const uint64_t ws = wave_sum_u64(bsum);
-    if (lane == 0) s_blk[blk - blk0][wave] = ws;
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) cur[q] = nxt[q];
   }
-  __syncthreads();
-  // block sums, then this workgroup's share of the row total, added into R
-  // (cleared by the greedy pass; integer sums, so the order is immaterial)
-  if (wave == 0) {
-    uint64_t bt = 0;
-    if (lane < blk1 - blk0) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) bt += s_blk[lane][w];
-      if (Rb) Rb[static_cast<long>(row) * nb + blk0 + lane] = bt;
-    }
-    const uint64_t tot = wave_sum_u64(bt);
-    if (lane == 0)
-      atomicAdd(reinterpret_cast<unsigned long long*>(R + row), static_cast<unsigned long long>(tot));
+}
+
+// Workgroups of the persistent sampling kernel: one per CU of the device
+// (looked up once per device).
+int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
   }
+  return v;
+}
+
+template <int MAXP>
+void launch_pipe(int rows, hipStream_t st, const void* logits, int N, int V, const int32_t* nn,
+                 const WeightConsts& wc, int32_t* am, float* mx, uint64_t* R, uint64_t* Rb) {
+  const int G = std::min(rows, device_cus());
+  if (V == MAXP * kRowThreads * 8)
+    hipLaunchKernelGGL((row_pipe_kernel<MAXP, true>), dim3(G), dim3(kRowThreads), 0, st,
+                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb);
+  else
+    hipLaunchKernelGGL((row_pipe_kernel<MAXP, false>), dim3(G), dim3(kRowThreads), 0, st,
+                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb);
+}
+
+// true when launched: bf16 rows of whole 16-byte vectors, up to 20 of them per
+// thread; rows that end inside a vector past the eighth (whose masking would
+// not fit the 128 registers) take the row-per-workgroup kernel instead
+bool launch_sampling_pipe(int rows, hipStream_t st, const void* logits, int N, int V,
+                          const int32_t* nn, const WeightConsts& wc, int32_t* am, float* mx,
+                          uint64_t* R, uint64_t* Rb) {
+  if (V % 8 != 0 || !aligned16(logits)) return false;
+  const int passes = (V + kRowThreads * 8 - 1) / (kRowThreads * 8);
+  if (passes > 8 && V % (kRowThreads * 8) != 0) return false;
+  if (passes <= 1) launch_pipe<1>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 2) launch_pipe<2>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 4) launch_pipe<4>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 8) launch_pipe<8>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 12) launch_pipe<12>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 16) launch_pipe<16>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else if (passes <= 20) launch_pipe<20>(rows, st, logits, N, V, nn, wc, am, mx, R, Rb);
+  else return false;
+  return true;
 }
 
 // Greedy merge and walk in one launch: one workgroup per request merges the
@@ -755,18 +986,18 @@ size_t greedy_ws_bytes(int rows, int S) {
 template <typename T>
 void launch_greedy(int rows, int N, int V, hipStream_t st, const void* logits, const int32_t* nn,
                    int S, int chunk, void* ws, int32_t* am, float* mx, float* lse,
-                   uint64_t* zero_R = nullptr, bool merge = true) {
+                   bool merge = true) {
   uint64_t* ws_key = static_cast<uint64_t*>(ws);
   float2* ws_ms = reinterpret_cast<float2*>(ws_key + static_cast<size_t>(rows) * S);
   const dim3 grid(S, rows);
   if (lse)
     hipLaunchKernelGGL((split_kernel<T, true>), grid, dim3(kSplitThreads), 0, st,
                        static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
-                       lse, zero_R);
+                       lse);
   else
     hipLaunchKernelGGL((split_kernel<T, false>), grid, dim3(kSplitThreads), 0, st,
                        static_cast<const T*>(logits), N, V, nn, S, chunk, ws_key, ws_ms, am, mx,
-                       lse, zero_R);
+                       lse);
   if (S > 1 && merge) {
     if (lse)
       hipLaunchKernelGGL((finalize_kernel<true>), dim3(rows), dim3(kWave), 0, st, N, nn, S, ws_key,
@@ -811,31 +1042,20 @@ extern "C" ddtree_status ddtree_vocab_reduce(const void* logits, ddtree_dtype dt
       return fail(DDTREE_EUNSUPPORTED, "ddtree_vocab_reduce: V = %d exceeds %d for sampling", V,
                   kMaxRowBlocks * DDTREE_R_BLOCK);
     const WeightConsts wc = weight_consts(temperature);
-    // bf16 rows without the log-sum-exp: the greedy pass (argmax, max) and a
-    // streaming weight pass, when the caller gave the greedy workspace
-    int S, chunk;
-    split_plan(rows, V, 2, &S, &chunk);
-    const bool streamed = dtype == DDTREE_BF16 && !lse && V % 8 == 0 && aligned16(logits) &&
-                          (S <= 1 || (workspace && workspace_bytes >= greedy_ws_bytes(rows, S) &&
-                                      aligned16(workspace)));
-    if (streamed) {
-      launch_greedy<uint16_t>(rows, N, V, stream, logits, num_nodes, S, chunk, workspace, argmax,
-                              maxv, nullptr, R, /*merge=*/false);
-      // two workgroups per row while the rows fill under two rounds of the
-      // chip's 512 slots (batched: 528 rows 87 -> 83 us); with many rounds the
-      // second table fill per row costs more than the balance gains (ragged:
-      // 2112 rows, 265 -> 282 us)
-      const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
-      const int halves = nb > 1 && rows < 1024 ? 2 : 1;
-      hipLaunchKernelGGL(wsum_kernel, dim3(rows, halves), dim3(kRowThreads), 0, stream,
-                         static_cast<const uint16_t*>(logits), N, V, num_nodes, wc, S,
-                         static_cast<const uint64_t*>(workspace), argmax, maxv, R, R_blocks);
-    } else if (dtype == DDTREE_BF16)
+    // bf16 rows without the log-sum-exp: one pass over HBM, rows pipelined
+    // through registers (row_pipe_kernel); otherwise a workgroup per row
+    const bool piped = dtype == DDTREE_BF16 && !lse &&
+                       launch_sampling_pipe(rows, stream, logits, N, V, num_nodes, wc, argmax,
+                                            maxv, R, R_blocks);
+    if (piped) {
+      // launched
+    } else if (dtype == DDTREE_BF16) {
       launch_sampling<uint16_t>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R,
                                 R_blocks, lse);
-    else
+    } else {
       launch_sampling<float>(rows, stream, logits, N, V, num_nodes, wc, argmax, maxv, R, R_blocks,
                              lse);
+    }
     return check_launch("ddtree_vocab_reduce");
   }
   int S, chunk;
@@ -885,11 +1105,11 @@ extern "C" ddtree_status ddtree_vocab_verify_greedy(const void* logits, ddtree_d
   if (dtype == DDTREE_BF16)
     hipLaunchKernelGGL((split_kernel<uint16_t, false>), grid, dim3(kSplitThreads), 0, stream,
                        static_cast<const uint16_t*>(logits), tree->N, V, tree->num_nodes, S, chunk,
-                       ws_key, ws_ms, argmax, maxv, nullptr, nullptr);
+                       ws_key, ws_ms, argmax, maxv, nullptr);
   else
     hipLaunchKernelGGL((split_kernel<float, false>), grid, dim3(kSplitThreads), 0, stream,
                        static_cast<const float*>(logits), tree->N, V, tree->num_nodes, S, chunk,
-                       ws_key, ws_ms, argmax, maxv, nullptr, nullptr);
+                       ws_key, ws_ms, argmax, maxv, nullptr);
   if (S == 1)   // the split pass wrote argmax and max itself: the plain walk follows
     return ddtree_verify_greedy(tree, argmax, accept_len, path_nodes, out_tokens, bonus, stream);
   hipLaunchKernelGGL(merge_walk_kernel, dim3(tree->B), dim3(kMergeWalkThreads), 0, stream, *tree,
