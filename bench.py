@@ -303,6 +303,7 @@ def run_gpu(cfg, args, rotate):
     # kernel durations
     r["attn_ms"], r["attn_reps"] = w.call_ms(w.attention)
     r["vocab_ms"], r["vocab_reps"] = w.call_ms(w.vocab)
+    r["decode_loop"] = run_decode_loop(w, max(100, args.steps))
     if not args.no_extras:
         extra_steps = max(args.steps, 100)
         if T == 0:
@@ -326,6 +327,87 @@ def run_gpu(cfg, args, rotate):
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return r
+
+
+def run_decode_loop(w, steps):
+    """A decode loop over growing per-request cache slabs: each step builds the
+    tree from the previous step's bonus token and prefix length, runs the tree
+    attention over the slabs with ddtree_tree_attention_ranges (its split plan
+    made anew on the host from the grown lengths), the vocabulary pass and the
+    walk, then ddtree_commit appends the accepted path's K/V and gives the next
+    (prefix length, root).  The accept lengths come back to the host each step
+    (a copy into pinned memory and a stream synchronisation) to update the
+    host's copy of the lengths, as a serving loop does.  Eager launches: the
+    plan changes every step.  Inputs rotate over the workload's sets."""
+    torch, lib, cfg = w.torch, w.lib, w.cfg
+    dev, B, D, T = w.dev, cfg.B, cfg.D, cfg.temperature
+    lens = np.diff(w.inp["ctx_offsets"]).astype(np.int64)
+    cap = int(lens.max()) + steps * (D + 1) + 1
+    base = np.arange(B, dtype=np.int64) * cap
+    s0 = w.sets[0]
+    kslab = torch.empty((B * cap, cfg.Hkv, cfg.Dh), dtype=s0["k_ctx"].dtype, device=dev)
+    vslab = torch.empty_like(kslab)
+    offs = w.inp["ctx_offsets"]
+    for b in range(B):
+        kslab[base[b]:base[b] + lens[b]] = s0["k_ctx"][offs[b]:offs[b + 1]]
+        vslab[base[b]:base[b] + lens[b]] = s0["v_ctx"][offs[b]:offs[b + 1]]
+    start_h = base.astype(np.int32)
+    start_d = torch.from_numpy(start_h).to(dev)
+    base_d = torch.from_numpy(base).to(dev)
+    prefix_h = lens.astype(np.int32)
+    prefix_d = [torch.from_numpy(prefix_h.copy()).to(dev), torch.empty((B,), dtype=torch.int32,
+                                                                     device=dev)]
+    root_d = [w.small["root_tok"].clone(), torch.empty((B,), dtype=torch.int32, device=dev)]
+    walk = {"accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+            "path_nodes": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+            "bonus": torch.empty((B,), dtype=torch.int32, device=dev)}
+    acc_h = torch.empty((B,), dtype=torch.int32, pin_memory=True)
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    regrown = 0
+    sm = w.small
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tokens = 0
+    for i in range(steps):
+        s = w.sets[i % w.rotate]
+        cur, nxt = i % 2, 1 - i % 2
+        need = lib.ddtree_tree_attention_ranges_workspace_size(B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh,
+                                                               prefix_h)
+        if need > ws.numel():
+            ws = torch.empty(2 * need, dtype=torch.uint8, device=dev)
+            regrown += 1
+        lib.ddtree_build(sm["draft_lp"], sm["draft_tok"], root_d[cur], prefix_d[cur], cfg.budget,
+                         tree=w.tree)
+        lib.ddtree_tree_attention_ranges(s["q"], kslab, vslab, start_d, prefix_d[cur], start_h,
+                                         prefix_h, s["k_tree"], s["v_tree"], w.tree,
+                                         out=w.attn_out, workspace=ws)
+        v = w.vocab(s)
+        if T > 0:
+            lib.ddtree_verify_sample(w.tree, s["logits"], v["maxv"], v["R"], v["R_blocks"], T,
+                                     sm["uniforms"], outputs=walk)
+        else:
+            lib.ddtree_verify_greedy(w.tree, v["argmax"], outputs=walk)
+        lib.ddtree_commit(w.tree, walk, s["k_tree"], s["v_tree"], kslab, vslab, base_d, cap,
+                          next_prefix_len=prefix_d[nxt], next_root=root_d[nxt])
+        acc_h.copy_(walk["accept_len"], non_blocking=True)
+        w.stream.synchronize()
+        a = acc_h.numpy()
+        prefix_h = (prefix_h + a + 1).astype(np.int32)
+        tokens += int(a.sum()) + B
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    consistent = bool(np.array_equal(prefix_d[steps % 2].cpu().numpy(), prefix_h))
+    del kslab, vslab
+    return {"steps": steps, "steps_per_s": round(steps / dt, 2),
+            "ms_per_step": round(1e3 * dt / steps, 4),
+            "tokens_per_s": round(tokens / dt, 1),
+            "accept_len_mean": round((tokens - steps * B) / (steps * B), 4),
+            "ctx_growth": [int(lens.sum()), int(prefix_h.astype(np.int64).sum())],
+            "workspace_regrown": regrown, "host_lengths_match_device": consistent,
+            "step": "build (previous bonus and prefix), ddtree_tree_attention_ranges over the "
+                    "slabs (plan made anew), vocabulary pass, walk, ddtree_commit, accept "
+                    "lengths to the host, synchronise; eager launches"}
 
 
 def run_commit(w):
@@ -644,6 +726,7 @@ def config_record(cfg, r, args, rotate):
                           ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma_util": round(flops / (r["attn_ms"] * 1e-3) / mfma_peak, 4),
         "accept_len_mean": r["accept_len_mean"],
+        "decode_loop": r["decode_loop"],
     }
     if "fused" in r:
         m = statistics.median(r["fused"])

@@ -92,7 +92,7 @@ def assert_tree_equal(got: dict, ref: dict):
 
 
 def assert_attention_close(o_gpu, o_ref, dtype, mask=None):
-    """spec tolerance: max-abs 2e-2 (bf16) / 1e-4 (fp32), also relative to max|o_ref|."""
+    """The attention tolerance: max-abs 2e-2 (bf16) / 1e-4 (fp32), also relative to max|o_ref|."""
     tol = 2e-2 if dtype == "bf16" else 1e-4
     sel = ~np.isnan(o_ref) if mask is None else mask
     err = np.abs(o_gpu[sel] - o_ref[sel]).max()
