@@ -65,7 +65,11 @@ typedef enum {
   DDTREE_EDEVICE = 3       /* a HIP launch or runtime call failed */
 } ddtree_status;
 
-typedef enum { DDTREE_F32 = 0, DDTREE_BF16 = 1 } ddtree_dtype;
+/* Element type codes.  The type is a plain 32-bit integer, not an enum, so
+ * that any value a caller passes is well defined on both sides of the ABI;
+ * values other than these two are rejected with DDTREE_EINVAL. */
+typedef int32_t ddtree_dtype;
+enum { DDTREE_F32 = 0, DDTREE_BF16 = 1 };
 
 /* Size limits (validated). */
 #define DDTREE_MAX_NODES 128  /* N = budget + 1 */

@@ -6,7 +6,8 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libddtree.so")
+# DDTREE_LIBRARY: another build of the same library (the host-sanitizer build)
+library_path = os.environ.get("DDTREE_LIBRARY") or os.path.join(_HERE, "libddtree.so")
 
 if not os.path.exists(library_path):
     raise ImportError(f"{library_path} is missing: build it first (__graft_entry__.build() or "
