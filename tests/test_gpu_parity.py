@@ -168,11 +168,13 @@ def _awkward_bf16_rows(V, seed):
     return workloads.f32_to_bf16_bits(x)
 
 
+@pytest.mark.parametrize("V", [40960 + 8 * 7, 163840])
 @pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 25.0])
-def test_vocab_sampling_awkward_rows(T):
-    """R and its block sums on rows built to miss the weight table (bit-exact)."""
+def test_vocab_sampling_awkward_rows(T, V):
+    """R and its block sums on rows built to miss the weight table (bit-exact):
+    a row length that ends inside a thread's vectors, and the full vocabulary
+    (every thread's 20 vectors whole)."""
     import tree_verification_build_amd as lib
-    V = 40960 + 8 * 7
     bits = _awkward_bf16_rows(V, 51)
     nn = np.array([bits.shape[1]], dtype=np.int32)
     say("vocab awkward rows", "T", T, "V", V)

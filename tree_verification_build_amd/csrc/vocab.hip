@@ -527,18 +527,27 @@ __global__ __launch_bounds__(kRowThreads) void row2_kernel(
 // and in [span, 0x7FFF] below it; min(off, span) is the entry within its
 // sign's half of the table (entry span of each half is 0), and the sign bit
 // of the pattern, kept in place, adds the negative half's 32768-byte offset.
-// Logits outside the window read a sentinel (2^56) that the sums count in
-// their top bits; below-window ones (tiny magnitudes) are then weighed with
-// weight() itself after the pass, above-window ones weigh 0, so every weight
-// is weight()'s own value.
+// Each half of the table: entry 0 is the weight 0 of magnitudes above the
+// window (a negative logit below m - 32/c: weight() is 0 there), entries 1 ..
+// span the window's patterns from the top down, entry span + 1 a sentinel
+// (2^56) that the sums count in their top bits for magnitudes below the
+// window; those rare logits are weighed with weight() itself after the pass,
+// so every weight is weight()'s own value.  The window spans kPipeTabE
+// binades (wider than the other kernels' kTabE: below-window logits cost a
+// re-read, above-window ones nothing).
+constexpr int kPipeTabE = 26;
+constexpr int kPipeSpan = kPipeTabE * 128;
 constexpr int kPipeNegEntries = 4096;                         // negative half: byte 32768
-constexpr uint64_t kOutside = 1ull << 56;   // sentinel of the outside entries
-constexpr int kPipeTabEntries = kPipeNegEntries + kTabSpan + 1;
+constexpr uint64_t kOutside = 1ull << 56;   // sentinel of the below-window entries
+constexpr int kPipeTabEntries = kPipeNegEntries + kPipeSpan + 2;
+static_assert(kPipeSpan + 2 <= kPipeNegEntries, "each half fits its 32 KB");
 
 typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t pk_sub_u16(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
+// a - b per 16-bit half, saturating at 0
+__device__ __forceinline__ uint32_t pk_sub_sat_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, a),
+                                                                    __builtin_bit_cast(u16x2_t, b)));
 }
 typedef int16_t i16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
@@ -551,6 +560,13 @@ __device__ __forceinline__ uint32_t pk_ashr15_i16(uint32_t a) {
 __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2_t, a),
                                                                 __builtin_bit_cast(u16x2_t, b)));
+}
+
+// (x & 0xFFFF) * 8 in one operation (the compiler emits a shift and a mask)
+__device__ __forceinline__ uint32_t mul_lo16_by8(uint32_t x) {
+  uint32_t r;
+  asm("v_mad_u32_u16 %0, %1, 8, 0" : "=v"(r) : "v"(x));
+  return r;
 }
 
 // Wave reductions by DPP row moves and lane reads: no shuffle-index
@@ -618,34 +634,39 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
   };
   auto inrow = [&](int p) { return WHOLE || t8 + static_cast<uint32_t>(p * kRowThreads * E) < static_cast<uint32_t>(V); };
   auto word = [&](const u32x4_t& v, int p, int k) { return inrow(p) ? v[k] : kNegInf2; };
-  // The running maximum of a thread's logits, kept as two signed 16-bit keys
-  // that order bf16 values as floats do (a negative pattern's magnitude bits
-  // flipped, so that larger magnitudes rank lower; -0 ranks just below +0):
-  // three packed operations per two logits.  vec_max folds a vector into it.
-  auto vec_max = [&](uint32_t acc2, const u32x4_t& v, int p) {
+  // The running maximum of a thread's logits as two packed pairs of 16-bit
+  // patterns, one packed operation each per two logits: .x the largest pattern
+  // as a signed 16-bit value (the largest positive logit, or +0: patterns of
+  // positive bf16 values order as their values do, and negative patterns are
+  // negative), .y the smallest as an unsigned one (the negative logit nearest
+  // zero, when no pattern is positive).  vec_max folds a vector into it.
+  struct MaxAcc {
+    uint32_t pos, neg;
+  };
+  auto vec_max = [&](MaxAcc acc, const u32x4_t& v, int p) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t w = word(v, p, k);
-      const uint32_t neg2 = pk_ashr15_i16(w);                    // 0xFFFF where negative
-      acc2 = pk_max_i16(acc2, w ^ (neg2 & 0x7FFF7FFFu));
+      acc.pos = pk_max_i16(acc.pos, w);
+      acc.neg = pk_min_u16(acc.neg, w);
     }
-    return acc2;
+    return acc;
   };
-  // back to a float: the larger key of the two halves, then its pattern
-  auto key_to_float = [](uint32_t acc2) {
-    const int32_t a = static_cast<int16_t>(acc2 & 0xFFFFu), b = static_cast<int16_t>(acc2 >> 16);
-    const int32_t kmax = max(a, b);
-    const uint32_t u = static_cast<uint32_t>(kmax) & 0xFFFFu;
-    const uint32_t pat = (u & 0x8000u) ? (u ^ 0x7FFFu) : u;
+  // back to a float: a positive pattern (or +0) if any, else the negative one
+  auto key_to_float = [](MaxAcc acc) {
+    const int32_t a = static_cast<int16_t>(acc.pos & 0xFFFFu), b = static_cast<int16_t>(acc.pos >> 16);
+    const int32_t pmax = max(a, b);
+    const uint32_t nmin = min(acc.neg & 0xFFFFu, acc.neg >> 16);
+    const uint32_t pat = pmax >= 0 ? static_cast<uint32_t>(pmax) : nmin;
     return __uint_as_float(pat << 16);
   };
-  constexpr uint32_t kKeyNegInf = 0x807F807Fu;   // the key of -inf (0xFF80), both halves
+  constexpr MaxAcc kKeyNegInf = {0x80008000u, 0xFFFFFFFFu};   // no logit yet
   u32x4_t raw[MAXP];
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) raw[p] = vload(row, p);
   // this thread's maximum over its logits of the row in raw: for the first
   // row here, for the next ones during the previous row's weight pass
-  uint32_t vkey = kKeyNegInf;
+  MaxAcc vkey = kKeyNegInf;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     vkey = vec_max(vkey, raw[p], p);
@@ -701,32 +722,30 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
     // ---- the weight table of this row (both halves; entry span of each is 0)
     const float big = max(fabsf(m), fabsf(m - 32.0f / wc.c));
     const int e_top = static_cast<int>((__float_as_uint(big) >> 23) & 0xFFu);
-    const int e_hi = min(e_top, 254), e_lo = max(e_top - kTabE + 1, 1);
+    const int e_hi = min(e_top, 254), e_lo = max(e_top - kPipeTabE + 1, 1);
     const uint32_t hi = (static_cast<uint32_t>(e_hi) << 7) | 127u;
     const uint32_t span = e_hi >= e_lo ? hi - (static_cast<uint32_t>(e_lo) << 7) + 1u : 0u;
-    for (int e = tid; e < kPipeTabEntries; e += kRowThreads) {
-      const uint32_t neg = e >= kPipeNegEntries ? 1u : 0u;
-      const uint32_t off = static_cast<uint32_t>(e) - neg * kPipeNegEntries;
-      // entry span of each half (every logit outside the window) holds a
-      // sentinel that counts such logits in bits 56 and up of the sums
-      uint64_t wv = off == span ? kOutside : 0ull;
-      if (off < span) {
-        const float l = __uint_as_float(((neg << 15) | (hi - off)) << 16);
-        // patterns above m occur in no row with this maximum
-        if (l <= m) wv = weight(l, m, wc);
+    for (int t = tid; t < 2 * (kPipeSpan + 2); t += kRowThreads) {
+      const uint32_t neg = t >= kPipeSpan + 2 ? 1u : 0u;
+      const uint32_t off = static_cast<uint32_t>(t) - neg * (kPipeSpan + 2);
+      uint64_t wv = off == span + 1u ? kOutside : 0ull;
+      if (off >= 1u && off <= span) {
+        const float l = __uint_as_float(((neg << 15) | (hi + 1u - off)) << 16);
+        // patterns above m occur in no row with this maximum; those whose
+        // exponent y falls below -32 weigh 0 (weight()'s own cut-off, computed
+        // the same way), skipped by whole waves as the window runs in order
+        if (l <= m && (l - m) * wc.c >= -32.0f) wv = weight(l, m, wc);
       }
-      s_tab[e] = wv;
+      s_tab[neg * kPipeNegEntries + off] = wv;
     }
     __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
     // ---- weights, per block of DDTREE_R_BLOCK tokens, loading the next row behind them
-    const uint32_t hi2 = hi | (hi << 16), span2 = span | (span << 16);
+    const uint32_t top2 = (hi + 1u) * 0x10001u, end2 = (span + 1u) * 0x10001u;
     const uint32_t lo_mag = hi + 1u - span;   // magnitudes below this are below the window
     const unsigned char* tab = reinterpret_cast<const unsigned char*>(s_tab);
     constexpr int kBlocks = (MAXP + kQ - 1) / kQ;
     uint64_t bsum[kBlocks];
-    uint32_t nkey = kKeyNegInf;   // the next row's maximum, as its vectors arrive
+    MaxAcc nkey = kKeyNegInf;   // the next row's maximum, as its vectors arrive
     uint32_t missed = 0;   // bit b: a logit of block b lies outside the window
 #pragma unroll
     for (int blk = 0; blk < kBlocks; ++blk) {
@@ -739,16 +758,19 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
           // several vectors at once (the row already takes 4 * MAXP registers)
           __asm__ volatile("" : "+v"(raw[p]));
           // the vector's eight table addresses, then its eight lookups in flight
-          // together, then their sum
+          // together, then their sum.  Entry index per half: the window entry c
+          // (< 4096) plus 4096 for a negative pattern (its sign bit moved to bit
+          // 12); byte address = index * 8, taken from each half by one shift
+          // (the low half's index is below 2^13, so the high half's index
+          // shifted right by 13 has nothing of it in its low three bits).
           uint32_t a[E];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const uint32_t w = word(raw[p], p, k);
-            const uint32_t mag2 = w & 0x7FFF7FFFu;
-            const uint32_t c2 = pk_min_u16(pk_sub_u16(hi2, mag2), span2);
-            const uint32_t addr2 = (c2 << 3) | (w & 0x80008000u);   // byte offsets, both halves
-            a[2 * k] = addr2 & 0xFFFFu;
-            a[2 * k + 1] = addr2 >> 16;
+            const uint32_t c2 = pk_min_u16(pk_sub_sat_u16(top2, w & 0x7FFF7FFFu), end2);
+            const uint32_t i2 = ((w >> 3) & 0x10001000u) | c2;
+            a[2 * k] = mul_lo16_by8(i2);
+            a[2 * k + 1] = i2 >> 13;
           }
           uint64_t t[E];
 #pragma unroll
@@ -763,7 +785,7 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
             nkey = vec_max(nkey, raw[p - kLag], p - kLag);
             // pinned here (the compiler would otherwise sink it to the next
             // row's start, where the loads would be waited for with no work)
-            __asm__ volatile("" : "+v"(nkey));
+            __asm__ volatile("" : "+v"(nkey.pos), "+v"(nkey.neg));
           }
         }
       }
@@ -773,19 +795,26 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
 #pragma unroll
     for (int p = MAXP - kLag; p < MAXP; ++p) nkey = vec_max(nkey, raw[p], p);
     vkey = nkey;
-    // logits outside the window (rare): those below it weighed directly (those
-    // above it weigh 0), re-read from memory after the whole pass, so that no
-    // load of the stream waits for them
+    // logits below the window (rare): weighed with weight() after the whole
+    // pass, from their block's vectors re-read from memory (so that no load of
+    // the stream waits for them), one vector at a time
     if (__builtin_amdgcn_ballot_w64(missed != 0)) {
 #pragma unroll
       for (int blk = 0; blk < kBlocks; ++blk) {
         if (missed & (1u << blk)) {
 #pragma unroll 1
-          for (int j = 0; j < kQ * E; ++j) {
-            const uint32_t i = t8 + static_cast<uint32_t>((blk * kQ + j / E) * kRowThreads * E + j % E);
-            if (i < static_cast<uint32_t>(V)) {
-              const uint32_t u = rp[i];
-              if ((u & 0x7FFFu) < lo_mag) bsum[blk] += weight(__uint_as_float(u << 16), m, wc);
+          for (int q = 0; q < kQ; ++q) {
+            const int p = blk * kQ + q;
+            if (p < MAXP) {
+              const u32x4_t v = vload(row, p);
+              uint64_t fix = 0;
+#pragma unroll
+              for (int k = 0; k < E; ++k) {
+                const uint32_t u = (word(v, p, k >> 1) >> (16 * (k & 1))) & 0xFFFFu;
+                const uint64_t wk = weight(__uint_as_float(u << 16), m, wc);
+                fix += (u & 0x7FFFu) < lo_mag ? wk : 0ull;
+              }
+              bsum[blk] += fix;
             }
           }
         }
@@ -805,6 +834,10 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
         if (Rb) Rb[static_cast<long>(row) * nb + lane] = valid ? bt : 0ull;
       }
       const uint64_t tot = wave_sum_u64_dpp(bt);
+      // the lowest index holding the maximum over the waves (read here, not
+      // before the weight pass, where the values would stay live through it)
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) first = min(first, s_i[w]);
       if (lane == 0) {
         R[row] = valid ? tot : 0ull;
         argmax[row] = valid ? static_cast<int32_t>(first) : -1;
