@@ -621,16 +621,17 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
   // logits: a load under a condition becomes a load into other registers
   // plus a copy, and the copy waits for the load.  Vector p of a row past its
   // end (WHOLE false) re-reads the row's last vector and is masked to -inf
-  // where it is used; with no next row, the loads re-read vector 0 of this
-  // row (cached, and never used).
+  // where it is used; with no next row, every thread loads the logits' first
+  // 16 bytes (one cached line, never used) instead of a row.
   // t8: this thread's first token of each vector, redefined opaquely every row
   // so that the compiler computes each vector's offset where it loads it
   // instead of keeping MAXP offsets live across the row loop
   uint32_t t8 = tid * E;
-  auto vload = [&](int r, int p) -> u32x4_t {
+  auto vload = [&](int r, int p, bool real = true) -> u32x4_t {
     uint32_t i = t8 + static_cast<uint32_t>(p * kRowThreads * E);
     if (!WHOLE) i = min(i, static_cast<uint32_t>(V - E));
-    return *reinterpret_cast<const u32x4_t*>(logits + static_cast<long>(r) * V + i);
+    const long off = real ? static_cast<long>(r) * V + i : 0l;
+    return *reinterpret_cast<const u32x4_t*>(logits + off);
   };
   auto inrow = [&](int p) { return WHOLE || t8 + static_cast<uint32_t>(p * kRowThreads * E) < static_cast<uint32_t>(V); };
   auto word = [&](const u32x4_t& v, int p, int k) { return inrow(p) ? v[k] : kNegInf2; };
@@ -680,7 +681,6 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
     __asm__ volatile("" : "+v"(t8));
     const int next = row + gridDim.x;
     const bool has_next = next < rows;
-    const int lrow = has_next ? next : row;   // the row the weight pass loads
     const bool valid = row % N < num_nodes[row / N];
     const uint16_t* rp = logits + static_cast<long>(row) * V;
     // ---- the row maximum (this thread's part: vkey), then the lowest index holding it
@@ -780,7 +780,7 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
           // keep every lookup of the block live at once)
           __asm__ volatile("" : "+v"(acc));
           // this vector is weighed: its registers take the next row's vector
-          raw[p] = vload(lrow, p);
+          raw[p] = vload(next, p, has_next);
           if (p >= kLag) {
             nkey = vec_max(nkey, raw[p - kLag], p - kLag);
             // pinned here (the compiler would otherwise sink it to the next
