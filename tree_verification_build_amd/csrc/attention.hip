@@ -882,14 +882,18 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   for (int sp0 = wave; sp0 < ns; sp0 += 4 * kCombU) {
     float2 ml[kCombU];
     float v[kCombU][PER];
+    // unconditional loads (of the last split where there is none, then
+    // masked): a load under a condition is waited for on its own, so the
+    // conditional form took one round trip per split
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
-      const int sp = sp0 + 4 * u;
-      if (sp < ns) {
-        const long pr = prow(sp);
-        ml[u] = a.ws_ml[pr];
-        load_partial<PT, PER>(ws + pr * DH + lane * PER, v[u]);
-      } else {
+      const long pr = prow(min(sp0 + 4 * u, ns - 1));
+      ml[u] = a.ws_ml[pr];
+      load_partial<PT, PER>(ws + pr * DH + lane * PER, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCombU; ++u) {
+      if (sp0 + 4 * u >= ns) {
         ml[u] = make_float2(kNegBig, 0.f);
 #pragma unroll
         for (int k = 0; k < PER; ++k) v[u][k] = 0.f;
