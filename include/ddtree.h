@@ -96,6 +96,8 @@ typedef struct {
   uint64_t* vis;         /* [B, N, W] bit j of row i: node i sees node j (ancestors and itself) */
   int32_t* num_nodes;    /* [B] 1 + number of nodes taken (<= N) */
   int32_t B, N, D, K, W; /* W = (N + 63) / 64 */
+  int32_t* max_depth;    /* [B] depth of the deepest node taken (0 if only the root), or
+                            NULL: written by ddtree_build when set, read by nothing else */
 } ddtree_tree;
 
 /*
@@ -141,6 +143,11 @@ ddtree_status ddtree_draft_topk(const void* logits, ddtree_dtype dtype, int32_t 
  *              tree->N must equal budget + 1 and tree->B/D/K/W match.
  * Order: larger cumulative score first (score(child) = fp32(score(parent) +
  * draft_lp), one rounded add), ties by smaller parent index then smaller rank.
+ * tree->max_depth, when not NULL, receives each request's deepest depth: the
+ * statistic that tells whether the budget went to breadth before the tree
+ * reached the drafter's last depth ("The Tree That Couldn't Branch",
+ * "Hypothesis 1: Best-First Search Exhaustion"; read beside node counts and
+ * accepted depths in "The Experiment: budget=7, topk_cap=1").
  * Errors: DDTREE_EINVAL for null pointers or out-of-range sizes.
  */
 ddtree_status ddtree_build(const float* draft_lp, const int32_t* draft_tok,

@@ -33,8 +33,10 @@ def build_tree(draft_lp, draft_tok, root_tok, prefix_len, budget: int) -> dict:
     """draft_lp f32 [B, D, K], draft_tok i32 [B, D, K], root_tok [B], prefix_len [B].
 
     Returns [B, N] arrays (N = budget + 1): token, parent, depth, rank, position,
-    first_child, next_sibling (i32), score (f32), vis (u64 [B, N, W]) and
-    num_nodes (i32 [B]).  Entries past num_nodes[b] hold -1 (score -inf, vis 0)."""
+    first_child, next_sibling (i32), score (f32), vis (u64 [B, N, W]),
+    num_nodes (i32 [B]) and max_depth (i32 [B], the depth of the deepest node
+    taken: the statistic of "Hypothesis 1: Best-First Search Exhaustion").
+    Entries past num_nodes[b] hold -1 (score -inf, vis 0)."""
     lp = np.asarray(draft_lp, dtype=np.float32)
     tok = np.asarray(draft_tok, dtype=np.int32)
     B, D, K = lp.shape
@@ -46,6 +48,7 @@ def build_tree(draft_lp, draft_tok, root_tok, prefix_len, budget: int) -> dict:
     out["score"] = np.full((B, N), -np.inf, dtype=np.float32)
     out["vis"] = np.zeros((B, N, W), dtype=np.uint64)
     out["num_nodes"] = np.zeros(B, dtype=np.int32)
+    out["max_depth"] = np.zeros(B, dtype=np.int32)
 
     for b in range(B):
         score = out["score"][b]
@@ -72,6 +75,7 @@ def build_tree(draft_lp, draft_tok, root_tok, prefix_len, budget: int) -> dict:
             out["token"][b, i] = tok[b, depth - 1, rank]
             out["parent"][b, i] = parent
             out["depth"][b, i] = depth
+            out["max_depth"][b] = max(out["max_depth"][b], depth)
             out["rank"][b, i] = rank
             out["position"][b, i] = prefix_len[b] + depth
             score[i] = np.float32(-negs)

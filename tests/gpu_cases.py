@@ -81,7 +81,7 @@ class Case:
 
 def assert_tree_equal(got: dict, ref: dict):
     for k in ("token", "parent", "depth", "rank", "position", "first_child", "next_sibling",
-              "num_nodes"):
+              "num_nodes", "max_depth"):
         if not np.array_equal(got[k], ref[k]):
             bad = np.argwhere(got[k] != ref[k])[:4]
             raise AssertionError(f"{k}: first mismatches at {bad.tolist()}: got "

@@ -125,6 +125,7 @@ def test_chain_topk1_is_greedy_chain():
         t = build_tree(lp, tok, np.array([42]), np.array([100]), budget)
         n = int(t["num_nodes"][0])
         assert n == 1 + min(budget, D)
+        assert int(t["max_depth"][0]) == min(budget, D)
         assert list(t["parent"][0, :n]) == [-1] + list(range(n - 1))
         assert list(t["token"][0, 1:n]) == list(tok[0, : n - 1, 0])
         for i in range(n):
@@ -145,7 +146,7 @@ def test_greedy_chain_depth_equals_tree_depth(seed):
             while c != -1:
                 chain += 1
                 c = int(t["first_child"][b, c])
-            assert chain == int(t["depth"][b, :n].max())
+            assert chain == int(t["depth"][b, :n].max()) == int(t["max_depth"][b])
 
 
 def test_hand_example_distinct_scores():
@@ -165,6 +166,7 @@ def test_hand_example_distinct_scores():
     assert list(t["first_child"][0]) == [1, 2, -1, 4, -1]
     assert list(t["next_sibling"][0]) == [-1, 3, -1, -1, -1]
     assert list(t["position"][0]) == [3, 4, 5, 4, 5]
+    assert int(t["max_depth"][0]) == 2
     assert [int(v) for v in t["vis"][0, :, 0]] == [0b1, 0b11, 0b111, 0b1001, 0b11001]
 
 
@@ -207,3 +209,16 @@ def test_hand_example_minus_inf_logprobs():
     assert list(t["token"][0]) == [9, 1, 3, 2, 4, 3, 4]
     assert list(t["score"][0][:3]) == [0.0, -1.0, -1.5]
     assert np.all(np.isneginf(t["score"][0][3:]))
+
+
+def test_flat_logprobs_exhaust_budget_at_depth_one():
+    # "Hypothesis 1: Best-First Search Exhaustion": with every log-prob equal
+    # (-1) a depth-d node scores exactly -d, so best-first takes all K^d nodes
+    # of depth d before any of depth d + 1: max_depth is 1 for budget <= K,
+    # 2 for K < budget <= K + K^2, 3 just past that.
+    D, K = 8, 4
+    lp = np.full((2, D, K), -1.0, dtype=np.float32)
+    tok = np.tile(np.arange(K, dtype=np.int32), (2, D, 1))
+    for budget, want in ((1, 1), (K, 1), (K + 1, 2), (K + K * K, 2), (K + K * K + 1, 3)):
+        t = build_tree(lp, tok, np.zeros(2, np.int32), np.zeros(2, np.int32), budget)
+        assert list(t["max_depth"]) == [want, want], budget

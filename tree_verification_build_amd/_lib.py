@@ -30,7 +30,8 @@ class _CTree(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("token", "parent", "depth", "rank", "position",
                                                "first_child", "next_sibling", "score", "vis",
                                                "num_nodes")] + \
-               [(n, ctypes.c_int32) for n in ("B", "N", "D", "K", "W")]
+               [(n, ctypes.c_int32) for n in ("B", "N", "D", "K", "W")] + \
+               [("max_depth", ctypes.c_void_p)]
 
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -141,7 +142,8 @@ def _dtype_code(t):
 
 
 class Tree:
-    """Device arrays of a token tree ([B, N] each; vis [B, N, W]; num_nodes [B])."""
+    """Device arrays of a token tree ([B, N] each; vis [B, N, W]; num_nodes and
+    max_depth [B])."""
 
     FIELDS = ("token", "parent", "depth", "rank", "position", "first_child", "next_sibling")
 
@@ -152,9 +154,10 @@ class Tree:
         self.score = torch.empty((B, N), dtype=torch.float32, device=device)
         self.vis = torch.empty((B, N, self.W), dtype=torch.int64, device=device)
         self.num_nodes = torch.empty((B,), dtype=torch.int32, device=device)
+        self.max_depth = torch.empty((B,), dtype=torch.int32, device=device)
         self._c = _CTree(*[t.data_ptr() for t in (*[getattr(self, f) for f in self.FIELDS],
                                                    self.score, self.vis, self.num_nodes)],
-                         B, N, D, K, self.W)
+                         B, N, D, K, self.W, self.max_depth.data_ptr())
 
     @property
     def cstruct(self):
@@ -165,6 +168,7 @@ class Tree:
         out["score"] = self.score.cpu().numpy()
         out["vis"] = self.vis.cpu().numpy().view(np.uint64)
         out["num_nodes"] = self.num_nodes.cpu().numpy()
+        out["max_depth"] = self.max_depth.cpu().numpy()
         return out
 
 

@@ -331,6 +331,12 @@ __global__ __launch_bounds__(64) void build_kernel(const float* __restrict__ dra
     }
   }
   if (lane == 0) t.num_nodes[b] = count;
+  if (t.max_depth) {
+    int m = max(dep[0], dep[1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if (lane == 0) t.max_depth[b] = m;
+  }
 }
 
 }  // namespace
