@@ -26,7 +26,8 @@ kernel rooflines and CPU baseline.  Timing protocol per workload: --warmup
 untimed steps, then --reps repetitions of exactly --steps synchronised steps
 (value = median rate); a sustained figure times repetitions of at least
 max(--steps, 200) steps and 1 s each; kernel durations come from HIP events
-around graphs of back-to-back calls on the calls' stream.  The CPU baseline is
+around graphs of back-to-back calls on the calls' stream (--eager: the same
+calls launched from Python, no graph anywhere).  The CPU baseline is
 the oracle on a bounded sample of the same workload, timed single-threaded on
 one core and on all cores of the process's affinity set.
 """
@@ -100,7 +101,7 @@ def summary(rates):
 class Workload:
     """Device inputs, buffers and the step functions of one workload."""
 
-    def __init__(self, cfg, rotate, result_copy=False):
+    def __init__(self, cfg, rotate, result_copy=False, eager=False):
         import torch
         import tree_verification_build_amd as lib
         import workloads
@@ -136,6 +137,7 @@ class Workload:
         # itself (the device-to-host transfer is its stores); with result_copy they stay
         # on the device and one copy per step brings them over
         self.result_copy = result_copy
+        self.eager = eager
         if result_copy:
             self.result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
             self.host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
@@ -240,6 +242,15 @@ class Workload:
         torch.cuda.synchronize()
         return lambda i: gs[i % self.rotate].replay()
 
+    def replayable(self, fn):
+        """fn captured into a HIP graph, returned as its replay (eager: fn itself)."""
+        if self.eager:
+            return fn
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            fn()
+        return g.replay
+
     def loop_rates(self, run, steps, reps, sync_each=True):
         """`reps` repetitions of exactly `steps` steps; steps/s of each."""
         torch, stream = self.torch, self.stream
@@ -263,14 +274,16 @@ class Workload:
 
     def call_ms(self, fn, min_calls=200, reps=5):
         """Average duration of one call: a graph of back-to-back calls over the
-        rotated input sets, replayed between two HIP events on this stream;
-        median over repetitions of at least min_calls calls."""
+        rotated input sets, replayed between two HIP events on this stream
+        (eager: the same calls launched from Python); median over repetitions
+        of at least min_calls calls."""
         torch, stream = self.torch, self.stream
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+
+        def calls():
             for i in range(self.rotate):
                 fn(self.sets[i])
-        g.replay()
+        once = self.replayable(calls)
+        once()
         torch.cuda.synchronize()
         per = max(1, -(-min_calls // self.rotate))
         out = []
@@ -278,7 +291,7 @@ class Workload:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(per):
-                g.replay()
+                once()
             e1.record(stream)
             torch.cuda.synchronize()
             out.append(e0.elapsed_time(e1) / (per * self.rotate))
@@ -288,7 +301,7 @@ class Workload:
 def run_gpu(cfg, args, rotate):
     """Every GPU figure of one workload."""
     import torch
-    w = Workload(cfg, rotate, result_copy=args.result_copy)
+    w = Workload(cfg, rotate, result_copy=args.result_copy, eager=args.eager)
     T = cfg.temperature
     main_step = w.step_fused if T == 0 else w.step
     for i in range(args.warmup):
@@ -302,6 +315,9 @@ def run_gpu(cfg, args, rotate):
     # the contract's loop: --reps repetitions of exactly --steps synchronised steps
     r["rates"] = w.loop_rates(run, args.steps, args.reps)
     r["accept_len_mean"] = float(w.host_result[0].float().mean())
+    r["tree_stats"] = {"num_nodes_mean": float(w.tree.num_nodes.float().mean()),
+                       "max_depth_mean": float(w.tree.max_depth.float().mean()),
+                       "max_depth_min": int(w.tree.max_depth.min())}
     r["sustained_steps"], r["sustained"] = w.sustained(run, max(args.steps, 200),
                                                        args.min_seconds, args.reps)
     # the same steps without the per-step synchronisation
@@ -450,17 +466,17 @@ def run_topk(w):
         cfg.B * cfg.D, cfg.V, cfg.K)), dtype=torch.uint8, device=dev)
     tk_tok = torch.empty((cfg.B, cfg.D, cfg.K), dtype=torch.int32, device=dev)
     tk_lp = torch.empty((cfg.B, cfg.D, cfg.K), dtype=torch.float32, device=dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    def calls():
         for x in dsets:
             lib.ddtree_draft_topk(x, cfg.K, tokens=tk_tok, logprobs=tk_lp, workspace=tk_ws)
-    g.replay()
+    once = w.replayable(calls)
+    once()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     treps = max(1, 200 // ncopy)
     e0.record(w.stream)
     for _ in range(treps):
-        g.replay()
+        once()
     e1.record(w.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (treps * ncopy)
@@ -503,15 +519,13 @@ def run_linear(w, reps=50):
                                         outputs=out)
     call()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        call()
-    g.replay()
+    once = w.replayable(call)
+    once()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(w.stream)
     for _ in range(reps):
-        g.replay()
+        once()
     e1.record(w.stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -733,6 +747,7 @@ def config_record(cfg, r, args, rotate):
                           ((r["attn_ms"] + r["vocab_ms"]) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "mfma_util": round(flops / (r["attn_ms"] * 1e-3) / mfma_peak, 4),
         "accept_len_mean": r["accept_len_mean"],
+        "tree_stats": r["tree_stats"],
         "decode_loop": r["decode_loop"],
     }
     rec["step"] = ("build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
