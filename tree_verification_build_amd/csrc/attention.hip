@@ -810,11 +810,15 @@ __global__ __launch_bounds__(NW * 64) void attn_dma_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ combine
-// One workgroup per (request, KV head, query row). Wave w takes splits
-// w, w + 4, w + 8, ...; it issues the loads of up to kCombU of them at once
-// (every lane reads the split's (max, sum) pair and Dh/64 output dims), so a
-// request with up to 4·kCombU splits costs one round trip to memory. The
-// four waves' (max, sum, acc) meet in LDS.
+// WPR waves per (request, KV head, query row), 4 / WPR rows per workgroup.
+// The waves of a row take its splits w, w + WPR, w + 2·WPR, ...; each issues
+// the loads of up to kCombU of them at once (every lane reads the split's
+// (max, sum) pair and Dh/64 output dims), so a row with up to WPR·kCombU
+// splits costs one round trip to memory.  With WPR = 1 a wave merges its row
+// alone; otherwise the row's waves meet in LDS.  The host takes the smallest
+// WPR whose round covers the most splits of any request: few splits (large
+// batches) get one wave per row, so the grid does not carry four mostly idle
+// waves per row.
 constexpr int kCombU = 8;
 
 template <typename PT, int PER>
@@ -830,14 +834,15 @@ __device__ __forceinline__ void load_partial(const PT* src, float (&v)[PER]) {
   }
 }
 
-template <typename elem, typename PT, int DH>
+template <typename elem, typename PT, int DH, int WPR>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   constexpr int PER = DH / 64;                // output dims per lane
+  constexpr int RPW = 4 / WPR;                // rows per workgroup
   __shared__ float s_m[4], s_l[4];
-  __shared__ float s_acc[4][DH];
+  __shared__ float s_acc[WPR > 1 ? 4 : 1][DH];
   const int b = blockIdx.x / a.Hkv, kvh = blockIdx.x % a.Hkv;
-  const int r = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = blockIdx.y * RPW + wave / WPR, sub = wave % WPR;
   int start, ns;
   if (a.tab_n > 0) {
     start = a.tab_split0[b];
@@ -859,19 +864,22 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     if (start >= a.total_splits) return;
     ns = min(ns, a.total_splits - start);
   }
-  if (ns <= 1) return;
+  if (ns <= 1) return;                        // the same for the whole workgroup
+  // a row past M (the last workgroup's spare waves) or a padding node does no
+  // merge, but its waves still reach the barrier below
+  bool live = r < a.M;
   const int node = r / a.G, head = kvh * a.G + r % a.G;
   const long orow = (static_cast<long>(b) * a.N + node) * a.Hq + head;
   elem* dst = static_cast<elem*>(a.out) + orow * DH;
-  if (node >= a.num_nodes[b]) {
-    if (wave == 0) {
+  if (live && node >= a.num_nodes[b]) {
+    if (sub == 0) {
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         if constexpr (sizeof(elem) == 2) dst[lane * PER + k] = 0; else dst[lane * PER + k] = 0.f;
       }
       if (a.lse && lane == 0) a.lse[orow] = -__builtin_huge_valf();
     }
-    return;
+    live = false;
   }
   const long pr0 = static_cast<long>(start) * a.Hkv + kvh;
   auto prow = [&](int sp) { return (pr0 + static_cast<long>(sp) * a.Hkv) * a.M + r; };
@@ -879,7 +887,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   float mw = kNegBig, lw = 0.f, acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.f;
-  for (int sp0 = wave; sp0 < ns; sp0 += 4 * kCombU) {
+  for (int sp0 = sub; live && sp0 < ns; sp0 += WPR * kCombU) {
     float2 ml[kCombU];
     float v[kCombU][PER];
     // unconditional loads (of the last split where there is none, then
@@ -887,13 +895,13 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     // conditional form took one round trip per split
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
-      const long pr = prow(min(sp0 + 4 * u, ns - 1));
+      const long pr = prow(min(sp0 + WPR * u, ns - 1));
       ml[u] = a.ws_ml[pr];
       load_partial<PT, PER>(ws + pr * DH + lane * PER, v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kCombU; ++u) {
-      if (sp0 + 4 * u >= ns) {
+      if (sp0 + WPR * u >= ns) {
         ml[u] = make_float2(kNegBig, 0.f);
 #pragma unroll
         for (int k = 0; k < PER; ++k) v[u][k] = 0.f;
@@ -915,30 +923,46 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
     }
     mw = mc;
   }
-  if (lane == 0) {
-    s_m[wave] = mw;
-    s_l[wave] = lw;
-  }
+  if constexpr (WPR == 1) {
+    if (!live) return;
+    const float inv = lw > 0.f ? 1.0f / lw : 0.f;
 #pragma unroll
-  for (int k = 0; k < PER; ++k) s_acc[wave][lane * PER + k] = acc[k];
-  __syncthreads();
-  if (wave != 0) return;
-  const float mstar = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
-  float f[4], lsum = 0.f;
+    for (int k = 0; k < PER; ++k) {
+      const float o = acc[k] * inv;
+      if constexpr (sizeof(elem) == 2) dst[lane * PER + k] = f32_to_bf16_rne(o);
+      else dst[lane * PER + k] = o;
+    }
+    if (a.lse && lane == 0) a.lse[orow] = (mw + __log2f(lw)) * kLn2;
+  } else {
+    if (lane == 0) {
+      s_m[wave] = mw;
+      s_l[wave] = lw;
+    }
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    f[w] = __builtin_amdgcn_exp2f(s_m[w] - mstar);
-    lsum += f[w] * s_l[w];
-  }
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    for (int k = 0; k < PER; ++k) s_acc[wave][lane * PER + k] = acc[k];
+    __syncthreads();
+    if (!live || sub != 0) return;
+    float mstar = s_m[wave];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int d = lane * PER + k;
-    const float o = (f[0] * s_acc[0][d] + f[1] * s_acc[1][d] + f[2] * s_acc[2][d] +
-                     f[3] * s_acc[3][d]) * inv;
-    if constexpr (sizeof(elem) == 2) dst[d] = f32_to_bf16_rne(o); else dst[d] = o;
+    for (int w = 1; w < WPR; ++w) mstar = max(mstar, s_m[wave + w]);
+    float f[WPR], lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) {
+      f[w] = __builtin_amdgcn_exp2f(s_m[wave + w] - mstar);
+      lsum += f[w] * s_l[wave + w];
+    }
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int d = lane * PER + k;
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) o += f[w] * s_acc[wave + w][d];
+      o *= inv;
+      if constexpr (sizeof(elem) == 2) dst[d] = f32_to_bf16_rne(o); else dst[d] = o;
+    }
+    if (a.lse && lane == 0) a.lse[orow] = (mstar + __log2f(lsum)) * kLn2;
   }
-  if (a.lse && lane == 0) a.lse[orow] = (mstar + __log2f(lsum)) * kLn2;
 }
 
 // ------------------------------------------------------------------ host side
@@ -1071,6 +1095,20 @@ ddtree_status attention_impl_args_error(const char* who, int Hq, int Hkv, int Dh
   return fail(DDTREE_EINVAL, "%s: Hq=%d must be a multiple of Hkv=%d", who, Hq, Hkv);
 }
 
+template <int WPR>
+void launch_combine(const AttnArgs& a, ddtree_dtype dtype, int Dh, hipStream_t stream) {
+  constexpr int RPW = 4 / WPR;
+  const dim3 g(a.B * a.Hkv, (a.M + RPW - 1) / RPW);
+  if (dtype == DDTREE_BF16) {
+    if (Dh == 128)
+      hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t, 128, WPR>), g, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<uint16_t, float, 64, WPR>), g, dim3(256), 0, stream, a);
+  } else {
+    if (Dh == 128) hipLaunchKernelGGL((combine_kernel<float, float, 128, WPR>), g, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((combine_kernel<float, float, 64, WPR>), g, dim3(256), 0, stream, a);
+  }
+}
+
 // Shared body of the packed-offset and range forms.  hr: host copy of the
 // context ranges (validated by the caller); a.ctx_offsets or a.ctx_start /
 // ctx_len already set to the device arrays.
@@ -1160,15 +1198,15 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
     else launch_qb<PolicyF32<64>>(qb, a, splits, stream);
   }
   if (multi) {
-    const dim3 g(B * Hkv, M);
-    if (dtype == DDTREE_BF16) {
-      if (Dh == 128)
-        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t, 128>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((combine_kernel<uint16_t, float, 64>), g, dim3(256), 0, stream, a);
-    } else {
-      if (Dh == 128) hipLaunchKernelGGL((combine_kernel<float, float, 128>), g, dim3(256), 0, stream, a);
-      else hipLaunchKernelGGL((combine_kernel<float, float, 64>), g, dim3(256), 0, stream, a);
+    int max_ns = 1;
+    for (int b = 0; b < B; ++b) {
+      const long L = hr.len_of(b);
+      max_ns = std::max<long>(max_ns, L > 0 ? (L + sk - 1) / sk : 1);
     }
+    const int wpr = max_ns <= kCombU ? 1 : max_ns <= 2 * kCombU ? 2 : 4;
+    if (wpr == 1) launch_combine<1>(a, dtype, Dh, stream);
+    else if (wpr == 2) launch_combine<2>(a, dtype, Dh, stream);
+    else launch_combine<4>(a, dtype, Dh, stream);
   }
   return check_launch(who);
 }
