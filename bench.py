@@ -1,15 +1,18 @@
 """Benchmark: DDTree tree-verify steps/s on one MI355X, every workload.
 
 One step = ddtree_build -> ddtree_tree_attention -> the vocabulary reduction
-and the walk, then accept_len and bonus reaching the host and a stream
-synchronisation (the serving loop's per-step sync).  Greedy workloads reduce
+and the walk, then accept_len and bonus reaching the host, which waits for
+them before the next step (the serving loop's per-step wait).  Greedy workloads reduce
 and walk with ddtree_vocab_verify_greedy (one launch; the same argmax, max and
 walk outputs as ddtree_vocab_reduce + ddtree_verify_greedy, whose step is
 reported beside it as "separate_calls_step"); sampling workloads call
 ddtree_vocab_reduce, then ddtree_verify_sample.  The walk kernel stores the two results straight
-into pinned host memory and the host busy-polls for the synchronisation
-(--result-copy adds an explicit device-to-host copy instead, --host-wait auto
-sleeps until signalled).  Each step is a captured HIP graph replayed once per
+into pinned host memory, accept_len last after a system-scope release, and
+the host waits by polling accept_len there (filled with -1 before the step);
+--step-wait sync synchronises the stream instead (reported beside the polled
+rate as "stream_sync_step"), --result-copy adds an explicit device-to-host copy
+and a synchronisation, --host-wait auto lets stream synchronisations sleep
+until signalled.  Each step is a captured HIP graph replayed once per
 step (--eager launches every call from Python).  Inputs are seeded synthetic
 tensors of the workload's shapes, resident in HBM before timing starts; several
 copies of the input set are rotated so that consecutive steps do not find their
@@ -23,7 +26,7 @@ Default run (--config all): the single-request workload gives the headline
 line's fields (value, roofline, cpu_baseline); every workload (tiny, single,
 batched, long, ragged) also gets an entry in "configs" with its steps/s,
 kernel rooflines and CPU baseline.  Timing protocol per workload: --warmup
-untimed steps, then --reps repetitions of exactly --steps synchronised steps
+untimed steps, then --reps repetitions of exactly --steps waited-for steps
 (value = median rate); a sustained figure times repetitions of at least
 max(--steps, 200) steps and 1 s each; kernel durations come from HIP events
 around graphs of back-to-back calls on the calls' stream (--eager: the same
@@ -101,7 +104,7 @@ def summary(rates):
 class Workload:
     """Device inputs, buffers and the step functions of one workload."""
 
-    def __init__(self, cfg, rotate, result_copy=False, eager=False):
+    def __init__(self, cfg, rotate, result_copy=False, eager=False, step_wait="sync"):
         import torch
         import tree_verification_build_amd as lib
         import workloads
@@ -138,6 +141,8 @@ class Workload:
         # on the device and one copy per step brings them over
         self.result_copy = result_copy
         self.eager = eager
+        # polling needs the walk's own stores in pinned memory
+        self.step_wait = "sync" if result_copy else step_wait
         if result_copy:
             self.result = torch.empty((2, cfg.B), dtype=torch.int32, device=dev)
             self.host_result = torch.empty((2, cfg.B), dtype=torch.int32, pin_memory=True)
@@ -251,17 +256,31 @@ class Workload:
             fn()
         return g.replay
 
-    def loop_rates(self, run, steps, reps, sync_each=True):
-        """`reps` repetitions of exactly `steps` steps; steps/s of each."""
+    def loop_rates(self, run, steps, reps, wait=None):
+        """`reps` repetitions of exactly `steps` steps; steps/s of each.  After
+        each step the host waits for its results: "poll" spins on accept_len in
+        pinned memory (filled with -1 before the step; the walk stores it last,
+        after the other results and a system-scope release), "sync"
+        synchronises the stream, "none" does not wait (pipelined steps)."""
         torch, stream = self.torch, self.stream
+        wait = wait or self.step_wait
+        acc = self.host_result[0].numpy() if wait == "poll" else None
         rates = []
         for _ in range(reps):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for i in range(steps):
-                run(i)
-                if sync_each:
-                    stream.synchronize()
+                if wait == "poll":
+                    acc.fill(-1)
+                    run(i)
+                    t1 = time.perf_counter()
+                    while (acc < 0).any():
+                        if time.perf_counter() - t1 > 5.0:
+                            raise RuntimeError(f"step {i}: no accept lengths after 5 s")
+                else:
+                    run(i)
+                    if wait == "sync":
+                        stream.synchronize()
             torch.cuda.synchronize()
             rates.append(steps / (time.perf_counter() - t0))
         return rates
@@ -301,7 +320,8 @@ class Workload:
 def run_gpu(cfg, args, rotate):
     """Every GPU figure of one workload."""
     import torch
-    w = Workload(cfg, rotate, result_copy=args.result_copy, eager=args.eager)
+    w = Workload(cfg, rotate, result_copy=args.result_copy, eager=args.eager,
+                 step_wait=args.step_wait)
     T = cfg.temperature
     main_step = w.step_fused if T == 0 else w.step
     for i in range(args.warmup):
@@ -312,8 +332,13 @@ def run_gpu(cfg, args, rotate):
         run(i)
         w.stream.synchronize()
     r = {"total_ctx": w.total_ctx}
-    # the contract's loop: --reps repetitions of exactly --steps synchronised steps
+    # the contract's loop: --reps repetitions of exactly --steps steps, the host
+    # waiting for each step's accept lengths before the next
     r["rates"] = w.loop_rates(run, args.steps, args.reps)
+    r["step_wait"] = w.step_wait
+    if w.step_wait != "sync":
+        # the same steps, each followed by a stream synchronisation instead
+        r["sync_rates"] = w.loop_rates(run, args.steps, args.reps, wait="sync")
     r["accept_len_mean"] = float(w.host_result[0].float().mean())
     r["tree_stats"] = {"num_nodes_mean": float(w.tree.num_nodes.float().mean()),
                        "max_depth_mean": float(w.tree.max_depth.float().mean()),
@@ -321,7 +346,7 @@ def run_gpu(cfg, args, rotate):
     r["sustained_steps"], r["sustained"] = w.sustained(run, max(args.steps, 200),
                                                        args.min_seconds, args.reps)
     # the same steps without the per-step synchronisation
-    r["pipelined"] = w.loop_rates(run, r["sustained_steps"], 3, sync_each=False)
+    r["pipelined"] = w.loop_rates(run, r["sustained_steps"], 3, wait="none")
     # kernel durations
     r["attn_ms"], r["attn_reps"] = w.call_ms(w.attention)
     r["vocab_ms"], r["vocab_reps"] = w.call_ms(w.vocab)
@@ -713,6 +738,13 @@ def run_cpu_baseline(cfg, seconds, inp=None):
 
 # ---------------------------------------------------------------------------- records
 
+STEP_WAIT_TEXT = {
+    "poll": "host polls accept_len in pinned memory (the walk stores it last, after a "
+            "system-scope release)",
+    "sync": "stream synchronisation",
+}
+
+
 def config_record(cfg, r, args, rotate):
     ab = algorithmic_bytes(cfg, r["total_ctx"])
     med = statistics.median(r["rates"])
@@ -728,6 +760,7 @@ def config_record(cfg, r, args, rotate):
         "reps": summary(r["rates"]),
         "sustained": dict(summary(r["sustained"]), steps_per_rep=r["sustained_steps"]),
         "pipelined_steps_per_s": round(statistics.median(r["pipelined"]), 2),
+        "step_wait": STEP_WAIT_TEXT[r.get("step_wait", "sync")],
         "ctx_tokens": r["total_ctx"],
         "input_sets_rotated": rotate,
         "attention": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -753,6 +786,12 @@ def config_record(cfg, r, args, rotate):
     rec["step"] = ("build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
                    "greedy walk in one launch)" if cfg.temperature == 0 else
                    "build, attention, ddtree_vocab_reduce, ddtree_verify_sample")
+    if "sync_rates" in r:
+        m = statistics.median(r["sync_rates"])
+        rec["stream_sync_step"] = {"steps_per_s": round(m, 2), "ms_per_step": round(1e3 / m, 4),
+                                   "reps": summary(r["sync_rates"]),
+                                   "step": "the same steps, each followed by a stream "
+                                           "synchronisation instead of the poll"}
     if "separate" in r:
         m = statistics.median(r["separate"])
         rec["separate_calls_step"] = {
@@ -804,6 +843,9 @@ def main():
     ap.add_argument("--host-wait", choices=("spin", "auto"), default="spin",
                     help="how the host waits for each step: busy-poll (spin) or the runtime's "
                          "default sleep-until-signalled (auto)")
+    ap.add_argument("--step-wait", choices=("poll", "sync"), default="poll",
+                    help="how the host waits for each step's results: poll accept_len in "
+                         "pinned memory (default) or synchronise the stream")
     ap.add_argument("--result-copy", action="store_true",
                     help="keep accept_len/bonus in device memory and copy them to the host "
                          "each step (default: the walk writes them to pinned host memory)")
@@ -858,9 +900,10 @@ def main():
                    "vocab": hcfg.V, "temperature": hcfg.temperature,
                    "input_sets_rotated": h["input_sets_rotated"],
                    "launch": "eager" if args.eager else "hip_graph", "host_wait": host_wait,
+                   "step_wait": h["step_wait"],
                    "result_to_host": "copy" if args.result_copy else "pinned_store",
                    "value_is": f"median steps/s over {args.reps} repetitions of {args.steps} "
-                               "synchronised steps"},
+                               "steps, each waited for on the host (step_wait)"},
         "roofline": dict(h["attention"], kernel="ddtree_tree_attention"),
         "reps": h["reps"],
         "sustained": h["sustained"],

@@ -46,6 +46,16 @@
  *     lengths (the *_host arrays) hold the same values as the device arrays.
  *   - Tensors are dense, row-major, with 16-byte aligned base pointers.
  *   - Calls are thread-safe (no shared state); calls on one stream are ordered.
+ *   - Walk results without a stream synchronisation: every walk
+ *     (ddtree_verify_greedy, ddtree_vocab_verify_greedy, ddtree_verify_sample,
+ *     ddtree_verify_sample_lazy, ddtree_verify_sample_top_p,
+ *     ddtree_verify_linear_sample) stores accept_len[b] last, after request b's
+ *     other outputs and a system-scope release.  A host that places accept_len
+ *     (and the other outputs it wants to read) in mapped pinned host memory,
+ *     fills accept_len with a negative value before enqueuing the step, and
+ *     polls it may read request b's bonus, out_tokens and path_nodes as soon
+ *     as accept_len[b] >= 0, without waiting for the kernels to end.  Later
+ *     work on the stream still runs after the walk has ended.
  */
 #ifndef DDTREE_H
 #define DDTREE_H

@@ -207,6 +207,12 @@ __device__ __forceinline__ WalkNodes walk_load(const ddtree_tree& t, int b, int 
   return w;
 }
 
+// A release fence at system scope: the calling wave's earlier stores (and
+// those its workgroup made before a barrier) are visible to the host before
+// any of its later stores.  Release only: unlike __threadfence_system() it
+// does not also invalidate the L2.
+__device__ __forceinline__ void release_system() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, ""); }
+
 // s_am: the argmax of every node of the request (-1 for padding nodes), in
 // LDS; w: walk_load() with the nodes >= num_nodes[b] already set to -2.
 __device__ __forceinline__ void walk_run(const ddtree_tree& t, int b, const int32_t* s_am,
@@ -240,9 +246,12 @@ __device__ __forceinline__ void walk_run(const ddtree_tree& t, int b, const int3
   if (lane == 0) {
     path[0] = 0;
     outt[a] = bon;
-    accept_len[b] = a;
     bonus[b] = bon;
   }
+  // accept_len last, after a system-scope release: a host that polls it in
+  // mapped host memory finds the request's other outputs written
+  release_system();
+  if (lane == 0) accept_len[b] = a;
 }
 
 // ---------------------------------------------------------------- element access

@@ -198,7 +198,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
       s_a = a;
       s_blk = blk;
       s_trem = tdraw - ((static_cast<uint64_t>(exh) << 32) | exl);
-      accept_len[b] = a;
     }
     for (int k = a + 1 + lane; k <= D; k += kWave) {
       path[k] = -1;
@@ -279,6 +278,16 @@ __global__ __launch_bounds__(kSampleThreads) void sample_kernel(
       outt[s_a] = pick;
       bonus[b] = pick;
     }
+    // this wave's stores complete and visible before the barrier below (a
+    // workgroup barrier alone does not wait for another wave's stores)
+    release_system();
+  }
+  // accept_len last, after every wave's outputs and a system-scope release:
+  // a host that polls it in mapped host memory finds the other outputs written
+  __syncthreads();
+  if (tid == 0) {
+    release_system();
+    accept_len[b] = s_a;
   }
 }
 
@@ -540,7 +549,6 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
       path[0] = 0;
       s_blk = blk;
       s_trem = tdraw - ((static_cast<uint64_t>(exh) << 32) | exl);
-      accept_len[b] = a;
     }
     for (int k = a + 1 + lane; k <= D; k += kWave) {
       path[k] = -1;
@@ -588,6 +596,13 @@ __global__ __launch_bounds__(kSampleThreads) void sample_lazy_kernel(
       outt[a] = pick;
       bonus[b] = pick;
     }
+    release_system();   // as in sample_kernel
+  }
+  // accept_len last (as in sample_kernel)
+  __syncthreads();
+  if (tid == 0) {
+    release_system();
+    accept_len[b] = a;
   }
 }
 
@@ -872,10 +887,12 @@ __global__ __launch_bounds__(kSampleThreads) void linear_sample_kernel(
     __syncthreads();
   }
   if (tid == 0) {
-    accept_len[b] = k;
     outt[k] = s_pick;
     bonus[b] = s_pick;
     for (int j = k + 1; j <= D; ++j) outt[j] = -1;
+    // accept_len last, after a system-scope release (as in the tree walks)
+    release_system();
+    accept_len[b] = k;
   }
 }
 
