@@ -14,7 +14,8 @@
  *   ddtree_tree_attention  every tree node attends to its request's context
  *                          (streamed from HBM once, shared by all nodes) and
  *                          to its own ancestors (ddtree_tree_attention_ranges:
- *                          the same with per-request context row ranges)
+ *                          the same with per-request context row ranges;
+ *                          ..._ranges_capped: lengths read on the device)
  *   ddtree_vocab_reduce    per-node argmax / max / log-sum-exp and, for
  *                          sampling, the exact integer softmax total R
  *   ddtree_verify_greedy   greedy verified-tree walk -> accept length, bonus
@@ -305,6 +306,37 @@ ddtree_status ddtree_tree_attention_ranges(const void* q, const void* k_ctx, con
                                            ddtree_dtype dtype, float scale, void* out,
                                            float* lse, void* workspace, size_t workspace_bytes,
                                            hipStream_t stream);
+
+/*
+ * ddtree_tree_attention_ranges_capped -- ddtree_tree_attention_ranges with the
+ * context lengths read from device memory when the kernels run: the host
+ * gives only an upper bound per request, so one call captured in a HIP graph
+ * stays valid while the caches grow (a decode loop replays the captured step
+ * while ddtree_commit advances ctx_len on the device).
+ * Source: as ddtree_tree_attention_ranges ("Dissecting DDTree's Tree-Parallel
+ * Evaluation Strategy", Section 2: the cache grows by the committed tokens).
+ *   ctx_start      [B] int32 device, as in ddtree_tree_attention_ranges
+ *   ctx_len        [B] int32 device: the lengths, read when the kernels run;
+ *                  a length above its bound is read as the bound, a negative
+ *                  one as 0
+ *   ctx_start_host [B] the starts in host memory
+ *   ctx_cap_host   [B] host upper bounds of the lengths: they fix the work split,
+ *                  the grid and the workspace (the splits past a request's
+ *                  current length stay idle)
+ *   workspace      ddtree_tree_attention_ranges_workspace_size(..., ctx_cap_host)
+ *                  bytes
+ * Every other argument and the outputs are those of ddtree_tree_attention_ranges;
+ * results equal that call's with ctx_len_host = ctx_cap_host's split size, i.e.
+ * within the attention tolerance of the exact-length call.
+ * Errors: as ddtree_tree_attention_ranges, with the bounds checked as the
+ *         lengths are there; DDTREE_EUNSUPPORTED for B > 64.
+ */
+ddtree_status ddtree_tree_attention_ranges_capped(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_start,
+    const int32_t* ctx_len, const int32_t* ctx_start_host, const int32_t* ctx_cap_host,
+    const void* k_tree, const void* v_tree, const ddtree_tree* tree, int32_t Hq, int32_t Hkv,
+    int32_t Dh, ddtree_dtype dtype, float scale, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ddtree_vocab_reduce -- one pass over the target logits of every tree node.

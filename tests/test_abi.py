@@ -164,6 +164,19 @@ def test_host_validation_rejects_bad_arguments():
                                             1, 0.125, fake, None, None, 0, None) == 1
     assert lib.ddtree_tree_attention_ranges(*rg, st1, ln1, fake, fake, ctypes.byref(t), 4, 4, 96,
                                             1, 0.125, fake, None, None, 0, None) == 2
+    # capped range form: the same checks on the bounds, and at most 64 requests
+    cap = lib.ddtree_tree_attention_ranges_capped
+    assert cap(*rg, st1, lnbad, fake, fake, ctypes.byref(t), 4, 4, 64, 1, 0.125, fake, None,
+               None, 0, None) == 1
+    assert cap(*rg, st1, None, fake, fake, ctypes.byref(t), 4, 4, 64, 1, 0.125, fake, None,
+               None, 0, None) == 1
+    assert cap(*rg, st1, ln1, fake, fake, ctypes.byref(t), 4, 4, 96, 1, 0.125, fake, None,
+               None, 0, None) == 2
+    t65 = _fake_tree(65, 33, 8, 4, 1)
+    st65, ln65 = (ctypes.c_int32 * 65)(*range(0, 65 * 64, 64)), (ctypes.c_int32 * 65)(*[64] * 65)
+    assert cap(*rg, st65, ln65, fake, fake, ctypes.byref(t65), 4, 4, 64, 1, 0.125, fake, None,
+               fake, 1 << 30, None) == 2
+    assert b"requests" in lib.ddtree_last_error()
     # attention
     offs = (ctypes.c_int32 * 2)(0, 64)
     args = [fake, fake, fake, fake, offs, fake, fake, ctypes.byref(t)]

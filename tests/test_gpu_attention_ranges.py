@@ -192,3 +192,112 @@ def test_device_lengths_disagreeing_with_host_copy(direction):
     torch.cuda.synchronize()
     ref, _ = c.oracle_attention()
     assert_attention_close(attn_to_f64(out), ref, "bf16")
+
+
+def _slabs(c, caps, seed):
+    """Request b's context at the start of a slab of caps[b] rows (the rest NaN)."""
+    i, cfg = c.inp, c.cfg
+    lens = i["ctx_lens"].astype(np.int64)
+    rng = np.random.default_rng(seed)
+    gaps = rng.integers(0, 40, size=cfg.B)
+    start = np.zeros(cfg.B, np.int64)
+    row = 3
+    for b in range(cfg.B):
+        row += int(gaps[b])
+        start[b] = row
+        row += int(caps[b])
+    kc = _nan_rows(row + 5, cfg.Hkv, cfg.Dh, cfg.dtype)
+    vc = _nan_rows(row + 5, cfg.Hkv, cfg.Dh, cfg.dtype)
+    offs = i["ctx_offsets"]
+    for b in range(cfg.B):
+        kc[start[b]:start[b] + lens[b]] = i["k_ctx"][offs[b]:offs[b + 1]]
+        vc[start[b]:start[b] + lens[b]] = i["v_ctx"][offs[b]:offs[b + 1]]
+    return kc, vc, start.astype(np.int32)
+
+
+def _oracle_over(c, kc, vc, start, lens, tree):
+    cfg = c.cfg
+    pk = np.concatenate([kc[start[b]:start[b] + lens[b]] for b in range(cfg.B)])
+    pv = np.concatenate([vc[start[b]:start[b] + lens[b]] for b in range(cfg.B)])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    o, _ = oracle.tree_attention(c.inp["q"], pk, pv, offs, c.inp["k_tree"], c.inp["v_tree"],
+                                 tree["vis"], tree["num_nodes"], dtype=cfg.dtype)
+    return o
+
+
+CAPPED = ["ranges_b3_bf16", "ranges_b20_bf16", "ranges_b5_dh64", "ranges_b18_f32"]
+
+
+@pytest.mark.parametrize("name", CAPPED)
+def test_capped_ranges(name):
+    """Bounds above the lengths: the oracle's output over the device lengths;
+    bounds equal to the lengths: bit for bit the exact-length range form."""
+    import tree_verification_build_amd as lib
+    c = _case(name)
+    cfg = c.cfg
+    lens = c.inp["ctx_lens"].astype(np.int32)
+    rng = np.random.default_rng(31)
+    caps = (lens + rng.integers(0, 700, size=cfg.B)).astype(np.int32)
+    say("attention ranges capped", name, "caps", caps.tolist()[:6])
+    kc, vc, start = _slabs(c, caps, 7)
+    kd, vd = dev_tensor(kc, cfg.dtype), dev_tensor(vc, cfg.dtype)
+    sd, ld = dev_tensor(start, None), dev_tensor(lens, None)
+    t = c.gpu_tree()
+    o_cap, _ = lib.ddtree_tree_attention_ranges_capped(c.d("q"), kd, vd, sd, ld, start, caps,
+                                                       c.d("k_tree"), c.d("v_tree"), t)
+    o_eq, _ = lib.ddtree_tree_attention_ranges_capped(c.d("q"), kd, vd, sd, ld, start, lens,
+                                                      c.d("k_tree"), c.d("v_tree"), t)
+    o_rng, _ = lib.ddtree_tree_attention_ranges(c.d("q"), kd, vd, sd, ld, start, lens,
+                                                c.d("k_tree"), c.d("v_tree"), t)
+    torch.cuda.synchronize()
+    bits = torch.int16 if cfg.dtype == "bf16" else torch.int32
+    assert torch.equal(o_eq.cpu().view(bits), o_rng.cpu().view(bits))
+    assert_attention_close(attn_to_f64(o_cap), _oracle_over(c, kc, vc, start, lens, c.tree),
+                           cfg.dtype)
+
+
+def test_capped_graph_replays_as_contexts_grow():
+    """One captured call, replayed while the device lengths grow (and one
+    request's shrinks to 0) and new context rows are written: every replay
+    matches the oracle over the lengths of that moment."""
+    import tree_verification_build_amd as lib
+    c = _case("ranges_b20_bf16")
+    cfg = c.cfg
+    lens = c.inp["ctx_lens"].astype(np.int32)
+    grow = 3 * 200
+    caps = (lens + grow).astype(np.int32)
+    kc, vc, start = _slabs(c, caps, 8)
+    kd, vd = dev_tensor(kc, cfg.dtype), dev_tensor(vc, cfg.dtype)
+    sd, ld = dev_tensor(start, None), dev_tensor(lens, None)
+    t = c.gpu_tree()
+    out = torch.empty_like(c.d("q"))
+    ws = torch.empty(max(16, lib.ddtree_tree_attention_ranges_workspace_size(
+        cfg.B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, caps)), dtype=torch.uint8, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.ddtree_tree_attention_ranges_capped(c.d("q"), kd, vd, sd, ld, start, caps,
+                                                c.d("k_tree"), c.d("v_tree"), t, out=out,
+                                                workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    cur = lens.copy()
+    for step in range(4):
+        if step > 0:
+            add = rng.integers(0, 201, size=cfg.B).astype(np.int32)
+            new = np.minimum(cur + add, caps)
+            if step == 2:
+                new[0] = 0
+            for b in range(cfg.B):
+                if new[b] > cur[b]:
+                    rows = rng.standard_normal((new[b] - cur[b], cfg.Hkv, cfg.Dh)).astype(np.float32)
+                    kc[start[b] + cur[b]:start[b] + new[b]] = workloads.f32_to_bf16_bits(rows)
+                    vc[start[b] + cur[b]:start[b] + new[b]] = workloads.f32_to_bf16_bits(rows[::-1])
+            kd.copy_(dev_tensor(kc, cfg.dtype))
+            vd.copy_(dev_tensor(vc, cfg.dtype))
+            ld.copy_(torch.from_numpy(new))
+            cur = new
+        g.replay()
+        torch.cuda.synchronize()
+        say("capped graph replay", step, "total context", int(cur.sum()))
+        assert_attention_close(attn_to_f64(out), _oracle_over(c, kc, vc, start, cur, c.tree),
+                               cfg.dtype)

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     ddtree_draft_topk,
     ddtree_draft_topk_workspace_size, ddtree_last_error,
     ddtree_sampling_constants, ddtree_tree_attention, ddtree_tree_attention_ranges,
+    ddtree_tree_attention_ranges_capped,
     ddtree_tree_attention_ranges_workspace_size, ddtree_tree_attention_workspace_size,
     ddtree_tree_attention_tuned, ddtree_tree_attention_tuned_workspace_size,
     ddtree_tree_attention_noalloc,

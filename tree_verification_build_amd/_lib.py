@@ -55,6 +55,7 @@ lib.ddtree_tree_attention_ranges_workspace_size.restype = _sz
 lib.ddtree_tree_attention_ranges.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _tp, _i32,
                                              _i32, _i32, ctypes.c_int, _f32, _vp, _vp, _vp, _sz,
                                              _vp]
+lib.ddtree_tree_attention_ranges_capped.argtypes = lib.ddtree_tree_attention_ranges.argtypes
 lib.ddtree_vocab_reduce_workspace_size.argtypes = [_i32, _i32, _i32]
 lib.ddtree_vocab_reduce_workspace_size.restype = _sz
 lib.ddtree_vocab_reduce.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _f32, _vp, _vp, _vp,
@@ -77,7 +78,8 @@ lib.ddtree_commit.argtypes = [_tp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c
 lib.ddtree_sampling_constants.argtypes = [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]
 for _f in ("ddtree_draft_topk", "ddtree_build", "ddtree_tree_attention",
            "ddtree_tree_attention_tuned", "ddtree_tree_attention_noalloc",
-           "ddtree_tree_attention_ranges", "ddtree_vocab_reduce",
+           "ddtree_tree_attention_ranges", "ddtree_tree_attention_ranges_capped",
+           "ddtree_vocab_reduce",
            "ddtree_verify_greedy", "ddtree_vocab_verify_greedy", "ddtree_verify_sample",
            "ddtree_verify_sample_lazy",
            "ddtree_verify_linear_sample", "ddtree_commit", "ddtree_vocab_top_p",
@@ -321,6 +323,24 @@ def ddtree_tree_attention_ranges(q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_
                                  want_lse=False, workspace=None, stream=None):
     """Tree attention with request b's context = rows [ctx_start[b], ctx_start[b] +
     ctx_len[b]) of k_ctx / v_ctx.  Returns (out [B, N, Hq, Dh], lse or None)."""
+    return _ranges(lib.ddtree_tree_attention_ranges, q, k_ctx, v_ctx, ctx_start, ctx_len,
+                   ctx_start_host, ctx_len_host, k_tree, v_tree, tree, scale, out, want_lse,
+                   workspace, stream)
+
+
+def ddtree_tree_attention_ranges_capped(q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_host,
+                                        ctx_cap_host, k_tree, v_tree, tree, scale=None, out=None,
+                                        want_lse=False, workspace=None, stream=None):
+    """ddtree_tree_attention_ranges with the lengths read from ctx_len on the device when
+    the kernels run; ctx_cap_host (host) bounds them and fixes the plan, so a captured
+    call stays valid while ctx_len grows up to the bounds.  Returns (out, lse or None)."""
+    return _ranges(lib.ddtree_tree_attention_ranges_capped, q, k_ctx, v_ctx, ctx_start, ctx_len,
+                   ctx_start_host, ctx_cap_host, k_tree, v_tree, tree, scale, out, want_lse,
+                   workspace, stream)
+
+
+def _ranges(fn, q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_host, ctx_len_host, k_tree,
+            v_tree, tree, scale, out, want_lse, workspace, stream):
     B, N, Hq, Dh = q.shape
     Hkv = k_tree.shape[2]
     _dev(q, "q", (torch.bfloat16, torch.float32))
@@ -343,7 +363,7 @@ def ddtree_tree_attention_ranges(q, k_ctx, v_ctx, ctx_start, ctx_len, ctx_start_
     lse = torch.empty((B, N, Hq), dtype=torch.float32, device=q.device) if want_lse else None
     need = int(lib.ddtree_tree_attention_ranges_workspace_size(B, N, Hq, Hkv, Dh, hlp))
     workspace = _scratch(workspace, need, q.device, stream)
-    _check(lib.ddtree_tree_attention_ranges(
+    _check(fn(
         _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len), hsp, hlp,
         _ptr(k_tree), _ptr(v_tree), tree.cstruct, Hq, Hkv, Dh, _dtype_code(q),
         0.0 if scale is None else float(scale), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(), _stream(stream)))

@@ -84,6 +84,10 @@ struct AttnArgs {
   int tab_split0[kTabMax + 1];
   int tab_off[kTabMax];
   int tab_len[kTabMax];
+  // capped form (ddtree_tree_attention_ranges_capped): tab_len holds upper
+  // bounds that fix the plan; the kernels read the lengths from ctx_len when
+  // they run, take the splits those lengths need and leave the rest idle
+  int dyn_len;
 };
 
 // ------------------------------------------------------------------ dtype policies
@@ -258,8 +262,15 @@ __device__ __forceinline__ SplitItem lookup_split(const AttnArgs& a, int sid, in
       const int mid = (lo + hi) >> 1;
       if (a.tab_split0[mid] <= sid) lo = mid; else hi = mid;
     }
-    return SplitItem{lo, sid - a.tab_split0[lo], a.tab_split0[lo + 1] - a.tab_split0[lo],
-                     a.tab_off[lo], a.tab_len[lo]};
+    SplitItem it{lo, sid - a.tab_split0[lo], a.tab_split0[lo + 1] - a.tab_split0[lo],
+                 a.tab_off[lo], a.tab_len[lo]};
+    if (a.dyn_len) {
+      // the length now in device memory, clamped to the planned bound
+      it.len = min(max(a.ctx_len[lo], 0), a.tab_len[lo]);
+      it.nsplit = it.len > 0 ? (it.len + a.split_keys - 1) / a.split_keys : 1;
+      if (it.split >= it.nsplit) it.b = -1;   // a split past the context: idle
+    }
+    return it;
   }
   if (wave == 0) find_split(a, sid, a.split_keys, lane, shared_item);
   __syncthreads();
@@ -847,6 +858,11 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   if (a.tab_n > 0) {
     start = a.tab_split0[b];
     ns = a.tab_split0[b + 1] - start;
+    if (a.dyn_len) {
+      // the splits the main kernel ran for the length in device memory
+      const int Ld = min(max(a.ctx_len[b], 0), a.tab_len[b]);
+      ns = min(ns, Ld > 0 ? (Ld + a.split_keys - 1) / a.split_keys : 1);
+    }
   } else {
     const int SK = a.split_keys;
     auto nsplits = [&](int bb) {
@@ -1166,6 +1182,8 @@ ddtree_status attention_impl(AttnArgs& a, const char* who, const void* q, const 
   a.split_keys = sk;
   a.total_splits = splits;
   a.tab_n = 0;
+  if (a.dyn_len && B > kTabMax)
+    return fail(DDTREE_EUNSUPPORTED, "%s: more than %d requests", who, kTabMax);
   if (B <= kTabMax) {
     a.tab_n = B;
     int acc = 0;
@@ -1274,6 +1292,7 @@ ddtree_status packed_attention(const char* who, const void* q, const void* k_ctx
   a.ctx_offsets = ctx_offsets;
   a.ctx_start = nullptr;
   a.ctx_len = nullptr;
+  a.dyn_len = 0;
   return attention_impl(a, who, q, k_ctx, v_ctx, hr, k_tree, v_tree, tree, Hq, Hkv, Dh, dtype,
                         scale, out, lse, workspace, workspace_bytes, tuning, stream);
 }
@@ -1341,14 +1360,19 @@ extern "C" ddtree_status ddtree_tree_attention(
                                      workspace_bytes, nullptr, stream);
 }
 
-extern "C" ddtree_status ddtree_tree_attention_ranges(
-    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_start,
-    const int32_t* ctx_len, const int32_t* ctx_start_host, const int32_t* ctx_len_host,
-    const void* k_tree, const void* v_tree, const ddtree_tree* tree, int32_t Hq, int32_t Hkv,
-    int32_t Dh, ddtree_dtype dtype, float scale, void* out, float* lse, void* workspace,
-    size_t workspace_bytes, hipStream_t stream) {
-  using namespace ddt;
-  const char* who = "ddtree_tree_attention_ranges";
+namespace ddt {
+namespace {
+
+// Validation and launch of the range forms: exact lengths (capped = false)
+// or upper bounds of lengths read from the device when the kernels run.
+ddtree_status ranges_attention(const char* who, bool capped, const void* q, const void* k_ctx,
+                               const void* v_ctx, const int32_t* ctx_start,
+                               const int32_t* ctx_len, const int32_t* ctx_start_host,
+                               const int32_t* ctx_len_host, const void* k_tree,
+                               const void* v_tree, const ddtree_tree* tree, int32_t Hq,
+                               int32_t Hkv, int32_t Dh, ddtree_dtype dtype, float scale,
+                               void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   ddtree_status st = check_tree(tree, who);
   if (st != DDTREE_OK) return st;
   if (!ctx_start || !ctx_len || !ctx_start_host || !ctx_len_host)
@@ -1362,8 +1386,35 @@ extern "C" ddtree_status ddtree_tree_attention_ranges(
   a.ctx_offsets = nullptr;
   a.ctx_start = ctx_start;
   a.ctx_len = ctx_len;
+  a.dyn_len = capped ? 1 : 0;
   return attention_impl(a, who, q, k_ctx, v_ctx, HostRanges{nullptr, ctx_start_host, ctx_len_host},
-                        k_tree, v_tree,
-                        tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
-                        nullptr, stream);
+                        k_tree, v_tree, tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace,
+                        workspace_bytes, nullptr, stream);
+}
+
+}  // namespace
+}  // namespace ddt
+
+extern "C" ddtree_status ddtree_tree_attention_ranges(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_start,
+    const int32_t* ctx_len, const int32_t* ctx_start_host, const int32_t* ctx_len_host,
+    const void* k_tree, const void* v_tree, const ddtree_tree* tree, int32_t Hq, int32_t Hkv,
+    int32_t Dh, ddtree_dtype dtype, float scale, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  return ddt::ranges_attention("ddtree_tree_attention_ranges", false, q, k_ctx, v_ctx, ctx_start,
+                               ctx_len, ctx_start_host, ctx_len_host, k_tree, v_tree, tree, Hq,
+                               Hkv, Dh, dtype, scale, out, lse, workspace, workspace_bytes,
+                               stream);
+}
+
+extern "C" ddtree_status ddtree_tree_attention_ranges_capped(
+    const void* q, const void* k_ctx, const void* v_ctx, const int32_t* ctx_start,
+    const int32_t* ctx_len, const int32_t* ctx_start_host, const int32_t* ctx_cap_host,
+    const void* k_tree, const void* v_tree, const ddtree_tree* tree, int32_t Hq, int32_t Hkv,
+    int32_t Dh, ddtree_dtype dtype, float scale, void* out, float* lse, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  return ddt::ranges_attention("ddtree_tree_attention_ranges_capped", true, q, k_ctx, v_ctx,
+                               ctx_start, ctx_len, ctx_start_host, ctx_cap_host, k_tree, v_tree,
+                               tree, Hq, Hkv, Dh, dtype, scale, out, lse, workspace,
+                               workspace_bytes, stream);
 }
