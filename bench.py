@@ -351,6 +351,7 @@ def run_gpu(cfg, args, rotate):
     r["attn_ms"], r["attn_reps"] = w.call_ms(w.attention)
     r["vocab_ms"], r["vocab_reps"] = w.call_ms(w.vocab)
     r["decode_loop"] = run_decode_loop(w, max(100, args.steps))
+    r["decode_loop_graph"] = run_decode_loop_graph(w, max(100, args.steps))
     if not args.no_extras:
         extra_steps = max(args.steps, 100)
         if T == 0:
@@ -456,6 +457,106 @@ def run_decode_loop(w, steps):
             "step": "build (previous bonus and prefix), ddtree_tree_attention_ranges over the "
                     "slabs (plan made anew), vocabulary pass and walk (one launch when greedy), "
                     "ddtree_commit, accept lengths to the host, synchronise; eager launches"}
+
+
+def run_decode_loop_graph(w, steps):
+    """The decode loop of run_decode_loop with each step a replayed HIP graph:
+    build from the previous step's (prefix length, root) on the device,
+    ddtree_tree_attention_ranges_capped over the slabs (the lengths read on the
+    device when the kernels run, the slab capacities as bounds, so the captured
+    call stays valid as the caches grow), vocabulary pass and walk,
+    ddtree_commit appending the accepted K/V and writing the next (prefix
+    length, root).  One graph per (input set, step parity): the (prefix, root)
+    and walk buffers alternate between steps.  The host waits for every step's
+    accept lengths by polling them in pinned memory (the walk's completion
+    protocol) and keeps its own copy of the lengths; nothing else crosses."""
+    torch, lib, cfg = w.torch, w.lib, w.cfg
+    dev, B, D, T = w.dev, cfg.B, cfg.D, cfg.temperature
+    lens = np.diff(w.inp["ctx_offsets"]).astype(np.int64)
+    cap = int(lens.max()) + steps * (D + 1) + 1
+    base = np.arange(B, dtype=np.int64) * cap
+    s0 = w.sets[0]
+    kslab = torch.empty((B * cap, cfg.Hkv, cfg.Dh), dtype=s0["k_ctx"].dtype, device=dev)
+    vslab = torch.empty_like(kslab)
+    offs = w.inp["ctx_offsets"]
+    for b in range(B):
+        kslab[base[b]:base[b] + lens[b]] = s0["k_ctx"][offs[b]:offs[b + 1]]
+        vslab[base[b]:base[b] + lens[b]] = s0["v_ctx"][offs[b]:offs[b + 1]]
+    start_h = base.astype(np.int32)
+    caps_h = np.full(B, cap, dtype=np.int32)
+    start_d = torch.from_numpy(start_h).to(dev)
+    base_d = torch.from_numpy(base).to(dev)
+    prefix_d = [torch.from_numpy(lens.astype(np.int32)).to(dev),
+                torch.empty((B,), dtype=torch.int32, device=dev)]
+    root_d = [w.small["root_tok"].clone(), torch.empty((B,), dtype=torch.int32, device=dev)]
+    walks = [{"accept_len": torch.empty((B,), dtype=torch.int32, pin_memory=True),
+              "bonus": torch.empty((B,), dtype=torch.int32, pin_memory=True),
+              "path_nodes": torch.empty((B, D + 1), dtype=torch.int32, device=dev),
+              "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=dev)}
+             for _ in range(2)]
+    ws = torch.empty(max(16, lib.ddtree_tree_attention_ranges_workspace_size(
+        B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, caps_h)), dtype=torch.uint8, device=dev)
+    sm = w.small
+    keep = []
+
+    def step(si, p):
+        s = w.sets[si]
+        lib.ddtree_build(sm["draft_lp"], sm["draft_tok"], root_d[p], prefix_d[p], cfg.budget,
+                         tree=w.tree)
+        lib.ddtree_tree_attention_ranges_capped(s["q"], kslab, vslab, start_d, prefix_d[p],
+                                                start_h, caps_h, s["k_tree"], s["v_tree"],
+                                                w.tree, out=w.attn_out, workspace=ws)
+        if T > 0:
+            v = w.vocab(s)
+            keep.append(v)
+            lib.ddtree_verify_sample(w.tree, s["logits"], v["maxv"], v["R"], v["R_blocks"], T,
+                                     sm["uniforms"], outputs=walks[p])
+        else:
+            lib.ddtree_vocab_verify_greedy(s["logits"], w.tree, workspace=w.ws_v,
+                                           outputs=walks[p], argmax=w.f_am, maxv=w.f_mx)
+        lib.ddtree_commit(w.tree, walks[p], s["k_tree"], s["v_tree"], kslab, vslab, base_d, cap,
+                          next_prefix_len=prefix_d[1 - p], next_root=root_d[1 - p])
+
+    graphs = {}
+    for si in range(w.rotate):
+        for p in range(2):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(si, p)
+            graphs[si, p] = g
+    torch.cuda.synchronize()
+    # capturing ran nothing: the slabs and lengths are still the initial ones
+    prefix_h = lens.astype(np.int32)
+    acc = [x["accept_len"].numpy() for x in walks]
+    tokens = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        p = i % 2
+        a = acc[p]
+        a.fill(-1)
+        graphs[i % w.rotate, p].replay()
+        t1 = time.perf_counter()
+        while (a < 0).any():
+            if time.perf_counter() - t1 > 5.0:
+                raise RuntimeError(f"decode step {i}: no accept lengths after 5 s")
+        prefix_h = (prefix_h + a + 1).astype(np.int32)
+        tokens += int(a.sum()) + B
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    consistent = bool(np.array_equal(prefix_d[steps % 2].cpu().numpy(), prefix_h))
+    del graphs, kslab, vslab, keep
+    return {"steps": steps, "steps_per_s": round(steps / dt, 2),
+            "ms_per_step": round(1e3 * dt / steps, 4),
+            "tokens_per_s": round(tokens / dt, 1),
+            "accept_len_mean": round((tokens - steps * B) / (steps * B), 4),
+            "ctx_growth": [int(lens.sum()), int(prefix_h.astype(np.int64).sum())],
+            "host_lengths_match_device": consistent,
+            "step": "build from the device's (prefix length, root), "
+                    "ddtree_tree_attention_ranges_capped over the slabs (lengths read on the "
+                    "device, slab capacities as bounds), vocabulary pass and walk, "
+                    "ddtree_commit; one replayed HIP graph per step, the host polling the "
+                    "accept lengths in pinned memory"}
 
 
 def run_commit(w):
@@ -782,6 +883,7 @@ def config_record(cfg, r, args, rotate):
         "accept_len_mean": r["accept_len_mean"],
         "tree_stats": r["tree_stats"],
         "decode_loop": r["decode_loop"],
+        "decode_loop_graph": r["decode_loop_graph"],
     }
     rec["step"] = ("build, attention, ddtree_vocab_verify_greedy (vocabulary reduction and "
                    "greedy walk in one launch)" if cfg.temperature == 0 else

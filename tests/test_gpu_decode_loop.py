@@ -140,3 +140,123 @@ def test_decode_loop_matches_oracle_chain(name):
     assert accepted > 0
     assert np.array_equal(_bits(kc, dt), k_ref.view(np.int16 if dt == "bf16" else np.int32))
     assert np.array_equal(_bits(vc, dt), v_ref.view(np.int16 if dt == "bf16" else np.int32))
+
+
+@pytest.mark.parametrize("name", ["sample_bf16_gqa", "greedy_bf16", "greedy_f32_dh64"])
+def test_decode_loop_graph_matches_oracle_chain(name):
+    """The same chain with each GPU step a replayed HIP graph, captured once
+    per step parity before the loop: the attention is
+    ddtree_tree_attention_ranges_capped (the lengths read on the device, the
+    slab capacities as bounds), the walk writes accept_len and bonus to pinned
+    host memory and ddtree_commit reads them there, and the (prefix length,
+    root) and walk buffers alternate between steps.  Each step's inputs are
+    copied into the captured buffers before its replay; nothing is planned or
+    read back on the host."""
+    import tree_verification_build_amd as lib
+    cfg, steps = CASES[name]
+    B, D, T, dt = cfg.B, cfg.D, cfg.temperature, cfg.dtype
+    inp0 = workloads.make_inputs(cfg)
+    lens = inp0["ctx_lens"].astype(np.int64)
+    cap = int(lens.max()) + steps * (D + 1) + 1
+    base = np.arange(B, dtype=np.int64) * cap
+    k_ref = _fill(B * cap, cfg.Hkv, cfg.Dh, dt)
+    v_ref = _fill(B * cap, cfg.Hkv, cfg.Dh, dt)
+    offs = inp0["ctx_offsets"]
+    for b in range(B):
+        k_ref[base[b]:base[b] + lens[b]] = inp0["k_ctx"][offs[b]:offs[b + 1]]
+        v_ref[base[b]:base[b] + lens[b]] = inp0["v_ctx"][offs[b]:offs[b + 1]]
+    prefix_ref = inp0["prefix_len"].astype(np.int32)
+    root_ref = inp0["root_tok"].astype(np.int32)
+    kc, vc = dev_tensor(k_ref, dt), dev_tensor(v_ref, dt)
+    base_d = torch.from_numpy(base).to(DEV)
+    start_h = base.astype(np.int32)
+    caps_h = np.full(B, cap, dtype=np.int32)
+    start_d = torch.from_numpy(start_h).to(DEV)
+    prefix_d = [torch.from_numpy(prefix_ref.copy()).to(DEV), torch.zeros(B, dtype=torch.int32,
+                                                                          device=DEV)]
+    root_d = [torch.from_numpy(root_ref.copy()).to(DEV), torch.zeros(B, dtype=torch.int32,
+                                                                      device=DEV)]
+    # the captured input buffers, filled before every replay
+    i0, c0 = _step_inputs(cfg, 0)
+    tree0 = oracle.build_tree(i0["draft_lp"], i0["draft_tok"], root_ref, prefix_ref, cfg.budget)
+    logits0, _ = workloads.make_target_logits(c0, i0, tree0["depth"], tree0["num_nodes"])
+    buf = {"draft_lp": dev_tensor(i0["draft_lp"], None), "draft_tok": dev_tensor(i0["draft_tok"], None),
+           "q": dev_tensor(i0["q"], dt), "k_tree": dev_tensor(i0["k_tree"], dt),
+           "v_tree": dev_tensor(i0["v_tree"], dt), "logits": dev_tensor(logits0, dt),
+           "uniforms": dev_tensor(i0["uniforms"], None)}
+    t = lib.alloc_tree(B, cfg.budget, D, cfg.K, DEV)
+    attn = torch.empty_like(buf["q"])
+    ws_a = torch.empty(max(16, lib.ddtree_tree_attention_ranges_workspace_size(
+        B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh, caps_h)), dtype=torch.uint8, device=DEV)
+    ws_v = torch.empty(max(16, lib.ddtree_vocab_reduce_workspace_size(B, cfg.N, cfg.V)),
+                       dtype=torch.uint8, device=DEV)
+    walks = [{"accept_len": torch.empty((B,), dtype=torch.int32, pin_memory=True),
+              "bonus": torch.empty((B,), dtype=torch.int32, pin_memory=True),
+              "path_nodes": torch.empty((B, D + 1), dtype=torch.int32, device=DEV),
+              "out_tokens": torch.empty((B, D + 1), dtype=torch.int32, device=DEV)}
+             for _ in range(2)]
+    keep = []
+
+    def step(p):
+        lib.ddtree_build(buf["draft_lp"], buf["draft_tok"], root_d[p], prefix_d[p], cfg.budget,
+                         tree=t)
+        lib.ddtree_tree_attention_ranges_capped(buf["q"], kc, vc, start_d, prefix_d[p], start_h,
+                                                caps_h, buf["k_tree"], buf["v_tree"], t,
+                                                out=attn, workspace=ws_a)
+        v = lib.ddtree_vocab_reduce(buf["logits"], t.num_nodes, T, workspace=ws_v)
+        keep.append(v)
+        if T > 0:
+            lib.ddtree_verify_sample(t, buf["logits"], v["maxv"], v["R"], v["R_blocks"], T,
+                                     buf["uniforms"], outputs=walks[p])
+        else:
+            lib.ddtree_verify_greedy(t, v["argmax"], outputs=walks[p])
+        lib.ddtree_commit(t, walks[p], buf["k_tree"], buf["v_tree"], kc, vc, base_d, cap,
+                          next_prefix_len=prefix_d[1 - p], next_root=root_d[1 - p])
+
+    graphs = []
+    for p in range(2):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(p)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    accepted = 0
+    for s in range(steps):
+        say("decode loop graph", name, "step", s, "prefix", prefix_ref[:4].tolist())
+        i, cs = _step_inputs(cfg, s)
+        tree = oracle.build_tree(i["draft_lp"], i["draft_tok"], root_ref, prefix_ref, cfg.budget)
+        logits, _ = workloads.make_target_logits(cs, i, tree["depth"], tree["num_nodes"])
+        pk = np.concatenate([k_ref[base[b]:base[b] + prefix_ref[b]] for b in range(B)])
+        pv = np.concatenate([v_ref[base[b]:base[b] + prefix_ref[b]] for b in range(B)])
+        poffs = np.concatenate([[0], np.cumsum(prefix_ref)]).astype(np.int32)
+        o_ref, _ = oracle.tree_attention(i["q"], pk, pv, poffs, i["k_tree"], i["v_tree"],
+                                         tree["vis"], tree["num_nodes"], dtype=dt)
+        vr = oracle.vocab_reduce(logits, tree["num_nodes"], T, dtype=dt)
+        if T > 0:
+            w_ref = oracle.verify_sample(tree, logits, vr["maxv"], vr["R"], T, i["uniforms"], D,
+                                         dtype=dt)
+        else:
+            w_ref = oracle.verify_greedy(tree, vr["argmax"], D)
+        cm = oracle.commit_path(tree, w_ref["accept_len"], w_ref["path_nodes"], w_ref["bonus"],
+                                i["k_tree"], i["v_tree"], k_ref, v_ref, base, cap)
+        for k, a in (("draft_lp", i["draft_lp"]), ("draft_tok", i["draft_tok"]),
+                     ("uniforms", i["uniforms"])):
+            buf[k].copy_(dev_tensor(a, None))
+        for k, a in (("q", i["q"]), ("k_tree", i["k_tree"]), ("v_tree", i["v_tree"]),
+                     ("logits", logits)):
+            buf[k].copy_(dev_tensor(a, dt))
+        p = s % 2
+        graphs[p].replay()
+        torch.cuda.synchronize()
+        assert_tree_equal(t.to_numpy(), tree)
+        assert_attention_close(attn_to_f64(attn), o_ref, dt)
+        for k in w_ref:
+            assert np.array_equal(walks[p][k].cpu().numpy(), w_ref[k]), (s, k)
+        assert np.array_equal(prefix_d[1 - p].cpu().numpy(), cm["next_prefix_len"]), s
+        assert np.array_equal(root_d[1 - p].cpu().numpy(), cm["next_root"]), s
+        k_ref, v_ref = cm["k_cache"], cm["v_cache"]
+        prefix_ref, root_ref = cm["next_prefix_len"], cm["next_root"]
+        accepted += int(w_ref["accept_len"].sum())
+    assert accepted > 0
+    assert np.array_equal(_bits(kc, dt), k_ref.view(np.int16 if dt == "bf16" else np.int32))
+    assert np.array_equal(_bits(vc, dt), v_ref.view(np.int16 if dt == "bf16" else np.int32))

@@ -123,9 +123,10 @@ def _scratch(workspace, need, device, stream):
     return ws
 
 
-def _dev(t, name, dtype=None, shape=None):
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+def _dev(t, name, dtype=None, shape=None, pinned_ok=False):
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor"
+                        + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
@@ -562,9 +563,10 @@ def ddtree_commit(tree, walk, k_tree, v_tree, k_cache, v_cache, cache_base, capa
         raise ValueError(f"k_cache has shape {tuple(k_cache.shape)}, expected (rows, {Hkv}, {Dh})")
     _dev(v_cache, "v_cache", k_tree.dtype, tuple(k_cache.shape))
     _dev(cache_base, "cache_base", torch.int64, (B,))
-    _dev(walk["accept_len"], "accept_len", torch.int32, (B,))
-    _dev(walk["path_nodes"], "path_nodes", torch.int32, (B, tree.D + 1))
-    _dev(walk["bonus"], "bonus", torch.int32, (B,))
+    # a walk's outputs may sit in pinned host memory (read by the kernel over the bus)
+    _dev(walk["accept_len"], "accept_len", torch.int32, (B,), pinned_ok=True)
+    _dev(walk["path_nodes"], "path_nodes", torch.int32, (B, tree.D + 1), pinned_ok=True)
+    _dev(walk["bonus"], "bonus", torch.int32, (B,), pinned_ok=True)
     dev = k_tree.device
     if next_prefix_len is None:
         next_prefix_len = torch.empty((B,), dtype=torch.int32, device=dev)
