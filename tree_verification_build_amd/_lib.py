@@ -103,7 +103,9 @@ def _check(st):
 
 
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
+    # the current device's index given explicitly: torch's own lookup of the
+    # default device goes through an availability check on every call
+    s = torch.cuda.current_stream(torch.cuda.current_device()) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
 
 
