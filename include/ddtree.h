@@ -193,7 +193,8 @@ ddtree_status ddtree_build(const float* draft_lp, const int32_t* draft_tok,
  * Context lengths: the host copy decides the work split and the grid.  For
  * B <= 64 the kernels take every context range from the host copy (the device
  * array is not read), so a call captured in a HIP graph keeps the ranges it
- * was captured with.  For B > 64 the kernels look their ranges up in the
+ * was captured with (ddtree_tree_attention_ranges_capped reads the lengths on
+ * the device instead, for captured steps over growing caches).  For B > 64 the kernels look their ranges up in the
  * device array, which must then hold the host copy's values; if it does not,
  * the output is undefined but no workspace access leaves the planned splits.
  * Errors: DDTREE_EINVAL (null pointers, sizes, small workspace),
