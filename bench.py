@@ -377,7 +377,11 @@ def run_gpu(cfg, args, rotate):
     return r
 
 
-DECODE_WARMUP = 3   # untimed chained steps before each decode loop's timed ones
+DECODE_WARMUP = 3   # untimed chained steps before the graph-replayed decode loop's timed ones
+# untimed steps before the eager loop's: in a fresh process its first eager launches of
+# the range-form attention stall once or twice for tens of milliseconds (at the first
+# call and near the 90th), a start-up cost of the launch path, not a per-step one
+EAGER_DECODE_WARMUP = 120
 
 
 def run_decode_loop(w, steps):
@@ -393,7 +397,7 @@ def run_decode_loop(w, steps):
     torch, lib, cfg = w.torch, w.lib, w.cfg
     dev, B, D, T = w.dev, cfg.B, cfg.D, cfg.temperature
     lens = np.diff(w.inp["ctx_offsets"]).astype(np.int64)
-    cap = int(lens.max()) + (DECODE_WARMUP + steps) * (D + 1) + 1
+    cap = int(lens.max()) + (EAGER_DECODE_WARMUP + steps) * (D + 1) + 1
     base = np.arange(B, dtype=np.int64) * cap
     s0 = w.sets[0]
     kslab = torch.empty((B * cap, cfg.Hkv, cfg.Dh), dtype=s0["k_ctx"].dtype, device=dev)
@@ -419,13 +423,15 @@ def run_decode_loop(w, steps):
     sm = w.small
     torch.cuda.synchronize()
     tokens = 0
-    for i in range(DECODE_WARMUP + steps):
-        if i == DECODE_WARMUP:
+    for i in range(EAGER_DECODE_WARMUP + steps):
+        if i == EAGER_DECODE_WARMUP:
             # untimed steps first: the first calls of a process pay one-time costs
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             tokens = 0
             grown0 = int(prefix_h.astype(np.int64).sum())
+            per_step = []
+        ts = time.perf_counter()
         s = w.sets[i % w.rotate]
         cur, nxt = i % 2, 1 - i % 2
         need = lib.ddtree_tree_attention_ranges_workspace_size(B, cfg.N, cfg.Hq, cfg.Hkv, cfg.Dh,
@@ -452,13 +458,17 @@ def run_decode_loop(w, steps):
         a = acc_h.numpy()
         prefix_h = (prefix_h + a + 1).astype(np.int32)
         tokens += int(a.sum()) + B
+        if i >= EAGER_DECODE_WARMUP:
+            per_step.append(time.perf_counter() - ts)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    consistent = bool(np.array_equal(prefix_d[(DECODE_WARMUP + steps) % 2].cpu().numpy(),
+    consistent = bool(np.array_equal(prefix_d[(EAGER_DECODE_WARMUP + steps) % 2].cpu().numpy(),
                                      prefix_h))
     del kslab, vslab
-    return {"steps": steps, "untimed_first": DECODE_WARMUP, "steps_per_s": round(steps / dt, 2),
+    return {"steps": steps, "untimed_first": EAGER_DECODE_WARMUP, "steps_per_s": round(steps / dt, 2),
             "ms_per_step": round(1e3 * dt / steps, 4),
+            "median_ms_per_step": round(1e3 * float(np.median(per_step)), 4),
+            "max_ms_per_step": round(1e3 * float(np.max(per_step)), 4),
             "tokens_per_s": round(tokens / dt, 1),
             "accept_len_mean": round((tokens - steps * B) / (steps * B), 4),
             "ctx_growth": [grown0, int(prefix_h.astype(np.int64).sum())],
