@@ -32,7 +32,7 @@ def compute():
     g = oracle.verify_greedy(t, vr["argmax"], cfg.D)
     s = oracle.verify_sample(t, logits, vr["maxv"], vr["R"], 0.8, inp["uniforms"], cfg.D)
     out = {k: t[k].tolist() for k in ("token", "parent", "depth", "rank", "position",
-                                      "first_child", "next_sibling", "num_nodes")}
+                                      "first_child", "next_sibling", "num_nodes", "max_depth")}
     out["score_hex"] = [[float(x).hex() for x in row] for row in t["score"]]
     out["vis"] = [[[int(w) for w in n] for n in row] for row in t["vis"]]
     out["argmax"] = vr["argmax"].tolist()
