@@ -189,7 +189,7 @@ class Workload:
                                             self.cfg.temperature, workspace=self.ws_v)
 
     def step(self, i):
-        """build -> attention -> vocabulary reduction -> walk (the survey's step)."""
+        """build -> attention -> vocabulary reduction -> walk (one verify step)."""
         s = self.sets[i % self.rotate]
         lib, T = self.lib, self.cfg.temperature
         self.build()
