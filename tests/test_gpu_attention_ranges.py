@@ -301,3 +301,30 @@ def test_capped_graph_replays_as_contexts_grow():
         say("capped graph replay", step, "total context", int(cur.sum()))
         assert_attention_close(attn_to_f64(out), _oracle_over(c, kc, vc, start, cur, c.tree),
                                cfg.dtype)
+
+
+def test_capped_lengths_outside_the_bounds():
+    """Device lengths above their bounds are read as the bounds, negative ones as
+    0: the same output, bit for bit, as lengths already clamped."""
+    import tree_verification_build_amd as lib
+    c = _case("ranges_b3_bf16")
+    cfg = c.cfg
+    lens = c.inp["ctx_lens"].astype(np.int32)
+    caps = lens.copy()
+    kc, vc, start = _slabs(c, caps + 200, 12)
+    kd, vd = dev_tensor(kc, cfg.dtype), dev_tensor(vc, cfg.dtype)
+    sd = dev_tensor(start, None)
+    wild = (lens + 150).astype(np.int32)
+    wild[1] = -7
+    clamped = np.minimum(np.maximum(wild, 0), caps).astype(np.int32)
+    t = c.gpu_tree()
+    say("attention ranges capped, lengths outside the bounds", wild.tolist(), caps.tolist())
+    o_w, _ = lib.ddtree_tree_attention_ranges_capped(c.d("q"), kd, vd, sd, dev_tensor(wild, None),
+                                                     start, caps, c.d("k_tree"), c.d("v_tree"), t)
+    o_c, _ = lib.ddtree_tree_attention_ranges_capped(c.d("q"), kd, vd, sd,
+                                                     dev_tensor(clamped, None), start, caps,
+                                                     c.d("k_tree"), c.d("v_tree"), t)
+    torch.cuda.synchronize()
+    assert torch.equal(o_w.cpu().view(torch.int16), o_c.cpu().view(torch.int16))
+    assert_attention_close(attn_to_f64(o_c), _oracle_over(c, kc, vc, start, clamped, c.tree),
+                           cfg.dtype)
