@@ -16,16 +16,26 @@
 // one split, each writes an unnormalised partial (O, running max, sum) and a
 // combine kernel merges them; otherwise the split writes the output directly.
 //
-// Inside a workgroup (4 or 8 waves): 256 threads load one K/V tile per step
+// Inside a workgroup (4 or 8 waves).  bf16 at head_dim 128 (attn_dma_kernel):
+// the K and V tiles go from global memory straight into a ring of LDS stages
+// (global_load_lds, rows XOR-swizzled), the next tiles' loads in flight while
+// the current one is used; V^T fragments come from transposing LDS reads.
+// fp32 and head_dim 64 (attn_kernel): 256 threads load one K/V tile per step
 // with 16-byte coalesced loads (each thread: 4 consecutive keys of one
 // 16-byte column, for K and for V) into registers, then store it to LDS --
 // K row-major, V transposed -- and immediately issue the loads of the next
-// tile.  Wave w < QB owns query rows [16w, 16w + 16) and computes on MFMA:
+// tile.  Either way wave w < QB owns query rows [16w, 16w + 16) and computes
+// on MFMA:
 //   S^T (keys x queries) = K Q^T      (A = K from LDS, B = Q^T in registers)
 //   O^T (dims x queries) += V^T P^T   (A = V^T from LDS, B = P^T, which is
 //                                      exactly S^T's accumulator layout)
 // with an online softmax in base 2.  bf16 uses v_mfma_f32_16x16x32_bf16,
 // fp32 uses v_mfma_f32_16x16x4_f32.
+//
+// The split plan comes from host copies of the context lengths; the capped
+// range form plans from host upper bounds and reads the lengths themselves
+// from device memory when the kernels run (splits past a request's length
+// exit at once), so that one captured call serves growing caches.
 #include <algorithm>
 #include <cmath>
 #include <mutex>
