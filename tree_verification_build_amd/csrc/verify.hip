@@ -6,11 +6,16 @@
 //
 // Sampled (same page, Section 3; "Implementing Temperature-Aware Tree
 // Sampling for DDTree", "Path B"): one 1024-thread workgroup per request.
-// Wave 0 first gathers, in parallel, the weight every node's token has under
-// its parent's target row, then walks the tree with exact integer draws
-// (t = mulhi(u, R_res); accept iff t < w).  If the walk stops, the whole
-// workgroup recomputes the weights of the stopping node's row, removes the
-// rejected tokens, and finds the bonus token by an exact integer prefix scan.
+// The workgroup first gathers, in parallel, the weight every node's token has
+// under its parent's target row; wave 0 walks the tree with exact integer
+// draws (t = mulhi(u, R_res); accept iff t < w).  Where the walk stops, the
+// residual draw finds its 32768-token block from the row's block sums (the
+// rejected tokens' weights taken off their blocks), the whole workgroup
+// weighs that block, and an exact integer prefix scan picks the bonus token.
+//
+// Every walk stores accept_len last: each wave that wrote outputs releases
+// them at system scope, then one thread releases again and stores accept_len,
+// so a host polling accept_len in mapped host memory finds the rest written.
 #include "common.hpp"
 
 namespace ddt {
