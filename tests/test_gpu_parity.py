@@ -444,3 +444,29 @@ def test_walk_outputs_in_pinned_host_memory(name):
         res.append({k: x.cpu().numpy().copy() for k, x in o.items()})
     for k in res[0]:
         assert np.array_equal(res[0][k], res[1][k]), k
+
+
+# More than 128 query rows per KV head are cut into 128-row slices along the
+# grid's z axis, each streaming the context once: up to the limit of 1024 rows
+# (128 nodes x 8 grouped heads), for the bf16 DMA kernel and the fp32 one.
+ROW_SLICES = {
+    "bf16_m1024": dict(dtype="bf16", budget=127, Hq=8, Hkv=1, D=16, K=8, V=1024),
+    "f32_m256": dict(dtype="f32", budget=63, Hq=8, Hkv=2, D=8, K=8, V=1024),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROW_SLICES))
+def test_attention_row_slices(name):
+    cfg = workloads.config("ragged", B=2, ctx=(100, 700), Dh=128, temperature=0.0,
+                           seed_index=60 + len(name), **ROW_SLICES[name])
+    c = Case(cfg)
+    M = (cfg.budget + 1) * cfg.Hq // cfg.Hkv
+    say("attention row slices", name, "M", M, "slices", (M + 127) // 128)
+    t = c.gpu_tree()
+    out, lse = c.gpu_attention(t)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = c.oracle_attention()
+    assert_attention_close(attn_to_f64(out), o_ref, cfg.dtype)
+    l = lse.cpu().numpy().astype(np.float64)
+    sel = np.isfinite(lse_ref)
+    assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
