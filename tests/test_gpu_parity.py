@@ -13,7 +13,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_cases import Case, assert_attention_close, assert_tree_equal, attn_to_f64, say
+from tests.gpu_cases import Case, assert_attention_close, assert_tree_equal, attn_to_f64, \
+    dev_tensor, say
 
 pytestmark = pytest.mark.gpu
 
@@ -470,3 +471,33 @@ def test_attention_row_slices(name):
     l = lse.cpu().numpy().astype(np.float64)
     sel = np.isfinite(lse_ref)
     assert np.abs(l[sel] - lse_ref[sel]).max() < 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [1, 3, 8, 9, 100])
+def test_vocab_tiny_rows(V, dtype):
+    """Vocabularies shorter than one 16-byte vector per thread (and a single
+    token): argmax / max / lse greedy, R and R_blocks sampling, bit for bit."""
+    import tree_verification_build_amd as lib
+    rng = np.random.default_rng(1000 + V)
+    B, N = 3, 5
+    x = rng.normal(0, 2, size=(B, N, V)).astype(np.float32)
+    x[0, 1, :] = 0.5                                   # ties: the lowest index wins
+    nn = np.array([5, 3, 1], dtype=np.int32)
+    bits = workloads.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    dev = dev_tensor(bits, dtype)
+    nd = torch.from_numpy(nn).to("cuda:0")
+    say("vocab tiny rows", dtype, "V", V)
+    g = lib.ddtree_vocab_reduce(dev, nd, 0.0, want_lse=True)
+    s = lib.ddtree_vocab_reduce(dev, nd, 0.9)
+    torch.cuda.synchronize()
+    ref_g = oracle.vocab_reduce(bits, nn, 0.0, dtype=dtype)
+    ref_s = oracle.vocab_reduce(bits, nn, 0.9, dtype=dtype)
+    assert np.array_equal(g["argmax"].cpu().numpy(), ref_g["argmax"])
+    assert np.array_equal(g["maxv"].cpu().numpy().view(np.uint32), ref_g["maxv"].view(np.uint32))
+    lse, lse_ref = g["lse"].cpu().numpy().astype(np.float64), ref_g["lse"]
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.abs(lse[fin] - lse_ref[fin]).max() < 1e-5
+    assert np.array_equal(s["R"].cpu().numpy().view(np.uint64), ref_s["R"])
+    assert np.array_equal(s["R_blocks"].cpu().numpy().view(np.uint64), ref_s["R_blocks"])
