@@ -501,3 +501,46 @@ def test_vocab_tiny_rows(V, dtype):
     assert np.abs(lse[fin] - lse_ref[fin]).max() < 1e-5
     assert np.array_equal(s["R"].cpu().numpy().view(np.uint64), ref_s["R"])
     assert np.array_equal(s["R_blocks"].cpu().numpy().view(np.uint64), ref_s["R_blocks"])
+
+
+def test_deep_chain_full_accept():
+    """A 64-deep chain (top-k 1, budget 64, the depth limit) whose target
+    argmax follows it to the end: the build's visibility rows over 64
+    ancestors, and the greedy walks (separate and fused) and the sampled walk
+    at T 0.05 accepting all 64 tokens, bit for bit with the oracle."""
+    import tree_verification_build_amd as lib
+    cfg = workloads.config("single", B=2, ctx=96, D=64, K=1, budget=64, V=512, Hq=2, Hkv=2,
+                           temperature=0.0, seed_index=71)
+    c = Case(cfg)
+    tree = c.tree
+    assert int(tree["max_depth"].min()) == 64
+    rng = np.random.default_rng(72)
+    x = rng.normal(0, 1, size=(cfg.B, cfg.N, cfg.V)).astype(np.float32)
+    for b in range(cfg.B):
+        for i in range(cfg.N - 1):
+            x[b, i, tree["token"][b, i + 1]] = 12.0
+    bits = workloads.f32_to_bf16_bits(x)
+    lg = dev_tensor(bits, "bf16")
+    t = c.gpu_tree()
+    assert_tree_equal(t.to_numpy(), tree)
+    v = lib.ddtree_vocab_reduce(lg, t.num_nodes, 0.0)
+    g = lib.ddtree_verify_greedy(t, v["argmax"])
+    f = lib.ddtree_vocab_verify_greedy(lg, t)
+    T = 0.05
+    vs = lib.ddtree_vocab_reduce(lg, t.num_nodes, T)
+    u = dev_tensor(c.inp["uniforms"], None)
+    s = lib.ddtree_verify_sample(t, lg, vs["maxv"], vs["R"], vs["R_blocks"], T, u)
+    torch.cuda.synchronize()
+    ref_v = oracle.vocab_reduce(bits, tree["num_nodes"], 0.0, dtype="bf16")
+    ref_g = oracle.verify_greedy(tree, ref_v["argmax"], cfg.D)
+    ref_vs = oracle.vocab_reduce(bits, tree["num_nodes"], T, dtype="bf16")
+    ref_s = oracle.verify_sample(tree, bits, ref_vs["maxv"], ref_vs["R"], T, c.inp["uniforms"],
+                                 cfg.D, dtype="bf16")
+    assert list(ref_g["accept_len"]) == [64] * cfg.B
+    for k in ref_g:
+        assert np.array_equal(g[k].cpu().numpy(), ref_g[k]), ("greedy", k)
+        assert np.array_equal(f[k].cpu().numpy(), ref_g[k]), ("fused", k)
+    for k in ref_s:
+        assert np.array_equal(s[k].cpu().numpy(), ref_s[k]), ("sample", k)
+    say("deep chain", "greedy accept", ref_g["accept_len"].tolist(), "sampled accept",
+        ref_s["accept_len"].tolist())
