@@ -368,10 +368,8 @@ ddtree_status ddtree_tree_attention_ranges_capped(
  *             16-byte aligned device scratch; contents need no
  *             initialisation and are garbage afterwards (calls sharing it
  *             must not overlap).  Required when greedy and that size is
- *             non-zero.  Optional when sampling: with it, bf16 rows without
- *             lse take the greedy pass for argmax and max and then a
- *             streaming weight pass; without it (NULL or too small), one
- *             pass holds each row in registers.  Both give the same outputs.
+ *             non-zero.  Unused when sampling (may be NULL): a workgroup
+ *             takes each row whole, bf16 rows without lse held in registers.
  * Errors: DDTREE_EINVAL (null pointers, sizes, temperature < 0 or NaN),
  *         DDTREE_EUNSUPPORTED (sampling with V > 64 * DDTREE_R_BLOCK).
  */

@@ -189,11 +189,78 @@ def test_vocab_sampling_awkward_rows(T, V):
     assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
 
 
+def _sign_rows(V, seed):
+    """bf16 rows whose maximum lies on the negative side or is a signed zero:
+    log-softmax values (every logit negative), negatives with a -0 before a
+    +0 (equal as floats: the -0's index is the argmax), negatives with -0 as
+    their only zeros, and a positive maximum repeated at scattered indices."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    x = rng.normal(0, 3, size=V)
+    top = x.max()
+    rows.append((x - top - np.log(np.exp(x - top).sum())).astype(np.float32))
+    r = (-np.abs(rng.normal(0, 2, size=V)) - 0.01).astype(np.float32)
+    lo, hi = sorted(int(i) for i in rng.choice(V, size=2, replace=False))
+    r[lo], r[hi] = -0.0, 0.0
+    rows.append(r)
+    r = (-np.abs(rng.normal(0, 2, size=V)) - 0.01).astype(np.float32)
+    r[rng.choice(V, size=5, replace=False)] = -0.0
+    rows.append(r)
+    r = rng.normal(0, 3, size=V).astype(np.float32)
+    r[rng.choice(V, size=7, replace=False)] = 40.0
+    rows.append(r)
+    return workloads.f32_to_bf16_bits(np.stack(rows)[None])
+
+
+@pytest.mark.parametrize("V", [40960 + 8 * 7, 163840])
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_vocab_sign_rows(T, V):
+    """Row maxima that are negative or a signed zero, and repeated maxima:
+    argmax, max, R and R_blocks bit for bit with the oracle."""
+    import tree_verification_build_amd as lib
+    bits = _sign_rows(V, 52)
+    nn = np.array([bits.shape[1]], dtype=np.int32)
+    say("vocab sign rows", "T", T, "V", V)
+    logits = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    r = lib.ddtree_vocab_reduce(logits, torch.from_numpy(nn).to("cuda:0"), T)
+    torch.cuda.synchronize()
+    ref = oracle.vocab_reduce(bits, nn, T, dtype="bf16")
+    assert np.array_equal(r["argmax"].cpu().numpy(), ref["argmax"])
+    assert np.array_equal(r["maxv"].cpu().numpy().view(np.uint32), ref["maxv"].view(np.uint32))
+    if T > 0:
+        assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
+        assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
+
+
+@pytest.mark.parametrize("B,N,V", [(4, 69, 163840), (4, 69, 40960 + 8 * 7), (8, 76, 163840)])
+def test_vocab_sampling_uneven_rounds(B, N, V):
+    """Sampling rows that leave the last round of the persistent workgroups
+    partly filled (the CU count plus 20 rows, twice it plus 96): the
+    workgroups with one row fewer start late, which changes only the timing.
+    argmax, max, R and R_blocks bit for bit with the oracle, padding rows
+    included."""
+    import tree_verification_build_amd as lib
+    rng = np.random.default_rng(B * 1000 + N + V)
+    x = rng.normal(0, 3, size=(B, N, V)).astype(np.float32)
+    bits = workloads.f32_to_bf16_bits(x)
+    nn = rng.integers(1, N + 1, size=B).astype(np.int32)
+    nn[0] = N
+    say("vocab uneven rounds", B, N, V, "cus",
+        torch.cuda.get_device_properties(0).multi_processor_count)
+    logits = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    r = lib.ddtree_vocab_reduce(logits, torch.from_numpy(nn).to("cuda:0"), 0.7)
+    torch.cuda.synchronize()
+    ref = oracle.vocab_reduce(bits, nn, 0.7, dtype="bf16")
+    assert np.array_equal(r["argmax"].cpu().numpy(), ref["argmax"])
+    assert np.array_equal(r["maxv"].cpu().numpy().view(np.uint32), ref["maxv"].view(np.uint32))
+    assert np.array_equal(r["R"].cpu().numpy().view(np.uint64), ref["R"])
+    assert np.array_equal(r["R_blocks"].cpu().numpy().view(np.uint64), ref["R_blocks"])
+
+
 @pytest.mark.parametrize("name", ["bf16_gqa", "batched"])
 def test_vocab_sampling_without_workspace(name):
-    """Called without the greedy workspace, a bf16 sampling reduce runs the
-    single-kernel row pass (the row held in registers) instead of the greedy
-    pass plus the streaming weight pass: same outputs, bit for bit."""
+    """Called with no workspace (a sampling reduce needs none), through the C
+    ABI directly: the same outputs as the oracle, bit for bit."""
     from tree_verification_build_amd import _lib as L
     c = case(name)
     T = c.cfg.temperature if c.cfg.temperature > 0 else 0.8

@@ -603,14 +603,15 @@ template <int MAXP, bool WHOLE>
 __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
     const uint16_t* __restrict__ logits, int rows, int N, int V,
     const int32_t* __restrict__ num_nodes, WeightConsts wc, int32_t* __restrict__ argmax,
-    float* __restrict__ maxv, uint64_t* __restrict__ R, uint64_t* __restrict__ Rb) {
+    float* __restrict__ maxv, uint64_t* __restrict__ R, uint64_t* __restrict__ Rb, int heavy,
+    uint32_t stagger) {
   constexpr int E = 8;
   constexpr int kWaves = kRowThreads / kWave;
   constexpr int kQ = DDTREE_R_BLOCK / (kRowThreads * E);   // vectors per thread per block
   static_assert(kQ == 4, "four 8192-token vectors per weight block");
   __shared__ uint64_t s_tab[kPipeTabEntries];
   __shared__ uint64_t s_blk[kMaxRowBlocks][kWaves];
-  __shared__ float s_f[kWaves];
+  __shared__ float s_f[kWaves], s_f2[kWaves];
   __shared__ uint32_t s_i[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = (V + DDTREE_R_BLOCK - 1) / DDTREE_R_BLOCK;
@@ -628,8 +629,15 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
   // instead of keeping MAXP offsets live across the row loop
   uint32_t t8 = tid * E;
   auto vload = [&](int r, int p, bool real = true) -> u32x4_t {
+    if (WHOLE) {
+      // a uniform base (row and vector) plus the thread's 32-bit byte offset:
+      // scalar-register addressing, no per-vector address arithmetic
+      const uint16_t* base = real ? logits + static_cast<long>(r) * V + p * kRowThreads * E : logits;
+      const uint32_t off = real ? 2u * t8 : 0u;
+      return *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(base) + off);
+    }
     uint32_t i = t8 + static_cast<uint32_t>(p * kRowThreads * E);
-    if (!WHOLE) i = min(i, static_cast<uint32_t>(V - E));
+    i = min(i, static_cast<uint32_t>(V - E));
     const long off = real ? static_cast<long>(r) * V + i : 0l;
     return *reinterpret_cast<const u32x4_t*>(logits + off);
   };
@@ -641,28 +649,28 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
   // positive bf16 values order as their values do, and negative patterns are
   // negative), .y the smallest as an unsigned one (the negative logit nearest
   // zero, when no pattern is positive).  vec_max folds a vector into it.
-  struct MaxAcc {
-    uint32_t pos, neg;
-  };
+  typedef uint32_t MaxAcc;
   auto vec_max = [&](MaxAcc acc, const u32x4_t& v, int p) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t w = word(v, p, k);
-      acc.pos = pk_max_i16(acc.pos, w);
-      acc.neg = pk_min_u16(acc.neg, w);
-    }
+    for (int k = 0; k < 4; ++k) acc = pk_max_i16(acc, word(v, p, k));
     return acc;
   };
-  // back to a float: a positive pattern (or +0) if any, else the negative one
+  // back to a float: the largest non-negative pattern, -inf if none
   auto key_to_float = [](MaxAcc acc) {
-    const int32_t a = static_cast<int16_t>(acc.pos & 0xFFFFu), b = static_cast<int16_t>(acc.pos >> 16);
+    const int32_t a = static_cast<int16_t>(acc & 0xFFFFu), b = static_cast<int16_t>(acc >> 16);
     const int32_t pmax = max(a, b);
-    const uint32_t nmin = min(acc.neg & 0xFFFFu, acc.neg >> 16);
-    const uint32_t pat = pmax >= 0 ? static_cast<uint32_t>(pmax) : nmin;
-    return __uint_as_float(pat << 16);
+    return pmax >= 0 ? __uint_as_float(static_cast<uint32_t>(pmax) << 16) : -__builtin_huge_valf();
   };
-  constexpr MaxAcc kKeyNegInf = {0x80008000u, 0xFFFFFFFFu};   // no logit yet
+  constexpr MaxAcc kKeyNegInf = 0x80008000u;   // no logit yet
   u32x4_t raw[MAXP];
+  // Workgroups [0, heavy) have one row more than the others.  The others wait
+  // `stagger` ticks of the constant-rate clock before their first loads, so
+  // that the heavy workgroups' first rows arrive at a larger share of the
+  // bandwidth and their extra row starts earlier (only the timing changes).
+  if (stagger && static_cast<int>(blockIdx.x) >= heavy) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < stagger) __builtin_amdgcn_s_sleep(1);
+  }
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) raw[p] = vload(row, p);
   // this thread's maximum over its logits of the row in raw: for the first
@@ -684,17 +692,36 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
     const bool valid = row % N < num_nodes[row / N];
     const uint16_t* rp = logits + static_cast<long>(row) * V;
     // ---- the row maximum (this thread's part: vkey), then the lowest index holding it
-    const float vmax = key_to_float(vkey);
+    float vmax = key_to_float(vkey);
     const float bm = wave_max_f32_dpp(vmax);
     if (lane == 0) s_f[wave] = bm;
     __syncthreads();
     float m = s_f[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = max(m, s_f[w]);
+    if (m == -__builtin_huge_valf()) {
+      // no pattern of the row is non-negative (the same for every thread):
+      // the maximum is the negative pattern nearest zero, the smallest one as
+      // an unsigned 16-bit value, taken from the row in registers
+      uint32_t neg = 0xFFFFFFFFu;
+#pragma unroll
+      for (int p = 0; p < MAXP; ++p) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) neg = pk_min_u16(neg, word(raw[p], p, k));
+      }
+      vmax = __uint_as_float(min(neg & 0xFFFFu, neg >> 16) << 16);
+      const float bn = wave_max_f32_dpp(vmax);
+      if (lane == 0) s_f2[wave] = bn;
+      __syncthreads();
+      m = s_f2[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = max(m, s_f2[w]);
+    }
     m = m + 0.0f;   // -0 -> +0
     // bf16 patterns equal to m as floats: m's own pattern, or either zero when m is 0
     uint32_t first = 0xFFFFFFFFu;
-    if (vmax == m) {
+    // (when m is 0, a thread may hold -0 with no non-negative pattern)
+    if (vmax == m || m == 0.0f) {
       // patterns equal to m as floats, compared with the zero patterns folded
       // together when m is 0; vectors are tested whole first
       const uint32_t zm = m == 0.0f ? 0x7FFFu : 0xFFFFu;
@@ -785,7 +812,7 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
             nkey = vec_max(nkey, raw[p - kLag], p - kLag);
             // pinned here (the compiler would otherwise sink it to the next
             // row's start, where the loads would be waited for with no work)
-            __asm__ volatile("" : "+v"(nkey.pos), "+v"(nkey.neg));
+            __asm__ volatile("" : "+v"(nkey));
           }
         }
       }
@@ -863,16 +890,41 @@ int device_cus() {
   return v;
 }
 
+// The late start of the workgroups with one row fewer, in ticks of the
+// device's constant-rate clock: 3 us, measured best on the sampling passes
+// of 528 and 2112 rows of 163,840 tokens (2 and 8 whole rounds of 256
+// workgroups plus 16 and 64 rows; 2-5 us tried).  Looked up once per device.
+constexpr double kStaggerUs = 3.0;
+uint32_t stagger_ticks() {
+  static uint32_t cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  uint32_t v = __atomic_load_n(&cached[dev], __ATOMIC_RELAXED);
+  if (v == 0) {
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+      khz = 100000;   // 100 MHz
+    v = static_cast<uint32_t>(kStaggerUs * 1e-3 * khz + 0.5);
+    __atomic_store_n(&cached[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
 template <int MAXP>
 void launch_pipe(int rows, hipStream_t st, const void* logits, int N, int V, const int32_t* nn,
                  const WeightConsts& wc, int32_t* am, float* mx, uint64_t* R, uint64_t* Rb) {
   const int G = std::min(rows, device_cus());
+  // rows = F * G + heavy: with 0 < heavy, the other workgroups start late
+  const int heavy = rows % G;
+  const uint32_t stagger = heavy ? stagger_ticks() : 0u;
   if (V == MAXP * kRowThreads * 8)
     hipLaunchKernelGGL((row_pipe_kernel<MAXP, true>), dim3(G), dim3(kRowThreads), 0, st,
-                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb);
+                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb,
+                       heavy, stagger);
   else
     hipLaunchKernelGGL((row_pipe_kernel<MAXP, false>), dim3(G), dim3(kRowThreads), 0, st,
-                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb);
+                       static_cast<const uint16_t*>(logits), rows, N, V, nn, wc, am, mx, R, Rb,
+                       heavy, stagger);
 }
 
 // true when launched: bf16 rows of whole 16-byte vectors, up to 20 of them per
