@@ -643,12 +643,12 @@ __global__ __launch_bounds__(kRowThreads) void row_pipe_kernel(
   };
   auto inrow = [&](int p) { return WHOLE || t8 + static_cast<uint32_t>(p * kRowThreads * E) < static_cast<uint32_t>(V); };
   auto word = [&](const u32x4_t& v, int p, int k) { return inrow(p) ? v[k] : kNegInf2; };
-  // The running maximum of a thread's logits as two packed pairs of 16-bit
-  // patterns, one packed operation each per two logits: .x the largest pattern
-  // as a signed 16-bit value (the largest positive logit, or +0: patterns of
-  // positive bf16 values order as their values do, and negative patterns are
-  // negative), .y the smallest as an unsigned one (the negative logit nearest
-  // zero, when no pattern is positive).  vec_max folds a vector into it.
+  // The running maximum of a thread's logits: a packed pair of 16-bit
+  // patterns, one packed operation per two logits, the largest pattern as a
+  // signed 16-bit value (patterns of non-negative bf16 values order as their
+  // values do, and negative patterns are negative).  A row with no
+  // non-negative pattern takes its maximum from the registers again, below.
+  // vec_max folds a vector into it.
   typedef uint32_t MaxAcc;
   auto vec_max = [&](MaxAcc acc, const u32x4_t& v, int p) {
 #pragma unroll
