@@ -76,6 +76,39 @@ def test_build_small_table_two_slot_sets(D, K, budget):
     assert_tree_equal(t.to_numpy(), ref)
 
 
+def test_build_random_small_tables():
+    """Trees of at most 65 nodes with a draft table of at most 64 entries (one
+    frontier slot set): random depths, top-k caps and budgets, including
+    budgets the tree cannot fill, 64 and 65 nodes, and log-probs drawn from a
+    few values so that scores tie and the parent, then rank, decide; bit for
+    bit with the oracle."""
+    import tree_verification_build_amd as lib
+    rng = np.random.default_rng(515)
+    cases = [(1, 1, 1), (1, 4, 4), (2, 2, 6), (2, 2, 10), (8, 4, 63), (8, 4, 64), (16, 4, 64),
+             (8, 8, 64), (4, 8, 40), (32, 2, 64), (64, 1, 64), (3, 5, 30)]
+    for _ in range(20):
+        D = int(rng.integers(1, 17))
+        K = int(rng.integers(1, min(8, 64 // D) + 1))
+        cases.append((D, K, int(rng.integers(1, 65))))
+    for ci, (D, K, budget) in enumerate(cases):
+        B = 4
+        if ci % 2:
+            vals = np.array([-0.25, -0.5, -1.0, -2.0], np.float32)   # ties
+            lp = -np.sort(-rng.choice(vals, size=(B, D, K)), axis=-1).astype(np.float32)
+        else:
+            lp = -np.sort(np.abs(rng.standard_normal((B, D, K))), axis=-1).astype(np.float32)
+        tok = np.stack([np.stack([rng.choice(5000, K, replace=False) for _ in range(D)])
+                        for _ in range(B)]).astype(np.int32)
+        root = rng.integers(0, 5000, size=B).astype(np.int32)
+        prefix = rng.integers(0, 100, size=B).astype(np.int32)
+        say("build random small table", D, K, budget)
+        ref = oracle.build_tree(lp, tok, root, prefix, budget)
+        t = lib.ddtree_build(*(torch.from_numpy(x).to("cuda:0") for x in (lp, tok, root, prefix)),
+                             budget)
+        torch.cuda.synchronize()
+        assert_tree_equal(t.to_numpy(), ref)
+
+
 def test_build_minus_inf_logprobs():
     """Draft log-probs of -inf (masked tokens) in the top-k: real offers that
     score -inf tie one another and are taken by parent, then rank, exactly as
