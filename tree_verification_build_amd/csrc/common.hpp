@@ -92,6 +92,33 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// Wave-uniform sum of a uint64 by DPP row moves and four lane reads (all
+// lanes must be active): no shuffle-index registers and no LDS round trips.
+__device__ __forceinline__ uint64_t wave_sum_u64_dpp(uint64_t v) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+#define DDT_ROW_ADD(ctrl)                                                                         \
+  do {                                                                                            \
+    const uint32_t l2 = static_cast<uint32_t>(                                                    \
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(lo), ctrl, 0xF, 0xF, false));             \
+    const uint32_t h2 = static_cast<uint32_t>(                                                    \
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(hi), ctrl, 0xF, 0xF, false));             \
+    const uint64_t t = ((static_cast<uint64_t>(hi) << 32) | lo) + ((static_cast<uint64_t>(h2) << 32) | l2); \
+    lo = static_cast<uint32_t>(t);                                                                \
+    hi = static_cast<uint32_t>(t >> 32);                                                          \
+  } while (0)
+  DDT_ROW_ADD(0xB1);    // quad_perm [1, 0, 3, 2]
+  DDT_ROW_ADD(0x4E);    // quad_perm [2, 3, 0, 1]
+  DDT_ROW_ADD(0x124);   // row_ror 4
+  DDT_ROW_ADD(0x128);   // row_ror 8
+#undef DDT_ROW_ADD
+  uint64_t tot = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    tot += (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(hi), 16 * r))) << 32) |
+           static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(lo), 16 * r));
+  return tot;
+}
+
 // ---------------------------------------------------------------- sampling weights
 // Constants of the integer softmax weights for one temperature.
 struct WeightConsts {

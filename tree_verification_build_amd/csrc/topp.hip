@@ -11,9 +11,12 @@
 //
 // One 1024-thread workgroup per node row.  With Tt = ceil(P * R / 2^32):
 //  1. a pass over the row sums and counts the weights at or above 2^e and
-//     copies those tokens (weight, id) to LDS; it succeeds when the sum reaches
-//     Tt and the tokens fit (kCap); e starts at 20 and is moved by bisection
-//     between exponents known to reach Tt and not to (1-4 passes);
+//     copies those tokens (weight, id) to LDS, each wave into its own region
+//     (positions from a ballot and a wave-uniform count: no atomics); it
+//     succeeds when the sum reaches Tt and every wave's tokens fit its region
+//     (kTpCap in all), and the regions are then packed into one list; e
+//     starts at 20 and is moved by bisection between exponents known to reach
+//     Tt and not to (1-4 passes);
 //  2. w* = the largest v with sum{w >= v} >= Tt, by 8-way interval search
 //     (7 thresholds per reduction) over the LDS candidates by one wave, or,
 //     when more than kCap tokens are needed, over the row itself (exact,
@@ -33,6 +36,7 @@ namespace {
 constexpr int kTpThreads = 1024;
 constexpr int kTpWaves = kTpThreads / kWave;
 constexpr int kTpCap = 8192;       // candidate tokens held in LDS (12 bytes each)
+constexpr int kTpRegion = kTpCap / (kTpThreads / kWave);   // per-wave share during a pass
 constexpr int kTpProbes = 7;       // thresholds per search round (8-way search)
 constexpr int kMaxSums = kTpProbes;       // sums per block-wide reduction
 
@@ -42,7 +46,7 @@ struct TpShared {
   uint64_t part[kTpWaves][kMaxSums];
   uint64_t tot[kMaxSums];
   uint64_t blk[kWave];
-  int n;
+  int cnt[kTpThreads / kWave];
 };
 
 // Sums of K per-thread values over the workgroup; every thread gets the totals.
@@ -51,7 +55,7 @@ __device__ __forceinline__ void block_sums(uint64_t (&v)[K], TpShared& s, int ti
   static_assert(K <= kMaxSums, "partial-sum buffer too small");
   const int lane = tid & (kWave - 1), wave = tid / kWave;
 #pragma unroll
-  for (int k = 0; k < K; ++k) v[k] = wave_sum_u64(v[k]);
+  for (int k = 0; k < K; ++k) v[k] = wave_sum_u64_dpp(v[k]);
   if (lane == 0) {
 #pragma unroll
     for (int k = 0; k < K; ++k) s.part[wave][k] = v[k];
@@ -144,15 +148,15 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
   // copies those tokens to LDS (any order); the attempt succeeds when their sum
   // reaches Tt and they fit.  e starts at 20 and moves by halving the interval
   // between the largest exponent known to reach Tt and the smallest known not to.
+  const int wave = tid / kWave;
   int e = 20, e_good = -1, e_bad = 34;
   bool in_lds = false;
   int nc = 0;
   for (int attempt = 0; attempt < 12; ++attempt) {
     const uint64_t lb = 1ull << e;
     const float ymin = static_cast<float>(e - 33);
-    if (tid == 0) s.n = 0;
-    __syncthreads();
-    uint64_t sc[2] = {0, 0};
+    uint64_t sc[3] = {0, 0, 0};
+    int wcount = 0;   // this wave's tokens so far (the same in every lane)
     row_scan(ymin, [&](uint64_t w, int id) {
       const bool c = w >= lb;
       if (c) {
@@ -161,19 +165,53 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
       }
       const uint64_t mask = __ballot(c);
       if (mask == 0) return;
-      int basei = 0;
-      if (lane == 0) basei = atomicAdd(&s.n, __popcll(mask));
-      basei = __shfl(basei, 0, kWave);
-      const int pos = basei + __popcll(mask & ((1ull << lane) - 1ull));
-      if (c && pos < kTpCap) {
-        s.w[pos] = w;
-        s.id[pos] = static_cast<uint32_t>(id);
+      const int pos = wcount + __popcll(mask & ((1ull << lane) - 1ull));
+      if (c && pos < kTpRegion) {
+        s.w[wave * kTpRegion + pos] = w;
+        s.id[wave * kTpRegion + pos] = static_cast<uint32_t>(id);
       }
+      wcount += __popcll(mask);
     });
-    block_sums<2>(sc, s, tid);
+    if (lane == 0) s.cnt[wave] = wcount;
+    sc[2] = wcount > kTpRegion ? 1u : 0u;   // 1 in each lane of a wave whose tokens overflowed
+    block_sums<3>(sc, s, tid);
     if (sc[0] >= Tt) {
       e_good = e;
-      if (sc[1] <= static_cast<uint64_t>(kTpCap)) {
+      if (sc[2] == 0) {
+        // pack the regions into one list: every thread reads its entries,
+        // then (after the barrier) writes them at its region's offset
+        constexpr int kPer = kTpCap / kTpThreads;
+        static_assert(kTpThreads == 2 * kTpRegion, "entry j of a thread lies in region 2j or 2j + 1");
+        int pre[kTpThreads / kWave];   // region offsets in the packed list
+        int acc = 0;
+#pragma unroll
+        for (int w = 0; w < kTpThreads / kWave; ++w) {
+          pre[w] = acc;
+          acc += s.cnt[w];
+        }
+        const bool upper = tid >= kTpRegion;
+        const int re = tid - (upper ? kTpRegion : 0);   // entry within its region
+        uint64_t pw[kPer];
+        uint32_t pid[kPer];
+        int dst[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int src = j * kTpThreads + tid;
+          const int cnt = upper ? s.cnt[2 * j + 1] : s.cnt[2 * j];
+          const int base = upper ? pre[2 * j + 1] : pre[2 * j];
+          dst[j] = re < cnt ? base + re : -1;
+          pw[j] = s.w[src];
+          pid[j] = s.id[src];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          if (dst[j] >= 0) {
+            s.w[dst[j]] = pw[j];
+            s.id[dst[j]] = pid[j];
+          }
+        }
+        __syncthreads();
         in_lds = true;
         nc = static_cast<int>(sc[1]);
         break;
@@ -271,7 +309,7 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
         },
         [&](auto& acc) {
 #pragma unroll
-          for (int k = 0; k < kTpProbes; ++k) acc[k] = wave_sum_u64(acc[k]);
+          for (int k = 0; k < kTpProbes; ++k) acc[k] = wave_sum_u64_dpp(acc[k]);
         },
         [&]() {
           __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
