@@ -37,6 +37,7 @@ constexpr int kTpThreads = 1024;
 constexpr int kTpWaves = kTpThreads / kWave;
 constexpr int kTpCap = 8192;       // candidate tokens held in LDS (12 bytes each)
 constexpr int kTpRegion = kTpCap / (kTpThreads / kWave);   // per-wave share during a pass
+constexpr int kTpRegs = 16;        // candidates per lane the searches keep in registers
 constexpr int kTpProbes = 7;       // thresholds per search round (8-way search)
 constexpr int kMaxSums = kTpProbes;       // sums per block-wide reduction
 
@@ -303,19 +304,42 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
 
   if (in_lds) {
     if (tid >= kWave) return;   // no workgroup barrier follows
-    search(
-        [&](uint64_t, auto&& f) {
-          for (int k = lane; k < nc; k += kWave) f(s.w[k], static_cast<int>(s.id[k]));
-        },
-        [&](auto& acc) {
+    auto reduce = [&](auto& acc) {
 #pragma unroll
-          for (int k = 0; k < kTpProbes; ++k) acc[k] = wave_sum_u64_dpp(acc[k]);
-        },
-        [&]() {
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-        },
-        lane, kWave);
+      for (int k = 0; k < kTpProbes; ++k) acc[k] = wave_sum_u64_dpp(acc[k]);
+    };
+    auto sync = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
+    if (nc <= kWave * kTpRegs) {
+      // up to kTpRegs candidates per lane, read from LDS once and kept in
+      // registers for every round of the searches
+      uint64_t cw[kTpRegs];
+      int cid[kTpRegs];
+      const int nr = (nc + kWave - 1) / kWave;   // rounds of 64 (the same in every lane)
+#pragma unroll
+      for (int j = 0; j < kTpRegs; ++j) {
+        const int k = j * kWave + lane;
+        cw[j] = j < nr && k < nc ? s.w[k] : 0ull;
+        cid[j] = j < nr && k < nc ? static_cast<int>(s.id[k]) : 0;
+      }
+      search(
+          [&](uint64_t, auto&& f) {
+#pragma unroll
+            for (int j = 0; j < kTpRegs; ++j) {
+              if (j >= nr) break;
+              if (j * kWave + lane < nc) f(cw[j], cid[j]);
+            }
+          },
+          reduce, sync, lane, kWave);
+    } else {
+      search(
+          [&](uint64_t, auto&& f) {
+            for (int k = lane; k < nc; k += kWave) f(s.w[k], static_cast<int>(s.id[k]));
+          },
+          reduce, sync, lane, kWave);
+    }
   } else {
     search(
         [&](uint64_t bound, auto&& f) {
