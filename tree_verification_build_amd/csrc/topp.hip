@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
 
   // 2-5. the search, by wave 0 alone over the LDS candidates (wave-level sums),
   // or by the whole workgroup over the row (workgroup sums)
-  auto search = [&](auto&& each, auto&& reduce, auto&& sync, int lid, int nlanes) {
+  auto search = [&](auto&& each, auto&& reduce, auto&& sync, int lid, int nlanes, bool wave_level) {
     // invariant: sum{w >= lo} >= Tt > sum{w >= hi}
     uint64_t lo = 1ull << e_good;
     uint64_t hi = 1ull << min(e_bad, 33);
@@ -256,11 +256,22 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
     const uint64_t ws = lo;
     // 3. tokens of weight w* that the nucleus takes, and the id cut among them
     uint64_t g[kTpProbes] = {};
-    each(ws, [&](uint64_t w, int) { g[0] += w > ws ? w : 0; });
+    int id_max = -1;   // the largest id of weight w* (wave-level search only)
+    each(ws, [&](uint64_t w, int id) {
+      g[0] += w > ws ? w : 0;
+      g[1] += w == ws ? 1 : 0;
+      if (wave_level && w == ws) id_max = max(id_max, id);
+    });
     reduce(g);
     const uint64_t sgt = g[0];
     const uint64_t take = (Tt - sgt + ws - 1) / ws;   // 1 <= take <= #{w = w*}
     long ilo = -1, ihi = V - 1;                        // #{.. id <= ilo} < take <= #{.. id <= ihi}
+    if (wave_level && take == g[1]) {
+      // every token of weight w* is taken (the usual case): the cut is the
+      // largest of their ids
+      ihi = static_cast<long>(static_cast<int32_t>(wave_max_u32(static_cast<uint32_t>(id_max) + 1u))) - 1;
+      ilo = ihi - 1;
+    }
     for (int round = 0; round < 40 && ihi - ilo > 1; ++round) {
       long th[kTpProbes];
       uint64_t acc[kTpProbes];
@@ -332,13 +343,13 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
               if (j * kWave + lane < nc) f(cw[j], cid[j]);
             }
           },
-          reduce, sync, lane, kWave);
+          reduce, sync, lane, kWave, true);
     } else {
       search(
           [&](uint64_t, auto&& f) {
             for (int k = lane; k < nc; k += kWave) f(s.w[k], static_cast<int>(s.id[k]));
           },
-          reduce, sync, lane, kWave);
+          reduce, sync, lane, kWave, true);
     }
   } else {
     search(
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
           row_scan(static_cast<float>(63 - __builtin_clzll(bound) - 33), f);
         },
         [&](auto& acc) { block_sums<kTpProbes>(acc, s, tid); },
-        [&]() { __syncthreads(); }, tid, kTpThreads);
+        [&]() { __syncthreads(); }, tid, kTpThreads, false);
   }
 }
 
