@@ -9,7 +9,9 @@
 // token: threshold weight w* and id*; a token is kept iff w > w*, or w = w*
 // and id <= id*.
 //
-// One 1024-thread workgroup per node row.  With Tt = ceil(P * R / 2^32):
+// One 512-thread workgroup per node row, two per CU (50 KB of LDS each), so
+// that one workgroup's single-wave searches overlap the other's row pass.
+// With Tt = ceil(P * R / 2^32):
 //  1. a pass over the row sums and counts the weights at or above 2^e and
 //     copies those tokens (weight, id) to LDS, each wave into its own region
 //     (positions from a ballot and a wave-uniform count: no atomics); it
@@ -19,7 +21,7 @@
 //     Tt and not to (1-4 passes);
 //  2. w* = the largest v with sum{w >= v} >= Tt, by 8-way interval search
 //     (7 thresholds per reduction) over the LDS candidates by one wave, or,
-//     when more than kCap tokens are needed, over the row itself (exact,
+//     when more than kTpCap tokens are needed, over the row itself (exact,
 //     slower);
 //  3. every pass over the row skips the weight polynomial of the tokens that
 //     provably weigh less than the pass's lower bound;
@@ -33,9 +35,9 @@
 namespace ddt {
 namespace {
 
-constexpr int kTpThreads = 1024;
+constexpr int kTpThreads = 512;
 constexpr int kTpWaves = kTpThreads / kWave;
-constexpr int kTpCap = 8192;       // candidate tokens held in LDS (12 bytes each)
+constexpr int kTpCap = 4096;       // candidate tokens held in LDS (12 bytes each)
 constexpr int kTpRegion = kTpCap / (kTpThreads / kWave);   // per-wave share during a pass
 constexpr int kTpRegs = 16;        // candidates per lane the searches keep in registers
 constexpr int kTpProbes = 7;       // thresholds per search round (8-way search)
@@ -73,7 +75,7 @@ __device__ __forceinline__ void block_sums(uint64_t (&v)[K], TpShared& s, int ti
 }
 
 template <typename T>
-__global__ __launch_bounds__(kTpThreads) void top_p_kernel(
+__global__ __launch_bounds__(kTpThreads, 4) void top_p_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
     const float* __restrict__ maxv, const uint64_t* __restrict__ R, WeightConsts wc, uint64_t P,
     uint64_t* __restrict__ thr_w, int32_t* __restrict__ thr_id, uint64_t* __restrict__ Rp,
@@ -182,7 +184,8 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
         // pack the regions into one list: every thread reads its entries,
         // then (after the barrier) writes them at its region's offset
         constexpr int kPer = kTpCap / kTpThreads;
-        static_assert(kTpThreads == 2 * kTpRegion, "entry j of a thread lies in region 2j or 2j + 1");
+        constexpr int kRR = kTpThreads / kTpRegion;   // regions per row of entries
+        static_assert(kRR * kTpRegion == kTpThreads && kRR <= 2, "entry j of a thread lies in region kRR * j + tid / kTpRegion");
         int pre[kTpThreads / kWave];   // region offsets in the packed list
         int acc = 0;
 #pragma unroll
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
           pre[w] = acc;
           acc += s.cnt[w];
         }
-        const bool upper = tid >= kTpRegion;
+        const bool upper = kRR == 2 && tid >= kTpRegion;
         const int re = tid - (upper ? kTpRegion : 0);   // entry within its region
         uint64_t pw[kPer];
         uint32_t pid[kPer];
@@ -198,8 +201,8 @@ __global__ __launch_bounds__(kTpThreads) void top_p_kernel(
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
           const int src = j * kTpThreads + tid;
-          const int cnt = upper ? s.cnt[2 * j + 1] : s.cnt[2 * j];
-          const int base = upper ? pre[2 * j + 1] : pre[2 * j];
+          const int cnt = upper ? s.cnt[kRR * j + 1] : s.cnt[kRR * j];
+          const int base = upper ? pre[kRR * j + 1] : pre[kRR * j];
           dst[j] = re < cnt ? base + re : -1;
           pw[j] = s.w[src];
           pid[j] = s.id[src];
