@@ -35,7 +35,7 @@ def test_algorithmic_bytes_sampling_adds_one_residual_row_per_request():
 
 def test_traffic_figure_only_for_the_profiled_source():
     # each committed profile names its workload and the attention source it was measured on
-    for name in ("single", "batched", "long", "ragged"):
+    for name in ("tiny", "single", "batched", "long", "ragged"):
         path = bench.traffic_profile(name)
         if not os.path.exists(path):
             assert bench.measured_traffic(name) is None
@@ -49,7 +49,9 @@ def test_traffic_figure_only_for_the_profiled_source():
             assert isinstance(t, int) and t > 0
         else:
             assert t is None
-    assert bench.measured_traffic("tiny") is None   # no counters for that workload
+    # no summary file at all: no figure
+    assert not os.path.exists(bench.traffic_profile("no_such_workload"))
+    assert bench.measured_traffic("no_such_workload") is None
 
 
 def test_more_than_one_gpu_is_refused():
