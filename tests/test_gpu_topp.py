@@ -141,3 +141,35 @@ def test_flat_rows_take_the_row_pass_search(dtype):
                                   ref[k]), (k, p)
         P = oracle.top_p_fixed(p)
         assert int(ref["thr_id"][0, 0]) == -(-P * V // (1 << 32)) - 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_candidate_list_sizes(dtype):
+    """Rows with k head tokens at five logit levels (many equal weights) and a tail
+    that weighs 0: the first candidate pass takes exactly the k head tokens, so k
+    walks the candidate list across the sizes the kernel treats differently (one
+    and two slots per thread of the sorted cut, the one-wave searches, more than
+    the LDS holds)."""
+    import tree_verification_build_amd as lib
+    ks = [1, 2, 64, 300, 511, 512, 513, 1000, 1024, 1025, 2500, 4096, 4097]
+    V, T = 40000, 1.0
+    rng = np.random.default_rng(4242)
+    base = np.full((1, len(ks), V), -57.0, np.float32)
+    for n, k in enumerate(ks):
+        ids = rng.choice(V, size=k, replace=False)
+        base[0, n, ids] = 3.0 - 0.5 * rng.integers(0, 5, size=k)
+    logits = base if dtype == "f32" else (base.view(np.uint32) >> 16).astype(np.uint16)
+    nn = np.array([len(ks)], np.int32)
+    x = dev_tensor(logits, dtype)
+    nd = torch.from_numpy(nn).cuda()
+    v = lib.ddtree_vocab_reduce(x, nd, T)
+    ref_v = oracle.vocab_reduce(logits, nn, T, dtype=dtype)
+    for p in (1e-6, 0.5, 0.9):
+        say("top_p candidate sizes", dtype, p)
+        tp = lib.ddtree_vocab_top_p(x, nd, v["maxv"], v["R"], T, p)
+        torch.cuda.synchronize()
+        ref = oracle.vocab_top_p(logits, ref_v["maxv"], nn, T, p, dtype=dtype)
+        for key in ("thr_w", "thr_id", "Rp", "Rp_blocks"):
+            got = tp[key].cpu().numpy()
+            assert np.array_equal(got.view(ref[key].dtype) if got.dtype != ref[key].dtype else got,
+                                  ref[key]), (key, p)

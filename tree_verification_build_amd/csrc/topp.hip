@@ -9,8 +9,7 @@
 // token: threshold weight w* and id*; a token is kept iff w > w*, or w = w*
 // and id <= id*.
 //
-// One 512-thread workgroup per node row, two per CU (50 KB of LDS each), so
-// that one workgroup's single-wave searches overlap the other's row pass.
+// One 512-thread workgroup per node row, two per CU (50 KB of LDS each).
 // With Tt = ceil(P * R / 2^32):
 //  1. a pass over the row sums and counts the weights at or above 2^e and
 //     copies those tokens (weight, id) to LDS, each wave into its own region
@@ -19,8 +18,13 @@
 //     (kTpCap in all), and the regions are then packed into one list; e
 //     starts at 20 and is moved by bisection between exponents known to reach
 //     Tt and not to (1-4 passes);
-//  2. w* = the largest v with sum{w >= v} >= Tt, by 8-way interval search
-//     (7 thresholds per reduction) over the LDS candidates by one wave, or,
+//  2. up to 2 * kTpThreads candidates: the workgroup sorts them by (weight
+//     desc, id asc) and scans their weights in that order; the nucleus's last
+//     token is the one whose running sum first reaches Tt, which gives w*, id*
+//     and R_p at once (steps 4-5 below describe the same cut);
+//     more candidates: w* = the largest v with sum{w >= v} >= Tt, by 8-way
+//     interval search (7 thresholds per reduction) over the LDS candidates by
+//     one wave (whose searches overlap the other workgroup's row pass), or,
 //     when more than kTpCap tokens are needed, over the row itself (exact,
 //     slower);
 //  3. every pass over the row skips the weight polynomial of the tokens that
@@ -72,6 +76,140 @@ __device__ __forceinline__ void block_sums(uint64_t (&v)[K], TpShared& s, int ti
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < K; ++k) v[k] = s.tot[k];
+}
+
+// Lane l's copy of lane l ^ j's 64-bit value (j < 64, a power of two): DPP for
+// the in-row distances 1, 2 and 8, a bpermute through LDS for the others.
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t v, int j, int lane) {
+  int lo = static_cast<int>(static_cast<uint32_t>(v)), hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+  if (j == 1) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false);   // quad_perm [1, 0, 3, 2]
+    hi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false);
+  } else if (j == 2) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false);   // quad_perm [2, 3, 0, 1]
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false);
+  } else if (j == 8) {
+    lo = __builtin_amdgcn_mov_dpp(lo, 0x128, 0xF, 0xF, false);  // row_ror 8: l + 8 mod 16 = l ^ 8
+    hi = __builtin_amdgcn_mov_dpp(hi, 0x128, 0xF, 0xF, false);
+  } else {
+    const int addr = (lane ^ j) << 2;
+    lo = __builtin_amdgcn_ds_bpermute(addr, lo);
+    hi = __builtin_amdgcn_ds_bpermute(addr, hi);
+  }
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+constexpr int kTpKeyIdBits = 22;   // ids < V <= 64 * DDTREE_R_BLOCK = 2^21
+constexpr uint64_t kTpKeyIdMask = (1ull << kTpKeyIdBits) - 1;
+
+// The nucleus of a candidate list of at most E * kTpThreads tokens, by the
+// whole workgroup: every candidate becomes the key (w << 22) | (2^22 - 1 - id),
+// unique per token and larger for a token earlier in the (weight desc, id asc)
+// order; a bitonic network sorts the keys descending over E * kTpThreads slots
+// (slot g = e * kTpThreads + tid; empty slots hold key 0, below every
+// candidate, since a candidate weighs at least 1); an inclusive scan of the
+// weights in that order then gives each token the mass up to and including it,
+// and the nucleus is every token whose mass before it is below Tt, its last
+// token the one whose scan first reaches Tt.  Exact integer arithmetic: the
+// same cut as the interval searches below.
+template <int E>
+__device__ void nucleus_by_sort(TpShared& s, int nc, int tid, uint64_t Tt, long row, int nb,
+                                uint64_t* __restrict__ thr_w, int32_t* __restrict__ thr_id,
+                                uint64_t* __restrict__ Rp, uint64_t* __restrict__ Rp_blocks) {
+  constexpr int n = E * kTpThreads;
+  static_assert(2 * n <= kTpCap, "the exchange buffers live in the candidate list");
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  uint64_t k[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int g = e * kTpThreads + tid;
+    k[e] = g < nc ? (s.w[g] << kTpKeyIdBits) | (kTpKeyIdMask - s.id[g]) : 0ull;
+  }
+  if (tid < kWave) s.blk[tid] = 0;
+  __syncthreads();   // the candidate list is read: its space holds the exchanges now
+  int parity = 0;
+#pragma unroll
+  for (int kk = 2; kk <= n; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      if (j >= kTpThreads) {
+        // the partner slot is this thread's other one (j = kTpThreads, kk = n:
+        // a descending merge, the larger key to the lower slot)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e * kTpThreads) & j) continue;
+          const int e2 = e + j / kTpThreads;
+          const uint64_t a = k[e], b = k[e2];
+          k[e] = a > b ? a : b;
+          k[e2] = a > b ? b : a;
+        }
+        continue;
+      }
+      uint64_t o[E];
+      if (j >= kWave) {
+        // across waves: two alternating buffers, so one barrier per step (a
+        // buffer is written again only after the next step's barrier, which
+        // every thread reaches after its reads of it)
+        uint64_t* buf = s.w + parity * n;
+        parity ^= 1;
+#pragma unroll
+        for (int e = 0; e < E; ++e) buf[e * kTpThreads + tid] = k[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = buf[(e * kTpThreads + tid) ^ j];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = xor_lane_u64(k[e], j, lane);
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int g = e * kTpThreads + tid;
+        // descending runs where bit kk of the slot is clear; the lower slot of
+        // a pair keeps the larger key in a descending run
+        const bool keep_max = ((g & j) == 0) == ((g & kk) == 0);
+        k[e] = keep_max ? (k[e] > o[e] ? k[e] : o[e]) : (k[e] < o[e] ? k[e] : o[e]);
+      }
+    }
+  }
+  // inclusive scan of the weights in slot order: within the wave by lane
+  // moves, then the earlier waves' and earlier slot rows' totals
+  uint64_t w[E], incl[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    w[e] = k[e] >> kTpKeyIdBits;
+    uint64_t v = w[e];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int src = lane >= d ? lane - d : lane;
+      const int lo = __builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(static_cast<uint32_t>(v)));
+      const int hi = __builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(static_cast<uint32_t>(v >> 32)));
+      if (lane >= d) v += (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+    }
+    incl[e] = v;
+    if (lane == kWave - 1) s.part[wave][e] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint64_t before = 0;
+    for (int e2 = 0; e2 < e; ++e2)
+      for (int wv = 0; wv < kTpWaves; ++wv) before += s.part[wv][e2];
+    for (int wv = 0; wv < wave; ++wv) before += s.part[wv][e];
+    incl[e] += before;
+    const uint64_t excl = incl[e] - w[e];
+    if (w[e] != 0 && excl < Tt) {
+      const int id = static_cast<int>(kTpKeyIdMask - (k[e] & kTpKeyIdMask));
+      atomicAdd(reinterpret_cast<unsigned long long*>(&s.blk[id / DDTREE_R_BLOCK]),
+                static_cast<unsigned long long>(w[e]));
+      if (incl[e] >= Tt) {   // the nucleus's last token: exactly one slot
+        thr_w[row] = w[e];
+        thr_id[row] = id;
+        Rp[row] = incl[e];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < nb) Rp_blocks[row * nb + tid] = s.blk[tid];
 }
 
 template <typename T>
@@ -160,7 +298,7 @@ __global__ __launch_bounds__(kTpThreads, 4) void top_p_kernel(
     const float ymin = static_cast<float>(e - 33);
     uint64_t sc[3] = {0, 0, 0};
     int wcount = 0;   // this wave's tokens so far (the same in every lane)
-    row_scan(ymin, [&](uint64_t w, int id) {
+    auto take = [&](uint64_t w, int id) {
       const bool c = w >= lb;
       if (c) {
         sc[0] += w;
@@ -174,7 +312,8 @@ __global__ __launch_bounds__(kTpThreads, 4) void top_p_kernel(
         s.id[wave * kTpRegion + pos] = static_cast<uint32_t>(id);
       }
       wcount += __popcll(mask);
-    });
+    };
+    row_scan(ymin, take);
     if (lane == 0) s.cnt[wave] = wcount;
     sc[2] = wcount > kTpRegion ? 1u : 0u;   // 1 in each lane of a wave whose tokens overflowed
     block_sums<3>(sc, s, tid);
@@ -316,7 +455,11 @@ __global__ __launch_bounds__(kTpThreads, 4) void top_p_kernel(
     (void)nlanes;
   };
 
-  if (in_lds) {
+  if (in_lds && nc <= kTpThreads) {
+    nucleus_by_sort<1>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
+  } else if (in_lds && nc <= 2 * kTpThreads) {
+    nucleus_by_sort<2>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
+  } else if (in_lds) {
     if (tid >= kWave) return;   // no workgroup barrier follows
     auto reduce = [&](auto& acc) {
 #pragma unroll
