@@ -9,7 +9,8 @@
 // token: threshold weight w* and id*; a token is kept iff w > w*, or w = w*
 // and id <= id*.
 //
-// One 512-thread workgroup per node row, two per CU (50 KB of LDS each).
+// One 512-thread workgroup per node row, up to three per CU (50 KB of LDS
+// and at most 80 registers each), so that more loads are in flight per CU.
 // With Tt = ceil(P * R / 2^32):
 //  1. a pass over the row sums and counts the weights at or above 2^e and
 //     copies those tokens (weight, id) to LDS, each wave into its own region
@@ -24,7 +25,7 @@
 //     and R_p at once (steps 4-5 below describe the same cut);
 //     more candidates: w* = the largest v with sum{w >= v} >= Tt, by 8-way
 //     interval search (7 thresholds per reduction) over the LDS candidates by
-//     one wave (whose searches overlap the other workgroup's row pass), or,
+//     one wave (whose searches overlap the other workgroups' row passes), or,
 //     when more than kTpCap tokens are needed, over the row itself (exact,
 //     slower);
 //  3. every pass over the row skips the weight polynomial of the tokens that
@@ -43,7 +44,7 @@ constexpr int kTpThreads = 512;
 constexpr int kTpWaves = kTpThreads / kWave;
 constexpr int kTpCap = 4096;       // candidate tokens held in LDS (12 bytes each)
 constexpr int kTpRegion = kTpCap / (kTpThreads / kWave);   // per-wave share during a pass
-constexpr int kTpRegs = 16;        // candidates per lane the searches keep in registers
+constexpr int kTpRegs = 8;         // candidates per lane the searches keep in registers
 constexpr int kTpProbes = 7;       // thresholds per search round (8-way search)
 constexpr int kMaxSums = kTpProbes;       // sums per block-wide reduction
 
@@ -213,7 +214,7 @@ __device__ void nucleus_by_sort(TpShared& s, int nc, int tid, uint64_t Tt, long 
 }
 
 template <typename T>
-__global__ __launch_bounds__(kTpThreads, 4) void top_p_kernel(
+__global__ __launch_bounds__(kTpThreads, 6) void top_p_kernel(
     const T* __restrict__ logits, int N, int V, const int32_t* __restrict__ num_nodes,
     const float* __restrict__ maxv, const uint64_t* __restrict__ R, WeightConsts wc, uint64_t P,
     uint64_t* __restrict__ thr_w, int32_t* __restrict__ thr_id, uint64_t* __restrict__ Rp,
