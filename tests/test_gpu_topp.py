@@ -147,8 +147,8 @@ def test_flat_rows_take_the_row_pass_search(dtype):
 def test_candidate_list_sizes(dtype):
     """Rows with k head tokens at five logit levels (many equal weights) and a tail
     that weighs 0: the first candidate pass takes exactly the k head tokens, so k
-    walks the candidate list across the sizes the kernel treats differently (one
-    and two slots per thread of the sorted cut, the one-wave searches, more than
+    walks the candidate list across the sizes the kernel treats differently (one,
+    two, four and eight slots per thread of the sorted cut, more than
     the LDS holds)."""
     import tree_verification_build_amd as lib
     ks = [1, 2, 64, 300, 511, 512, 513, 1000, 1024, 1025, 2500, 4096, 4097]

@@ -19,15 +19,13 @@
 //     (kTpCap in all), and the regions are then packed into one list; e
 //     starts at 20 and is moved by bisection between exponents known to reach
 //     Tt and not to (1-4 passes);
-//  2. up to 2 * kTpThreads candidates: the workgroup sorts them by (weight
-//     desc, id asc) and scans their weights in that order; the nucleus's last
-//     token is the one whose running sum first reaches Tt, which gives w*, id*
-//     and R_p at once (steps 4-5 below describe the same cut);
-//     more candidates: w* = the largest v with sum{w >= v} >= Tt, by 8-way
-//     interval search (7 thresholds per reduction) over the LDS candidates by
-//     one wave (whose searches overlap the other workgroups' row passes), or,
-//     when more than kTpCap tokens are needed, over the row itself (exact,
-//     slower);
+//  2. candidates in LDS: the workgroup sorts them by (weight desc, id asc)
+//     and scans their weights in that order; the nucleus's last token is the
+//     one whose running sum first reaches Tt, which gives w*, id* and R_p at
+//     once (steps 4-5 below describe the same cut);
+//     more than kTpCap tokens needed: w* = the largest v with
+//     sum{w >= v} >= Tt, by 8-way interval search (7 thresholds per
+//     reduction) over the row itself (exact, slower);
 //  3. every pass over the row skips the weight polynomial of the tokens that
 //     provably weigh less than the pass's lower bound;
 //  4. with S> = sum{w > w*}, the nucleus takes m = ceil((Tt - S>) / w*) of the
@@ -44,9 +42,8 @@ constexpr int kTpThreads = 512;
 constexpr int kTpWaves = kTpThreads / kWave;
 constexpr int kTpCap = 4096;       // candidate tokens held in LDS (12 bytes each)
 constexpr int kTpRegion = kTpCap / (kTpThreads / kWave);   // per-wave share during a pass
-constexpr int kTpRegs = 8;         // candidates per lane the searches keep in registers
 constexpr int kTpProbes = 7;       // thresholds per search round (8-way search)
-constexpr int kMaxSums = kTpProbes;       // sums per block-wide reduction
+constexpr int kMaxSums = 8;       // sums per block-wide reduction (and slot rows of the sorted cut)
 
 struct TpShared {
   uint64_t w[kTpCap];
@@ -118,7 +115,8 @@ __device__ void nucleus_by_sort(TpShared& s, int nc, int tid, uint64_t Tt, long 
                                 uint64_t* __restrict__ thr_w, int32_t* __restrict__ thr_id,
                                 uint64_t* __restrict__ Rp, uint64_t* __restrict__ Rp_blocks) {
   constexpr int n = E * kTpThreads;
-  static_assert(2 * n <= kTpCap, "the exchange buffers live in the candidate list");
+  static_assert(n <= kTpCap && E <= kMaxSums, "the exchange buffers live in the candidate list");
+  constexpr bool kTwoBuffers = 2 * n <= kTpCap;
   const int lane = tid & (kWave - 1), wave = tid / kWave;
   uint64_t k[E];
 #pragma unroll
@@ -134,30 +132,34 @@ __device__ void nucleus_by_sort(TpShared& s, int nc, int tid, uint64_t Tt, long 
 #pragma unroll
     for (int j = kk >> 1; j > 0; j >>= 1) {
       if (j >= kTpThreads) {
-        // the partner slot is this thread's other one (j = kTpThreads, kk = n:
-        // a descending merge, the larger key to the lower slot)
+        // the partner slot is one of this thread's own; bit kk of the lower
+        // slot (the same for every thread) gives the run's direction
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           if ((e * kTpThreads) & j) continue;
           const int e2 = e + j / kTpThreads;
+          const bool desc = ((e * kTpThreads) & kk) == 0;
           const uint64_t a = k[e], b = k[e2];
-          k[e] = a > b ? a : b;
-          k[e2] = a > b ? b : a;
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          k[e] = desc ? hi : lo;
+          k[e2] = desc ? lo : hi;
         }
         continue;
       }
       uint64_t o[E];
       if (j >= kWave) {
-        // across waves: two alternating buffers, so one barrier per step (a
-        // buffer is written again only after the next step's barrier, which
-        // every thread reaches after its reads of it)
-        uint64_t* buf = s.w + parity * n;
+        // across waves through LDS: with room for two buffers they alternate,
+        // so one barrier per step (a buffer is written again only after the
+        // next step's barrier, which every thread reaches after its reads of
+        // it); with room for one, a second barrier ends the step's reads
+        uint64_t* buf = s.w + (kTwoBuffers ? parity * n : 0);
         parity ^= 1;
 #pragma unroll
         for (int e = 0; e < E; ++e) buf[e * kTpThreads + tid] = k[e];
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = buf[(e * kTpThreads + tid) ^ j];
+        if (!kTwoBuffers) __syncthreads();
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) o[e] = xor_lane_u64(k[e], j, lane);
@@ -368,9 +370,9 @@ __global__ __launch_bounds__(kTpThreads, 6) void top_p_kernel(
     else e = (e_good + e_bad) / 2;
   }
 
-  // 2-5. the search, by wave 0 alone over the LDS candidates (wave-level sums),
-  // or by the whole workgroup over the row (workgroup sums)
-  auto search = [&](auto&& each, auto&& reduce, auto&& sync, int lid, int nlanes, bool wave_level) {
+  // 2-5. more candidates than the LDS holds: the search by the whole workgroup
+  // over the row (workgroup sums)
+  auto search = [&](auto&& each, auto&& reduce, auto&& sync, int lid) {
     // invariant: sum{w >= lo} >= Tt > sum{w >= hi}
     uint64_t lo = 1ull << e_good;
     uint64_t hi = 1ull << min(e_bad, 33);
@@ -399,22 +401,14 @@ __global__ __launch_bounds__(kTpThreads, 6) void top_p_kernel(
     const uint64_t ws = lo;
     // 3. tokens of weight w* that the nucleus takes, and the id cut among them
     uint64_t g[kTpProbes] = {};
-    int id_max = -1;   // the largest id of weight w* (wave-level search only)
     each(ws, [&](uint64_t w, int id) {
       g[0] += w > ws ? w : 0;
       g[1] += w == ws ? 1 : 0;
-      if (wave_level && w == ws) id_max = max(id_max, id);
     });
     reduce(g);
     const uint64_t sgt = g[0];
     const uint64_t take = (Tt - sgt + ws - 1) / ws;   // 1 <= take <= #{w = w*}
     long ilo = -1, ihi = V - 1;                        // #{.. id <= ilo} < take <= #{.. id <= ihi}
-    if (wave_level && take == g[1]) {
-      // every token of weight w* is taken (the usual case): the cut is the
-      // largest of their ids
-      ihi = static_cast<long>(static_cast<int32_t>(wave_max_u32(static_cast<uint32_t>(id_max) + 1u))) - 1;
-      ilo = ihi - 1;
-    }
     for (int round = 0; round < 40 && ihi - ilo > 1; ++round) {
       long th[kTpProbes];
       uint64_t acc[kTpProbes];
@@ -453,51 +447,16 @@ __global__ __launch_bounds__(kTpThreads, 6) void top_p_kernel(
       Rp[row] = sgt + take * ws;
     }
     if (lid < nb) Rp_blocks[row * nb + lid] = s.blk[lid];
-    (void)nlanes;
   };
 
   if (in_lds && nc <= kTpThreads) {
     nucleus_by_sort<1>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
   } else if (in_lds && nc <= 2 * kTpThreads) {
     nucleus_by_sort<2>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
+  } else if (in_lds && nc <= 4 * kTpThreads) {
+    nucleus_by_sort<4>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
   } else if (in_lds) {
-    if (tid >= kWave) return;   // no workgroup barrier follows
-    auto reduce = [&](auto& acc) {
-#pragma unroll
-      for (int k = 0; k < kTpProbes; ++k) acc[k] = wave_sum_u64_dpp(acc[k]);
-    };
-    auto sync = [&]() {
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-    };
-    if (nc <= kWave * kTpRegs) {
-      // up to kTpRegs candidates per lane, read from LDS once and kept in
-      // registers for every round of the searches
-      uint64_t cw[kTpRegs];
-      int cid[kTpRegs];
-      const int nr = (nc + kWave - 1) / kWave;   // rounds of 64 (the same in every lane)
-#pragma unroll
-      for (int j = 0; j < kTpRegs; ++j) {
-        const int k = j * kWave + lane;
-        cw[j] = j < nr && k < nc ? s.w[k] : 0ull;
-        cid[j] = j < nr && k < nc ? static_cast<int>(s.id[k]) : 0;
-      }
-      search(
-          [&](uint64_t, auto&& f) {
-#pragma unroll
-            for (int j = 0; j < kTpRegs; ++j) {
-              if (j >= nr) break;
-              if (j * kWave + lane < nc) f(cw[j], cid[j]);
-            }
-          },
-          reduce, sync, lane, kWave, true);
-    } else {
-      search(
-          [&](uint64_t, auto&& f) {
-            for (int k = lane; k < nc; k += kWave) f(s.w[k], static_cast<int>(s.id[k]));
-          },
-          reduce, sync, lane, kWave, true);
-    }
+    nucleus_by_sort<8>(s, nc, tid, Tt, row, nb, thr_w, thr_id, Rp, Rp_blocks);
   } else {
     search(
         [&](uint64_t bound, auto&& f) {
@@ -506,7 +465,7 @@ __global__ __launch_bounds__(kTpThreads, 6) void top_p_kernel(
           row_scan(static_cast<float>(63 - __builtin_clzll(bound) - 33), f);
         },
         [&](auto& acc) { block_sums<kTpProbes>(acc, s, tid); },
-        [&]() { __syncthreads(); }, tid, kTpThreads, false);
+        [&]() { __syncthreads(); }, tid);
   }
 }
 
